@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark: one packed continuous-batching tick of paged attention on one MI355X.
+
+A step is one whole tick of the hot path over one batch of synthetic input:
+slot mapping -> RoPE on the new Q/K + K/V page write -> paged attention
+(decode rows with split-KV and its merge, prefill chunks on MFMA).
+
+Default workload: the Qwen3-4B-shaped packed mixed tick (48 decode rows with
+contexts U[256, 4096] plus prefill chunks of 512/512/1024 tokens after 0-3
+cached 256-token pages; 32 query / 8 KV heads, head_dim 128, bf16, seed 1004).
+Inputs sit in HBM before timing starts; three copies of every buffer are
+rotated between steps so no step finds the previous step's pages in the
+256 MB Infinity Cache.
+
+Prints ONE JSON line. `value` = tick tokens per second. `roofline` refers to
+the dominant kernel (decode attention, HBM-bound), timed per launch with HIP
+events recorded on the library's stream. `cpu_baseline` = the CPU oracle
+(RoPE + write + float64 attention) on the same tick.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn KV read GB/s (% HBM peak) + packed-tick attn tokens/s, Qwen3-4B"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+WORKLOADS = {"cfg2": 2, "cfg3": 3, "cfg4": 4, "cfg5": 5}
+ROTATE = 3
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(t):
+    """Bytes / flops the method itself must move / compute (no re-reads, no scratch).
+
+    Decode row of a sequence with n keys: K and V rows n*Hkv*D*e each, the
+    query and output rows Hq*D*e each, and 4 bytes per page-table entry used.
+    Prefill chunk of L rows after P0 cached keys: 4*D*Hq*pairs flops over the
+    unmasked (row, key) pairs, pairs = L*P0 + L(L+1)/2.
+    """
+    e = 2 if t.dtype == "bf16" else 4
+    dec_bytes = 0
+    dec_kv = 0
+    flops = 0
+    pf_bytes = 0
+    for s in range(t.S):
+        n, L = int(t.seq_lens[s]), int(t.query_lens[s])
+        if L == 1:
+            kv = 2 * n * t.Hkv * t.D * e
+            dec_kv += kv
+            dec_bytes += kv + 2 * t.Hq * t.D * e + 4 * math.ceil(n / t.P)
+        elif L > 1:
+            p0 = n - L
+            pairs = L * p0 + L * (L + 1) // 2
+            flops += 4 * t.D * t.Hq * pairs
+            pf_bytes += 2 * n * t.Hkv * t.D * e + 2 * L * t.Hq * t.D * e
+    T = t.T
+    k1_bytes = T * ((t.Hq + 2 * t.Hkv) * t.D * e + 8 + t.D * 4) + T * (t.Hq + 3 * t.Hkv) * t.D * e
+    return {"decode_bytes": dec_bytes, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
+            "prefill_bytes": pf_bytes, "k1_bytes": k1_bytes}
+
+
+def cpu_baseline(t, reps):
+    """The oracle as it stands, on the same tick, timed on the host."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    table = oracle.rope_table(t.max_pos, t.D, t.theta) if t.theta is not None else None
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.run_tick(t.dtype, t.q, t.k, t.v, t.positions, t.block_tables, t.qsl, t.seq_lens,
+                        t.k_pool, t.v_pool, table, t.scale)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": t.T / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the full tick ({t.T} query rows, {t.S} sequences), {reps} runs, median "
+                      f"{med:.2f} s per tick; numpy float32 RoPE + float64 attention",
+            "seconds_per_tick": med,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg4", choices=sorted(WORKLOADS))
+    ap.add_argument("--kv-split", type=int, default=0)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_page_amd as pa
+    from paged_kv_cache_page_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pa.lib()
+    dev = "cuda:0"
+    cfg = WORKLOADS[args.workload]
+    log("generating", W.CONFIG_NAMES[cfg])
+    t = W.make_config(cfg, poison=False)
+
+    def dev_st(a):
+        if t.dtype == W.F32:
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def dev_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    copies = []
+    for r in range(ROTATE):
+        copies.append({
+            "q": dev_st(t.q), "k": dev_st(t.k), "v": dev_st(t.v),
+            "kp": dev_st(t.k_pool), "vp": dev_st(t.v_pool),
+            "bt": dev_i32(t.block_tables), "sl": dev_i32(t.seq_lens), "qsl": dev_i32(t.qsl),
+            "pos": dev_i32(t.positions), "slots": torch.empty(t.T, dtype=torch.int32, device=dev),
+            "out": torch.empty((t.T, t.Hq, t.D), dtype=torch.bfloat16 if t.dtype == W.BF16
+                               else torch.float32, device=dev),
+        })
+    table = pa.pa_rope_cos_sin_table(t.max_pos, t.D, t.theta, device=dev)
+    dt = pa.PA_BF16 if t.dtype == W.BF16 else pa.PA_F32
+    ws_bytes = pa.pa_paged_attention_workspace_size(t.S, t.T, t.Hq, t.D, t.max_query_len,
+                                                    t.max_seq_len, t.P, args.kv_split, dt)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = copies[i % ROTATE]
+        pa.pa_compute_slot_mapping(c["bt"], c["qsl"], c["pos"], t.P, t.num_pages, out=c["slots"],
+                                   stream=stream)
+        pa.pa_rope_and_cache_write(c["q"], c["k"], c["v"], c["pos"], c["slots"], table, c["kp"],
+                                   c["vp"], stream=stream)
+        pa.pa_paged_attention_varlen(c["q"], c["kp"], c["vp"], c["bt"], c["sl"], c["qsl"],
+                                     t.max_query_len, t.max_seq_len, scale=t.scale,
+                                     kv_split_tokens=args.kv_split, out=c["out"], workspace=ws,
+                                     stream=stream)
+
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    log("timed", args.steps, "steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # second pass with per-kernel events (recorded by the library on its stream)
+    log("per-kernel timing pass")
+    pa.pa_profile_start(16 * args.steps + 16)
+    for i in range(args.steps):
+        step(i)
+    recs = pa.pa_profile_stop()
+    pa.pa_profile_reset()
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    kernels = {n: {"avg_ms": float(np.mean(v)), "launches": len(v)} for n, v in per.items()}
+
+    work = algorithmic_work(t)
+    tokens_per_s = t.T / (ms_per_step / 1e3)
+    roof = None
+    extra = {}
+    if "decode_attention" in kernels:
+        dms = kernels["decode_attention"]["avg_ms"]
+        gbps = work["decode_bytes"] / (dms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "decode_attention", "achieved": round(gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": None, "bytes_per_launch": work["decode_bytes"]}
+        extra["kv_read_gbps"] = round(work["decode_kv_bytes"] / (dms / 1e3) / 1e9, 1)
+        extra["kv_hbm_frac"] = round(extra["kv_read_gbps"] / HBM_PEAK_GBPS, 4)
+    if "prefill_attention_mfma" in kernels and work["prefill_flops"]:
+        pms = kernels["prefill_attention_mfma"]["avg_ms"]
+        tf = work["prefill_flops"] / (pms / 1e3) / 1e12
+        extra["prefill_mfma"] = {"achieved_tflops": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                 "flops_per_launch": work["prefill_flops"]}
+    attn_ms = sum(v["avg_ms"] for n, v in kernels.items() if n not in
+                  ("slot_mapping", "rope_cache_write"))
+    extra["attention_only_tokens_per_s"] = round(t.T / (attn_ms / 1e3), 1) if attn_ms else None
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(t, args.cpu_reps)
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": t.dtype,
+        "data": "synthetic",
+        "config": {"workload": t.name, "seqs": t.S, "query_tokens": t.T,
+                   "decode_rows": int((t.query_lens == 1).sum()),
+                   "chunks": [int(x) for x in t.query_lens[t.query_lens > 1]],
+                   "heads_q_kv": [t.Hq, t.Hkv], "head_dim": t.D, "page_size": t.P,
+                   "pool_pages": t.num_pages, "seed": t.seed, "parallelism": "none (1 GPU)"},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+        "wall_s_timed_region": round(wall, 4), **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

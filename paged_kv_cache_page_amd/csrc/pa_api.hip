@@ -1,0 +1,295 @@
+// The C ABI of libpa (declared in include/pa.h): host-scalar checks, workspace
+// sizing, launch dispatch, and the optional kernel-timing hook.
+//
+// No entry point reads device memory from the host, allocates, frees or
+// synchronises (the profiling calls aside). Every check happens before the
+// first HIP call, so argument errors are reported without touching a GPU.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// ------------------------------------------------------------- timing ------
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+std::vector<ProfRec> g_recs;
+bool g_prof_on = false;
+int g_prof_n = 0;
+bool g_prof_open = false;  // a profile_before without its profile_after
+
+void destroy_events() {
+  for (auto& r : g_recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_recs.clear();
+  g_prof_n = 0;
+}
+}  // namespace
+
+void profile_before(const char* name, hipStream_t stream) {
+  g_prof_open = false;
+  if (!g_prof_on || g_prof_n >= (int)g_recs.size()) return;
+  g_recs[g_prof_n].name = name;
+  if (hipEventRecord(g_recs[g_prof_n].start, stream) == hipSuccess) g_prof_open = true;
+}
+
+void profile_after(hipStream_t stream) {
+  if (!g_prof_open) return;
+  g_prof_open = false;
+  if (hipEventRecord(g_recs[g_prof_n].stop, stream) == hipSuccess) ++g_prof_n;
+}
+
+// ------------------------------------------------------------- helpers -----
+namespace {
+
+constexpr int kDefaultSplitTokens = 512;
+constexpr int kMaxPartPages = 256;  // must match the decode kernel's page staging
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(pa_dtype_t dt) { return dt == PA_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_BF16; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+// Keys per split-KV partition actually used for these arguments.
+int split_tokens(int requested, int P) {
+  int pt = requested > 0 ? requested : kDefaultSplitTokens;
+  // the decode kernel stages the page ids of one partition in LDS
+  const int cap = ((kMaxPartPages - 2) * P) / 16 * 16;
+  if (pt > cap) pt = cap;
+  return pt;
+}
+
+// Whether prefill rows (L > 1) go to the MFMA kernel; otherwise every row of
+// the tick takes the per-token VALU path.
+bool use_mfma_prefill(pa_dtype_t dt, int D, int max_query_len) {
+  return max_query_len <= 1 || prefill_mfma_supported(dt, D, 1);
+}
+
+size_t workspace_bytes_for(int S, int T, int Hq, int D, int max_query_len, int max_seq_len,
+                           int P, int kv_split, pa_dtype_t dt) {
+  const int pt = split_tokens(kv_split, P);
+  const long max_parts = max_seq_len > 0 ? ((long)max_seq_len + pt - 1) / pt : 1;
+  if (max_parts <= 1) return 0;
+  const bool token_mode = !use_mfma_prefill(dt, D, max_query_len);
+  const long rows = token_mode ? T : S;
+  return (size_t)rows * (size_t)max_parts * (size_t)Hq * ((size_t)D + 2) * sizeof(float);
+}
+
+pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int32_t pa_abi_version(void) { return 1; }
+
+const char* pa_status_string(pa_status_t status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: a host argument is invalid";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: no kernel for this dtype/shape";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL: workspace below the size query";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP call failed";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+pa_status_t pa_rope_cos_sin_table(float* cos_sin, int32_t max_pos, int32_t head_dim,
+                                  double theta, void* stream) {
+  if (!cos_sin || max_pos < 1 || head_dim < 2 || head_dim % 2 || !(theta > 0.0) ||
+      !isfinite(theta))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(launch_rope_table(cos_sin, max_pos, head_dim, theta, (hipStream_t)stream));
+}
+
+pa_status_t pa_compute_slot_mapping(const int32_t* block_tables, const int32_t* query_start_loc,
+                                    const int32_t* positions, int32_t* slot_mapping, int32_t S,
+                                    int32_t T, int32_t max_blocks_per_seq, int32_t page_size,
+                                    int32_t num_pages, void* stream) {
+  if (S < 0 || T < 0 || max_blocks_per_seq < 1 || page_size < 1 || num_pages < 1)
+    return PA_ERR_INVALID_ARG;
+  if ((long)num_pages * page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (T > 0 && (S < 1 || !block_tables || !query_start_loc || !positions || !slot_mapping))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(launch_slot_mapping(block_tables, query_start_loc, positions, slot_mapping, S,
+                                      T, max_blocks_per_seq, page_size, num_pages,
+                                      (hipStream_t)stream));
+}
+
+pa_status_t pa_rope_and_cache_write(void* q, void* k, const void* v, const int32_t* positions,
+                                    const int32_t* slot_mapping, const float* cos_sin,
+                                    void* k_pool, void* v_pool, int32_t T, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, int32_t page_size,
+                                    int32_t num_pages, int32_t max_pos, pa_dtype_t dtype,
+                                    void* stream) {
+  if (!dtype_ok(dtype) || T < 0 || Hq < 0 || Hkv < 1 || head_dim < 1 || page_size < 1 ||
+      num_pages < 1)
+    return PA_ERR_INVALID_ARG;
+  if ((long)num_pages * page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (q && Hq < 1) return PA_ERR_INVALID_ARG;
+  if (cos_sin && max_pos < 1) return PA_ERR_INVALID_ARG;
+  if (head_dim % 16) return PA_ERR_UNSUPPORTED;  // 16-byte vectors on each half row
+  if (T == 0) return PA_OK;
+  if (!k || !v || !positions || !slot_mapping || !k_pool || !v_pool) return PA_ERR_INVALID_ARG;
+  if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || (cos_sin && !aligned16(cos_sin)))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(launch_rope_cache_write(dtype, q, k, v, positions, slot_mapping, cos_sin,
+                                          k_pool, v_pool, T, Hq, Hkv, head_dim, page_size,
+                                          num_pages, max_pos, (hipStream_t)stream));
+}
+
+size_t pa_paged_attention_workspace_size(int32_t S, int32_t T, int32_t Hq, int32_t head_dim,
+                                         int32_t max_query_len, int32_t max_seq_len,
+                                         int32_t page_size, int32_t kv_split_tokens,
+                                         pa_dtype_t dtype) {
+  if (S < 0 || T < 0 || Hq < 1 || head_dim < 1 || page_size < 1 || max_seq_len < 0 ||
+      max_query_len < 0 || !dtype_ok(dtype) || kv_split_tokens < 0)
+    return 0;
+  return workspace_bytes_for(S, T, Hq, head_dim, max_query_len, max_seq_len, page_size,
+                             kv_split_tokens, dtype);
+}
+
+pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      const int32_t* query_start_loc, void* out, int32_t S,
+                                      int32_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t max_blocks_per_seq, int32_t max_query_len,
+                                      int32_t max_seq_len, float scale, int32_t kv_split_tokens,
+                                      pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!dtype_ok(dtype) || S < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || head_dim < 1 ||
+      page_size < 1 || num_pages < 1 || max_blocks_per_seq < 1 || max_query_len < 0 ||
+      max_seq_len < 0 || !isfinite(scale))
+    return PA_ERR_INVALID_ARG;
+  if (kv_split_tokens != 0 && (kv_split_tokens < 16 || kv_split_tokens > 65536 ||
+                               kv_split_tokens % 16))
+    return PA_ERR_INVALID_ARG;
+  if ((long)num_pages * page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const int G = Hq / Hkv;
+  if (page_size % 16 || !decode_supported(dtype, head_dim, G)) return PA_ERR_UNSUPPORTED;
+  if (T == 0 || S == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  const size_t eb = (size_t)elem_bytes(dtype);
+  const size_t qbytes = (size_t)T * Hq * head_dim * eb;
+  const size_t pool_bytes = (size_t)num_pages * page_size * Hkv * head_dim * eb;
+  if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_pool, pool_bytes) ||
+      overlap(out, qbytes, v_pool, pool_bytes))
+    return PA_ERR_INVALID_ARG;
+  const size_t need = workspace_bytes_for(S, T, Hq, head_dim, max_query_len, max_seq_len,
+                                          page_size, kv_split_tokens, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && ((uintptr_t)workspace & 3u)) return PA_ERR_INVALID_ARG;
+
+  AttnArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.out = out;
+  a.ws = (float*)workspace;
+  a.S = S;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = head_dim;
+  a.P = page_size;
+  a.num_pages = num_pages;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.part_tokens = split_tokens(kv_split_tokens, page_size);
+  a.max_parts = max_seq_len > 0 ? (max_seq_len + a.part_tokens - 1) / a.part_tokens : 1;
+  if (a.max_parts < 1) a.max_parts = 1;
+  a.scale_log2e = scale * kLog2e;
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool token_mode = !use_mfma_prefill(dtype, head_dim, max_query_len);
+  hipError_t e = launch_decode(dtype, a, token_mode, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (a.max_parts > 1) {
+    e = launch_split_reduce(dtype, a, token_mode, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  if (!token_mode && max_query_len > 1) {
+    e = launch_prefill_mfma(dtype, a, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+pa_status_t pa_profile_start(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return PA_ERR_INVALID_ARG;
+  g_prof_on = false;
+  destroy_events();
+  g_recs.resize(capacity);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&g_recs[i].start) != hipSuccess ||
+        hipEventCreate(&g_recs[i].stop) != hipSuccess) {
+      g_recs.resize(i);
+      return PA_ERR_HIP;
+    }
+    g_recs[i].name = "";
+  }
+  g_prof_n = 0;
+  g_prof_on = true;
+  return PA_OK;
+}
+
+pa_status_t pa_profile_stop(int32_t* num_records) {
+  g_prof_on = false;
+  if (num_records) *num_records = g_prof_n;
+  if (g_prof_n > 0 && hipEventSynchronize(g_recs[g_prof_n - 1].stop) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
+pa_status_t pa_profile_get(int32_t index, char* name, int32_t name_len, float* milliseconds) {
+  if (index < 0 || index >= g_prof_n) return PA_ERR_INVALID_ARG;
+  if (name && name_len > 0) {
+    strncpy(name, g_recs[index].name, (size_t)name_len - 1);
+    name[name_len - 1] = '\0';
+  }
+  if (milliseconds) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_recs[index].start, g_recs[index].stop) != hipSuccess)
+      return PA_ERR_HIP;
+    *milliseconds = ms;
+  }
+  return PA_OK;
+}
+
+pa_status_t pa_profile_reset(void) {
+  g_prof_on = false;
+  destroy_events();
+  return PA_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

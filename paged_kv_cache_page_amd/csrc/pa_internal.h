@@ -1,0 +1,56 @@
+// Host-side launch interface between the C ABI (pa_api.hip) and the kernel
+// translation units. Nothing here is exported from libpa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+// Arguments of the attention kernels. All pointers are device memory.
+struct AttnArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  void* out;
+  float* ws;           // split-KV partials: o [rows*max_parts*Hq*D], then (m, l) pairs
+  int32_t S, T, Hq, Hkv, D, P, num_pages, max_blocks;
+  int32_t max_query_len, max_seq_len;
+  int32_t part_tokens;  // keys per split-KV partition
+  int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / part_tokens))
+  float scale_log2e;    // scale * log2(e): weights are exp2(s * scale_log2e - m)
+};
+
+// Kernel timing hook (pa_api.hip): called around every launch.
+void profile_before(const char* name, hipStream_t stream);
+void profile_after(hipStream_t stream);
+
+// K0 / a1 / K1 (pa_rope_cache.hip)
+hipError_t launch_rope_table(float* out, int max_pos, int D, double theta, hipStream_t s);
+hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* qsl, const int32_t* pos,
+                               int32_t* slots, int S, int T, int max_blocks, int P,
+                               int num_pages, hipStream_t s);
+hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* v,
+                                   const int32_t* pos, const int32_t* slots, const float* cs,
+                                   void* k_pool, void* v_pool, int T, int Hq, int Hkv, int D,
+                                   int P, int num_pages, int max_pos, hipStream_t s);
+
+// K2 + K3 (pa_decode.hip). token_mode = false: one row per decode sequence
+// (query length 1; other sequences skipped). token_mode = true: one row per
+// query token of every sequence (the VALU path for prefill rows).
+bool decode_supported(pa_dtype_t dt, int D, int G);
+hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipStream_t s);
+hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
+                               hipStream_t s);
+
+// K4 (pa_prefill.hip): MFMA prefill-chunk attention for sequences with L > 1.
+bool prefill_mfma_supported(pa_dtype_t dt, int D, int G);
+hipError_t launch_prefill_mfma(pa_dtype_t dt, const AttnArgs& a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,289 @@
+// K4: prefill-chunk paged attention on bf16 matrix cores (gfx950 MFMA).
+//
+// A chunk of L rows attends every earlier key in full and itself causally
+// (llm-serving-engine README, "_step_prefill": write K/V at the chunk start,
+// gather the prior K/V, apply the rectangular causal mask). With L rows, G
+// query heads per KV head and n keys the work is about 4*D*G*L*n flops over
+// 2*D*n*2 bytes of K/V per KV head: a dense contraction, so it runs on MFMA.
+//
+// Workgroup = 4 waves = 128 query rows of one KV head: row r is token r / G
+// of the tile and query head r % G, so each K/V tile is read once for the
+// whole GQA group. Each wave owns 32 rows (two 16-row blocks).
+//
+// Per 32-key tile (K row-major and V transposed, staged in LDS):
+//   S^T[key, row] = K[key, :] . Q[row, :]        v_mfma_f32_16x16x32_bf16, A = K, B = Q^T
+//   online softmax on S^T columns (one query row per lane column)
+//   O^T[dim, row] += V^T[dim, key] . P^T[key, row]   A = V^T (LDS), B = P^T (registers)
+// Computing the transposed products keeps a query row's scores, running max,
+// running sum and output column in the same lanes, so no transposes or
+// shuffles are needed between the two products: the S^T accumulator of a lane
+// (4 keys of each 16-key half, one query row) is exactly the P^T operand the
+// second MFMA needs, once the contraction's key order is defined to match.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerWg = kPfWaves * kRowsPerWave;  // 128
+constexpr int kBN = 32;                                // keys per tile
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(AttnArgs a, int n_mtiles) {
+  constexpr int TM = kRowsPerWg / G;    // tokens per workgroup
+  constexpr int DSTEPS = D / 32;        // k-steps of the QK^T product
+  constexpr int DBLK = D / 16;          // 16-dim output blocks
+  constexpr int KSTR = D + 8;           // LDS row stride of K (elements), 16-byte pad
+  constexpr int VSTR = kBN + 4;         // LDS row stride of V^T (elements), 8-byte pad
+  constexpr int C16 = D / 8;            // 16-byte chunks per head row
+
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VSTR];
+
+  const int bid = blockIdx.x;
+  const int kvh = bid % a.Hkv;
+  const int rest = bid / a.Hkv;
+  const int mt = rest % n_mtiles;
+  const int s = rest / n_mtiles;
+
+  const int q0 = a.qsl[s];
+  const int L = a.qsl[s + 1] - q0;
+  if (L <= 1) return;                   // decode rows belong to the decode kernel
+  const int i0 = mt * TM;
+  if (i0 >= L || q0 < 0 || q0 + L > a.T) return;
+  const int i1 = min(L, i0 + TM);
+  int n = a.seq_lens[s];
+  n = min(n, a.max_blocks * a.P);
+  if (n < L) return;                    // malformed row: nothing sensible to compute
+  const int kmax = n - L + i1;          // keys visible to the tile's last row
+  const int ntiles = (kmax + kBN - 1) / kBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;            // query row within a 16-row block
+  const int grp = lane >> 4;            // 0..3
+
+  const size_t row_bytes = (size_t)D * 2;
+  const int Hq = a.Hq;
+
+  // Q^T operand: rows of this lane, 8 dims per k-step.
+  uint4 qop[2][DSTEPS];
+  int tok[2], head[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int r = wave * kRowsPerWave + mb * 16 + col;
+    tok[mb] = i0 + r / G;
+    head[mb] = kvh * G + r % G;
+    const bool ok = tok[mb] < i1;
+    const char* qrow = (const char*)a.q + ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * row_bytes;
+#pragma unroll
+    for (int ds = 0; ds < DSTEPS; ++ds) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (ok) x = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
+      qop[mb][ds] = x;
+    }
+  }
+
+  f32x4_t acc_o[2][DBLK];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    m_run[mb] = kNegBig;
+    l_run[mb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) acc_o[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
+  const char* kpool = (const char*)a.k_pool + (size_t)kvh * row_bytes;
+  const char* vpool = (const char*)a.v_pool + (size_t)kvh * row_bytes;
+  const size_t slot_stride = (size_t)a.Hkv * row_bytes;
+  const int P = a.P;
+  const float sl2e = a.scale_log2e;
+  const int last_key = n - L;           // row i sees keys <= last_key + i
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int kb0 = kt * kBN;
+    // ---- stage K (row-major) ----
+    for (int c = tid; c < kBN * C16; c += kPfThreads) {
+      const int key = c / C16;
+      const int d8 = c % C16;
+      const int j = kb0 + key;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (j < kmax) {
+        const int page = clampi(bt_row[j / P], 0, a.num_pages - 1);
+        x = *reinterpret_cast<const uint4*>(kpool + ((size_t)page * P + j % P) * slot_stride +
+                                            d8 * 16);
+      }
+      *reinterpret_cast<uint4*>(&s_k[key * KSTR + d8 * 8]) = x;
+    }
+    // ---- stage V transposed: two keys per 32-bit LDS word ----
+    for (int c = tid; c < (kBN / 2) * C16; c += kPfThreads) {
+      const int kp = c % (kBN / 2);
+      const int d8 = c / (kBN / 2);
+      const int j = kb0 + 2 * kp;
+      uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+      if (j < kmax) {
+        const int page = clampi(bt_row[j / P], 0, a.num_pages - 1);
+        xa = *reinterpret_cast<const uint4*>(vpool + ((size_t)page * P + j % P) * slot_stride +
+                                             d8 * 16);
+      }
+      if (j + 1 < kmax) {
+        const int page = clampi(bt_row[(j + 1) / P], 0, a.num_pages - 1);
+        xb = *reinterpret_cast<const uint4*>(vpool + ((size_t)page * P + (j + 1) % P) *
+                                                         slot_stride + d8 * 16);
+      }
+      const uint32_t* wa = reinterpret_cast<const uint32_t*>(&xa);
+      const uint32_t* wb = reinterpret_cast<const uint32_t*>(&xb);
+      uint32_t* vt = reinterpret_cast<uint32_t*>(s_vt);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d = d8 * 8 + 2 * w;
+        vt[(d * VSTR) / 2 + kp] = (wa[w] & 0xFFFFu) | (wb[w] << 16);
+        vt[((d + 1) * VSTR) / 2 + kp] = (wa[w] >> 16) | (wb[w] & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for this wave's two row blocks ----
+    f32x4_t st[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) st[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < DSTEPS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 kop =
+            *reinterpret_cast<const uint4*>(&s_k[(kb * 16 + col) * KSTR + ds * 32 + grp * 8]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) st[mb][kb] = mfma16x16x32(kop, qop[mb][ds], st[mb][kb]);
+      }
+    }
+
+    // ---- online softmax per query row (this lane's column) ----
+    uint4 pop[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int limit = min(last_key + tok[mb], n - 1);
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = kb0 + kb * 16 + grp * 4 + i;
+          const float x = (j <= limit) ? st[mb][kb][i] * sl2e : -INFINITY;
+          sv[kb * 4 + i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(m_run[mb], tmax);
+      const float corr = fast_exp2(m_run[mb] - mn);
+      m_run[mb] = mn;
+      float psum = 0.f;
+      float pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pv[k] = fast_exp2(sv[k] - mn);
+        psum += pv[k];
+      }
+      l_run[mb] = l_run[mb] * corr + psum;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        acc_o[mb][db][0] *= corr;
+        acc_o[mb][db][1] *= corr;
+        acc_o[mb][db][2] *= corr;
+        acc_o[mb][db][3] *= corr;
+      }
+      pop[mb] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+    }
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int d = db * 16 + col;
+      const uint2 lo = *reinterpret_cast<const uint2*>(&s_vt[d * VSTR + grp * 4]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&s_vt[d * VSTR + 16 + grp * 4]);
+      const uint4 vop = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) acc_o[mb][db] = mfma16x16x32(vop, pop[mb], acc_o[mb][db]);
+    }
+    __syncthreads();  // tiles consumed before the next staging overwrites them
+  }
+
+  // ---- normalise and store ----
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    float lt = l_run[mb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (tok[mb] >= i1) continue;
+    const float inv = 1.f / lt;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
+                     ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const uint2 w = make_uint2(pack_bf16x2(acc_o[mb][db][0] * inv, acc_o[mb][db][1] * inv),
+                                 pack_bf16x2(acc_o[mb][db][2] * inv, acc_o[mb][db][3] * inv));
+      *reinterpret_cast<uint2*>(orow + db * 16 + grp * 4) = w;
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_pf(const AttnArgs& a, hipStream_t s) {
+  constexpr int TM = kRowsPerWg / G;
+  const int n_mtiles = (a.max_query_len + TM - 1) / TM;
+  const long blocks = (long)a.S * n_mtiles * a.Hkv;
+  if (blocks == 0) return hipSuccess;
+  profile_before("prefill_attention_mfma", s);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3((unsigned)blocks), dim3(kPfThreads), 0,
+                     s, a, n_mtiles);
+  profile_after(s);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pf_d(const AttnArgs& a, int G, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_pf<D, 1>(a, s);
+    case 2: return launch_pf<D, 2>(a, s);
+    case 4: return launch_pf<D, 4>(a, s);
+    case 8: return launch_pf<D, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(pa_dtype_t dt, int D, int /*G*/) {
+  return dt == PA_BF16 && (D == 64 || D == 128);
+}
+
+hipError_t launch_prefill_mfma(pa_dtype_t dt, const AttnArgs& a, hipStream_t s) {
+  if (dt != PA_BF16) return hipErrorInvalidValue;
+  const int G = a.Hq / a.Hkv;
+  if (a.D == 64) return launch_pf_d<64>(a, G, s);
+  if (a.D == 128) return launch_pf_d<128>(a, G, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,203 @@
+// K0: RoPE cos/sin table. a1: slot mapping. K1: RoPE on the new Q/K + page write.
+//
+// K1 is HBM-bound (about 0.1 flop per byte): one workgroup per new token moves
+// its Q/K rows through registers once (read, rotate, write back in place) and
+// stores K/V into the token's page slot with 16-byte vector accesses.
+//
+// This translation unit is compiled with -ffp-contract=off, and K1 also
+// disables contraction locally: the rotation must round each product and each
+// sum on its own, so the stored K is a fixed function of its inputs.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------- K0 -------
+// cos/sin of p * theta^(-2i/D), evaluated in double and rounded once to float.
+__global__ __launch_bounds__(256) void rope_table_kernel(float* __restrict__ out, int max_pos,
+                                                         int D, double theta) {
+  const int half = D / 2;
+  const long total = (long)max_pos * half;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (long)gridDim.x * blockDim.x) {
+    const int p = (int)(idx / half);
+    const int i = (int)(idx % half);
+    const double inv = pow(theta, -(2.0 * i) / (double)D);
+    const double ang = (double)p * inv;
+    out[(size_t)p * D + i] = (float)cos(ang);
+    out[(size_t)p * D + half + i] = (float)sin(ang);
+  }
+}
+
+hipError_t launch_rope_table(float* out, int max_pos, int D, double theta, hipStream_t s) {
+  const long total = (long)max_pos * (D / 2);
+  long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  profile_before("rope_table", s);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, max_pos,
+                     D, theta);
+  profile_after(s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- a1 -------
+// Token t belongs to the last sequence s with qsl[s] <= t (empty sequences
+// have qsl[s] == qsl[s+1] and are passed over by the search).
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ pos, int32_t* __restrict__ slots, int S, int T, int max_blocks,
+    int P, int num_pages) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = S;  // qsl[lo] <= t < qsl[hi] when the metadata is well formed
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int p = pos[t];
+  int slot = -1;
+  if (p >= 0) {
+    const int blk = p / P;
+    if (blk < max_blocks) {
+      const int page = bt[(size_t)lo * max_blocks + blk];
+      if (page >= 0 && page < num_pages) slot = page * P + p % P;
+    }
+  }
+  slots[t] = slot;
+}
+
+hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* qsl, const int32_t* pos,
+                               int32_t* slots, int S, int T, int max_blocks, int P,
+                               int num_pages, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  profile_before("slot_mapping", s);
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((T + 255) / 256), dim3(256), 0, s, bt, qsl, pos,
+                     slots, S, T, max_blocks, P, num_pages);
+  profile_after(s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- K1 -------
+// One 16-byte vector of the first half of a head row and the matching vector of
+// the second half: VP rotation pairs.
+template <typename ET>
+struct RotPair;
+
+template <>
+struct RotPair<BF16> {
+  static constexpr int VP = 8;
+  __device__ static void rotate(uint4& a, uint4& b, const float* c, const float* s) {
+#pragma clang fp contract(off)
+    uint32_t* aw = reinterpret_cast<uint32_t*>(&a);
+    uint32_t* bw = reinterpret_cast<uint32_t*>(&b);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float x1l = bf16_lo(aw[w]), x1h = bf16_hi(aw[w]);
+      const float x2l = bf16_lo(bw[w]), x2h = bf16_hi(bw[w]);
+      const float cl = c[2 * w], ch = c[2 * w + 1], sl = s[2 * w], sh = s[2 * w + 1];
+      const float p1l = x1l * cl, q1l = x2l * sl, p2l = x2l * cl, q2l = x1l * sl;
+      const float p1h = x1h * ch, q1h = x2h * sh, p2h = x2h * ch, q2h = x1h * sh;
+      aw[w] = pack_bf16x2(p1l - q1l, p1h - q1h);
+      bw[w] = pack_bf16x2(p2l + q2l, p2h + q2h);
+    }
+  }
+};
+
+template <>
+struct RotPair<F32> {
+  static constexpr int VP = 4;
+  __device__ static void rotate(uint4& a, uint4& b, const float* c, const float* s) {
+#pragma clang fp contract(off)
+    float* x1 = reinterpret_cast<float*>(&a);
+    float* x2 = reinterpret_cast<float*>(&b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p1 = x1[i] * c[i], q1 = x2[i] * s[i];
+      const float p2 = x2[i] * c[i], q2 = x1[i] * s[i];
+      x1[i] = p1 - q1;
+      x2[i] = p2 + q2;
+    }
+  }
+};
+
+template <typename ET>
+__global__ __launch_bounds__(256) void rope_cache_write_kernel(
+    char* __restrict__ q, char* __restrict__ k, const char* __restrict__ v,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ slots,
+    const float* __restrict__ cs, char* __restrict__ k_pool, char* __restrict__ v_pool, int Hq,
+    int Hkv, int D, int P, int num_pages, int max_pos) {
+  constexpr int EB = ET::kBytes;
+  constexpr int VP = RotPair<ET>::VP;       // elements per 16-byte vector
+  const int t = blockIdx.x;
+  const int half = D / 2;
+  const int vec_half = half / VP;           // vectors per half row
+  const int vec_row = D / VP;               // vectors per row
+  const size_t row_bytes = (size_t)D * EB;
+  const int p = pos[t];
+  const bool rotate = cs != nullptr && p >= 0 && p < max_pos;
+  const long slot = slots[t];
+  const bool store = slot >= 0 && slot < (long)num_pages * P;
+  const int nq = q ? Hq : 0;
+  const int rot_tasks = (nq + Hkv) * vec_half;
+  const int tasks = rot_tasks + Hkv * vec_row;
+  for (int task = threadIdx.x; task < tasks; task += blockDim.x) {
+    if (task < rot_tasks) {
+      const int h = task / vec_half;
+      const int c = task % vec_half;
+      const bool is_k = h >= nq;
+      const int kh = h - nq;
+      char* row = is_k ? k + ((size_t)t * Hkv + kh) * row_bytes
+                       : q + ((size_t)t * Hq + h) * row_bytes;
+      uint4* p1 = reinterpret_cast<uint4*>(row + (size_t)c * 16);
+      uint4* p2 = reinterpret_cast<uint4*>(row + (size_t)half * EB + (size_t)c * 16);
+      uint4 a = *p1, b = *p2;
+      if (rotate) {
+        float cv[VP], sv[VP];
+        const float4* cp = reinterpret_cast<const float4*>(cs + (size_t)p * D + c * VP);
+        const float4* sp = reinterpret_cast<const float4*>(cs + (size_t)p * D + half + c * VP);
+#pragma unroll
+        for (int i = 0; i < VP / 4; ++i) {
+          const float4 cc = cp[i], ss = sp[i];
+          cv[4 * i] = cc.x; cv[4 * i + 1] = cc.y; cv[4 * i + 2] = cc.z; cv[4 * i + 3] = cc.w;
+          sv[4 * i] = ss.x; sv[4 * i + 1] = ss.y; sv[4 * i + 2] = ss.z; sv[4 * i + 3] = ss.w;
+        }
+        RotPair<ET>::rotate(a, b, cv, sv);
+        *p1 = a;
+        *p2 = b;
+      }
+      if (is_k && store) {
+        char* dst = k_pool + ((size_t)slot * Hkv + kh) * row_bytes;
+        *reinterpret_cast<uint4*>(dst + (size_t)c * 16) = a;
+        *reinterpret_cast<uint4*>(dst + (size_t)half * EB + (size_t)c * 16) = b;
+      }
+    } else if (store) {
+      const int j = task - rot_tasks;
+      const int h = j / vec_row;
+      const int c = j % vec_row;
+      const uint4 x =
+          *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + h) * row_bytes + (size_t)c * 16);
+      *reinterpret_cast<uint4*>(v_pool + ((size_t)slot * Hkv + h) * row_bytes + (size_t)c * 16) = x;
+    }
+  }
+}
+
+hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* v,
+                                   const int32_t* pos, const int32_t* slots, const float* cs,
+                                   void* k_pool, void* v_pool, int T, int Hq, int Hkv, int D,
+                                   int P, int num_pages, int max_pos, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  profile_before("rope_cache_write", s);
+  if (dt == PA_BF16) {
+    hipLaunchKernelGGL(rope_cache_write_kernel<BF16>, dim3(T), dim3(256), 0, s, (char*)q,
+                       (char*)k, (const char*)v, pos, slots, cs, (char*)k_pool, (char*)v_pool,
+                       Hq, Hkv, D, P, num_pages, max_pos);
+  } else {
+    hipLaunchKernelGGL(rope_cache_write_kernel<F32>, dim3(T), dim3(256), 0, s, (char*)q,
+                       (char*)k, (const char*)v, pos, slots, cs, (char*)k_pool, (char*)v_pool,
+                       Hq, Hkv, D, P, num_pages, max_pos);
+  }
+  profile_after(s);
+  return hipGetLastError();
+}
+
+}  // namespace pa

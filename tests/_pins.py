@@ -162,8 +162,8 @@ def pin_large_logits(impl):
 def one_hot_tick(seed, dtype=W.F32, Hq=4, Hkv=2, D=8, P=4, seq_lens=(9, 14, 6),
                  query_lens=(1, 3, 1)):
     """K/V built so every query row's weight is exactly 1 on one chosen key and
-    exactly 0 elsewhere (gaps of >= 800 in the logit), and V encodes the key's
-    (page, row) as exact small integers."""
+    exactly 0 elsewhere (logit gaps of 1024), and V holds the key's page id, its
+    index and its row in the page as exact small integers."""
     t = tiny_tick(seed, Hq=Hq, Hkv=Hkv, D=D, P=P, seq_lens=seq_lens, query_lens=query_lens,
                   dtype=dtype)
     rng = np.random.default_rng(seed + 1)
@@ -177,8 +177,9 @@ def one_hot_tick(seed, dtype=W.F32, Hq=4, Hkv=2, D=8, P=4, seq_lens=(9, 14, 6),
             page, row = int(t.block_tables[s][j // P]), j % P
             kp[page, row, :, j % D] = 1.0       # key j points along axis j % D
             kp[page, row, :, (j + 1) % D] = -0.5
-            vp[page, row, :, :] = page * P + row
+            vp[page, row, :, 0] = page           # small integers: exact in bf16
             vp[page, row, :, 1] = j
+            vp[page, row, :, 2] = row
         for i in range(L):
             last = n - L + i
             j = int(rng.integers(0, last + 1))
@@ -199,7 +200,7 @@ def pin_one_hot_probe(impl):
     for s, i, j in targets:
         page, row = int(t.block_tables[s][j // t.P]), j % t.P
         row_out = got[t.qsl[s] + i]
-        assert np.all(row_out[:, 0] == page * t.P + row), (s, i, j)
+        assert np.all(row_out[:, 0] == page) and np.all(row_out[:, 2] == row), (s, i, j)
         assert np.all(row_out[:, 1] == j)
 
 

@@ -1,0 +1,163 @@
+"""The C ABI on the CPU: libpa.so loads, exports every entry point that
+include/pa.h declares, and rejects bad host arguments before any HIP call
+(no GPU needed, no kernel launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_page_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+F32, BF16 = pa.PA_F32, pa.PA_BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points_the_binding_knows():
+    names = declared_functions()
+    assert "pa_rope_and_cache_write" in names and "pa_paged_attention_varlen" in names
+    assert set(names) == set(pa.SIGNATURES), set(names) ^ set(pa.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_nothing_else():
+    # the dynamic symbol table lists only the pa_* API as defined functions
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {f for f in funcs if f.startswith("pa_")} == set(declared_functions())
+    assert not [f for f in funcs if f.startswith("_ZN2pa")], "internal C++ symbols leaked"
+
+
+def test_status_strings_and_version():
+    assert pa.pa_abi_version() == 1
+    for code in range(5):
+        assert pa.pa_status_string(code).startswith("PA_")
+    assert "UNKNOWN" in pa.pa_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x10000)      # an aligned non-null pointer; never dereferenced here
+
+
+def attn(**kw):
+    args = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, bt=FAKE, seq_lens=FAKE, qsl=FAKE,
+                out=ctypes.c_void_p(0x900000000), S=4, T=4, Hq=8, Hkv=2, D=128, P=256,
+                num_pages=64, max_blocks=16, max_query_len=1, max_seq_len=256, scale=0.1,
+                split=0, dtype=BF16, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_paged_attention_varlen(
+        a["q"], a["k_pool"], a["v_pool"], a["bt"], a["seq_lens"], a["qsl"], a["out"], a["S"],
+        a["T"], a["Hq"], a["Hkv"], a["D"], a["P"], a["num_pages"], a["max_blocks"],
+        a["max_query_len"], a["max_seq_len"], a["scale"], a["split"], a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(Hkv=0), INVALID),
+    (dict(num_pages=0), INVALID),
+    (dict(max_blocks=0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(split=8), INVALID),
+    (dict(split=100), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(D=16), UNSUPPORTED),                # bf16 needs D in {64, 128}
+    (dict(P=24), UNSUPPORTED),
+    (dict(Hq=32, Hkv=2), UNSUPPORTED),        # group 16
+    (dict(q=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(q=ctypes.c_void_p(0x10008)), INVALID),   # not 16-byte aligned
+    (dict(out=FAKE), INVALID),                     # out aliases q
+    (dict(max_seq_len=4096), WS_SMALL),            # needs split-KV scratch
+    (dict(num_pages=2 ** 30, P=256), INVALID),     # slot index would overflow int32
+])
+def test_attention_rejects_bad_host_arguments(kw, code):
+    assert attn(**kw) == code
+
+
+def test_attention_empty_tick_is_ok_without_touching_memory():
+    assert attn(T=0) == OK
+    assert attn(S=0, T=0) == OK
+
+
+def test_workspace_size_query():
+    lib = pa.lib()
+    # one partition: no scratch
+    assert lib.pa_paged_attention_workspace_size(64, 64, 32, 128, 1, 512, 256, 0, BF16) == 0
+    # 4096 keys in 512-key partitions: 8 partials of (D + 2) floats per (row, head)
+    n = lib.pa_paged_attention_workspace_size(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
+    assert n == 64 * 8 * 32 * 130 * 4
+    # explicit split of 1024 keys halves it
+    assert lib.pa_paged_attention_workspace_size(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == n // 2
+    # fp32 with prefill rows takes the per-token path: one row per token
+    m = lib.pa_paged_attention_workspace_size(4, 40, 4, 16, 20, 1024, 16, 0, F32)
+    assert m == 40 * 2 * 4 * 18 * 4
+    assert lib.pa_paged_attention_workspace_size(-1, 4, 4, 16, 1, 64, 16, 0, F32) == 0
+
+
+def cache_write(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, slots=FAKE, cs=FAKE, kp=FAKE, vp=FAKE, T=4,
+                Hq=8, Hkv=2, D=128, P=16, num_pages=8, max_pos=64, dtype=BF16, stream=None)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_rope_and_cache_write(a["q"], a["k"], a["v"], a["pos"], a["slots"], a["cs"],
+                                            a["kp"], a["vp"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                            a["P"], a["num_pages"], a["max_pos"], a["dtype"],
+                                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(Hkv=0), INVALID),
+    (dict(dtype=3), INVALID),
+    (dict(k=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(slots=None), INVALID),
+    (dict(kp=None), INVALID),
+    (dict(max_pos=0), INVALID),
+    (dict(Hq=0), INVALID),                       # q given but no query heads
+    (dict(D=40), UNSUPPORTED),
+    (dict(k=ctypes.c_void_p(0x10004)), INVALID),
+])
+def test_cache_write_rejects_bad_host_arguments(kw, code):
+    assert cache_write(**kw) == code
+
+
+def test_cache_write_empty_is_ok():
+    assert cache_write(T=0) == OK
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = pa.lib()
+    assert lib.pa_rope_cos_sin_table(None, 16, 64, 1e4, None) == INVALID
+    assert lib.pa_rope_cos_sin_table(FAKE, 0, 64, 1e4, None) == INVALID
+    assert lib.pa_rope_cos_sin_table(FAKE, 16, 63, 1e4, None) == INVALID
+    assert lib.pa_rope_cos_sin_table(FAKE, 16, 64, -1.0, None) == INVALID
+    assert lib.pa_compute_slot_mapping(FAKE, FAKE, FAKE, FAKE, 2, 4, 0, 16, 8, None) == INVALID
+    assert lib.pa_compute_slot_mapping(None, FAKE, FAKE, FAKE, 2, 4, 4, 16, 8, None) == INVALID
+    assert lib.pa_compute_slot_mapping(None, None, None, None, 0, 0, 4, 16, 8, None) == OK
+    assert lib.pa_profile_start(0) == INVALID
+    assert lib.pa_profile_get(0, None, 0, None) == INVALID
+    assert lib.pa_profile_reset() == OK

@@ -1,0 +1,196 @@
+"""GPU parity of paged attention over packed ticks (decode K2/K3, prefill K4 and
+the per-token VALU path) against the oracle, plus the invariants that must hold
+exactly on the GPU: page relabelling, shared prefix pages, packing order and
+the one-hot position probe."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_page_amd as pa
+from paged_kv_cache_page_amd import workloads as W
+from _gpu import (DEV, DevTick, check_attention, host_f32, host_storage, i32, run_gpu_tick, say,
+                  storage_tensor)
+import _pins
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_tick(t):
+    table = oracle.rope_table(t.max_pos, t.D, t.theta) if t.theta is not None else None
+    if t.new_in_pool:
+        return oracle.paged_attention_varlen(t.q, t.k_pool, t.v_pool, t.block_tables,
+                                             t.seq_lens, t.qsl, t.scale, t.dtype)
+    return oracle.run_tick(t.dtype, t.q, t.k, t.v, t.positions, t.block_tables, t.qsl,
+                           t.seq_lens, t.k_pool, t.v_pool, table, t.scale)["out"]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity(cfg):
+    """The five workloads end to end (table, slots, RoPE + write, attention),
+    unused slots and pages poisoned with NaN."""
+    t = W.make_config(cfg, poison=True)
+    say("config", cfg, t.name, "S", t.S, "T", t.T)
+    _, out = run_gpu_tick(t)
+    stats = check_attention(out, oracle_tick(t), t.dtype, t.name)
+    say("config", cfg, stats)
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_full_size_bench_launch_unpoisoned(cfg):
+    """The bench's launch configuration (default split, unpoisoned pools)."""
+    t = W.make_config(cfg, poison=False)
+    say("unpoisoned config", cfg)
+    _, out = run_gpu_tick(t)
+    check_attention(out, oracle_tick(t), t.dtype, t.name)
+
+
+def _small(seed, dtype=W.BF16, Hq=8, Hkv=2, D=128, P=16, seq_lens=(40, 300, 17, 129),
+           query_lens=(1, 1, 17, 33), theta=1e4, poison=True):
+    rng = np.random.default_rng(seed)
+    return W.build_tick(rng, name=f"small{seed}", dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, P=P,
+                        seq_lens=list(seq_lens), query_lens=list(query_lens), theta=theta,
+                        poison=poison)
+
+
+SMALL_CASES = [
+    # (dtype, Hq, Hkv, D, P, seq_lens, query_lens)
+    (W.BF16, 8, 2, 128, 16, (40, 300, 17, 129), (1, 1, 17, 33)),      # mixed, chunk from scratch
+    (W.BF16, 32, 4, 64, 16, (33, 500, 64, 47), (1, 1, 30, 47)),       # TinyLlama shape
+    (W.BF16, 8, 8, 128, 256, (1, 257, 600, 1000), (1, 1, 88, 129)),   # group 1, n = 1
+    (W.BF16, 16, 2, 64, 32, (5, 70, 200), (5, 1, 131)),               # group 8
+    (W.BF16, 4, 2, 128, 16, (16, 32, 48), (16, 16, 16)),              # page-aligned chunks
+    (W.F32, 4, 2, 16, 16, (5, 17, 33, 64), (1, 3, 1, 20)),            # fp32 prefill (token path)
+    (W.F32, 8, 1, 64, 16, (100, 3, 700), (1, 3, 65)),
+    (W.F32, 8, 4, 128, 32, (90, 190), (1, 45)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_small_packed_ticks(case):
+    dtype, Hq, Hkv, D, P, sl, ql = SMALL_CASES[case]
+    t = _small(100 + case, dtype, Hq, Hkv, D, P, sl, ql, theta=1e4 if case % 2 else 1e6)
+    say("small case", case, dtype, Hq, Hkv, D, P, sl, ql)
+    _, out = run_gpu_tick(t)
+    check_attention(out, oracle_tick(t), t.dtype, f"case{case}")
+
+
+@pytest.mark.parametrize("split", [16, 32, 112, 512, 4096, 65536])
+def test_split_count_invariance(split):
+    t = _small(7, seq_lens=(2000, 1, 700, 300), query_lens=(1, 1, 1, 120))
+    say("split", split)
+    _, out = run_gpu_tick(t, kv_split_tokens=split)
+    check_attention(out, oracle_tick(t), t.dtype, f"split{split}")
+
+
+def test_page_permutation_bitwise():
+    t = W.make_config(4, poison=True)
+    say("page permutation")
+    _, a = run_gpu_tick(t)
+    u = W.permute_pages(t, np.random.default_rng(5))
+    _, b = run_gpu_tick(u)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    t = W.make_config(5, poison=True)
+    d = DevTick(t).write()
+    a = d.attend()
+    torch.cuda.synchronize()
+    # give every sharing sequence its own copy of the prefix pages
+    bt = t.block_tables.copy()
+    kp, vp = d.k_pool, d.v_pool
+    extra = []
+    nxt = t.num_pages
+    for s in range(32):
+        for b in range(len(t.shared_pages)):
+            extra.append(int(bt[s, b]))
+            bt[s, b] = nxt
+            nxt += 1
+    idx = torch.tensor(extra, device=DEV, dtype=torch.long)
+    kp2 = torch.cat([kp, kp[idx]])
+    vp2 = torch.cat([vp, vp[idx]])
+    say("shared prefix vs private copies")
+    b_out = pa.pa_paged_attention_varlen(d.q, kp2, vp2, i32(bt), d.seq_lens, d.qsl,
+                                         t.max_query_len, t.max_seq_len, scale=t.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b_out.view(torch.int16))
+
+
+def _subset_tick(t, seqs):
+    """The same sequences as their own packed tick (rows copied, pools shared)."""
+    u = W.Tick(**{**t.__dict__})
+    seqs = list(seqs)
+    u.seq_lens = t.seq_lens[seqs]
+    u.query_lens = t.query_lens[seqs]
+    u.block_tables = t.block_tables[seqs]
+    u.qsl = np.zeros(len(seqs) + 1, np.int32)
+    u.qsl[1:] = np.cumsum(u.query_lens)
+    rows = np.concatenate([np.arange(t.qsl[s], t.qsl[s + 1]) for s in seqs])
+    u.q = t.q[rows]
+    u.positions = t.positions[rows]
+    u.k = t.k[rows] if t.k is not None else None
+    u.v = t.v[rows] if t.v is not None else None
+    return u, rows
+
+
+def test_mixed_tick_equals_separate_calls_and_any_order():
+    t = W.make_config(4, poison=True)
+    say("mixed tick vs separate")
+    d = DevTick(t).write()
+    whole = d.attend()
+    torch.cuda.synchronize()
+    whole_h = host_storage(whole, t.dtype)
+    # decode rows alone and chunk rows alone, on the pools the full tick wrote
+    for seqs in (range(48), range(48, 51), [50, 3, 48, 7, 49, 0]):
+        u, rows = _subset_tick(t, seqs)
+        q = storage_tensor(host_storage(d.q, t.dtype)[rows], t.dtype)
+        out = pa.pa_paged_attention_varlen(q, d.k_pool, d.v_pool, i32(u.block_tables),
+                                           i32(u.seq_lens), i32(u.qsl), u.max_query_len,
+                                           t.max_seq_len, scale=t.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_storage(out, t.dtype), whole_h[rows]), list(seqs)[:4]
+
+
+@pytest.mark.parametrize("dtype,D,G", [(W.F32, 16, 2), (W.BF16, 128, 4), (W.BF16, 64, 8),
+                                       (W.F32, 64, 1)])
+def test_one_hot_position_probe_exact(dtype, D, G):
+    """Each row's weight is exactly 1 on one key: the output must be that key's
+    V row exactly, which names the (page, row) the kernel read."""
+    Hkv = 2
+    t, targets = _pins.one_hot_tick(90 + D, dtype=dtype, Hq=Hkv * G, Hkv=Hkv, D=D, P=16,
+                                    seq_lens=(9, 14, 6) if D == 16 else (40, 14, 63),
+                                    query_lens=(1, 3, 1) if D == 16 else (1, 5, 7))
+    say("one-hot probe", dtype, D, G)
+    d = DevTick(t)
+    out = d.attend()
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    for s, i, j in targets:
+        page, row = int(t.block_tables[s][j // t.P]), j % t.P
+        r = got[t.qsl[s] + i]
+        assert np.all(r[:, 0] == page) and np.all(r[:, 2] == row), (s, i, j, r[:, :3])
+        assert np.all(r[:, 1] == j)
+
+
+def test_sequences_with_no_rows_and_host_bounds_larger_than_needed():
+    t = _small(8, seq_lens=(50, 20, 300, 9), query_lens=(1, 0, 40, 0))
+    say("empty sequences")
+    d = DevTick(t).write()
+    out = d.attend(max_query_len=t.max_query_len + 100, max_seq_len=t.max_seq_len + 1000)
+    torch.cuda.synchronize()
+    check_attention(out, oracle_tick(t), t.dtype, "empty-seqs")
+
+
+def test_profile_hook_records_kernels():
+    t = W.make_config(4, poison=False)
+    d = DevTick(t).write()
+    torch.cuda.synchronize()
+    pa.pa_profile_start(64)
+    d.attend()
+    rec = pa.pa_profile_stop()
+    names = [n for n, _ in rec]
+    assert "decode_attention" in names and "prefill_attention_mfma" in names
+    assert all(ms > 0 for _, ms in rec)
+    pa.pa_profile_reset()
