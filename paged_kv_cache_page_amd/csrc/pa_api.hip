@@ -7,6 +7,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "pa_device.h"
@@ -49,6 +51,31 @@ void profile_after(hipStream_t stream) {
   if (hipEventRecord(g_recs[g_prof_n].stop, stream) == hipSuccess) ++g_prof_n;
 }
 
+// ------------------------------------------------------- grid sizing -----
+namespace {
+std::mutex g_grid_mu;
+std::map<std::pair<int, const void*>, int> g_grid_cache;
+}  // namespace
+
+int persistent_grid(const void* func, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(g_grid_mu);
+  auto key = std::make_pair(dev, func);
+  auto it = g_grid_cache.find(key);
+  if (it != g_grid_cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, threads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int grid = cus * per_cu;
+  g_grid_cache[key] = grid;
+  return grid;
+}
+
 // ------------------------------------------------------------- helpers -----
 namespace {
 
@@ -81,14 +108,48 @@ bool use_mfma_prefill(pa_dtype_t dt, int D, int max_query_len) {
   return max_query_len <= 1 || prefill_mfma_supported(dt, D, 1);
 }
 
-size_t workspace_bytes_for(int S, int T, int Hq, int D, int max_query_len, int max_seq_len,
-                           int P, int kv_split, pa_dtype_t dt) {
+// Workspace layout: the plan lists (seq mode), padded to 256 bytes, then the
+// split-KV partials (o for every (row, partition, head), then (m, l) pairs).
+struct WsLayout {
+  long cap_dec, cap_pf;
+  size_t plan_bytes, partial_bytes;
+  int max_parts;
+  bool token_mode;
+};
+
+WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int max_seq_len, int P,
+                          int kv_split, pa_dtype_t dt) {
+  WsLayout w;
   const int pt = split_tokens(kv_split, P);
   const long max_parts = max_seq_len > 0 ? ((long)max_seq_len + pt - 1) / pt : 1;
-  if (max_parts <= 1) return 0;
-  const bool token_mode = !use_mfma_prefill(dt, D, max_query_len);
-  const long rows = token_mode ? T : S;
-  return (size_t)rows * (size_t)max_parts * (size_t)Hq * ((size_t)D + 2) * sizeof(float);
+  w.max_parts = (int)(max_parts < 1 ? 1 : max_parts);
+  w.token_mode = !use_mfma_prefill(dt, D, max_query_len);
+  w.cap_dec = 0;
+  w.cap_pf = 0;
+  w.plan_bytes = 0;
+  if (!w.token_mode) {
+    w.cap_dec = (long)S * w.max_parts;
+    if (max_query_len > 1) {
+      // a tile holds at least kPrefillRows / 8 tokens (the largest supported group is 8)
+      const int tm = kPrefillRows / 8;
+      const long by_seq = (long)S * ((max_query_len + tm - 1) / tm);
+      const long by_tok = (long)T / tm + S;
+      w.cap_pf = by_seq < by_tok ? by_seq : by_tok;
+    }
+    w.plan_bytes = ((size_t)(kPlanHeaderInts + 2 * (w.cap_dec + w.cap_pf)) * sizeof(int) + 255) /
+                   256 * 256;
+  }
+  const long rows = w.token_mode ? T : S;
+  w.partial_bytes = w.max_parts > 1 ? (size_t)rows * (size_t)w.max_parts * (size_t)Hq *
+                                          ((size_t)D + 2) * sizeof(float)
+                                    : 0;
+  return w;
+}
+
+size_t workspace_bytes_for(int S, int T, int Hq, int D, int max_query_len, int max_seq_len,
+                           int P, int kv_split, pa_dtype_t dt) {
+  const WsLayout w = workspace_layout(S, T, Hq, D, max_query_len, max_seq_len, P, kv_split, dt);
+  return w.plan_bytes + w.partial_bytes;
 }
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -200,10 +261,12 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_pool, pool_bytes) ||
       overlap(out, qbytes, v_pool, pool_bytes))
     return PA_ERR_INVALID_ARG;
-  const size_t need = workspace_bytes_for(S, T, Hq, head_dim, max_query_len, max_seq_len,
-                                          page_size, kv_split_tokens, dtype);
+  const WsLayout wl = workspace_layout(S, T, Hq, head_dim, max_query_len, max_seq_len,
+                                       page_size, kv_split_tokens, dtype);
+  const size_t need = wl.plan_bytes + wl.partial_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && ((uintptr_t)workspace & 3u)) return PA_ERR_INVALID_ARG;
+  if (need > 0 && ((uintptr_t)workspace & 255u)) return PA_ERR_INVALID_ARG;
+  if (wl.cap_dec > INT32_MAX / 2 || wl.cap_pf > INT32_MAX / 2) return PA_ERR_INVALID_ARG;
 
   AttnArgs a;
   a.q = q;
@@ -213,7 +276,10 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.seq_lens = seq_lens;
   a.qsl = query_start_loc;
   a.out = out;
-  a.ws = (float*)workspace;
+  a.plan = (int*)workspace;
+  a.ws = (float*)((char*)workspace + wl.plan_bytes);
+  a.cap_dec = (int32_t)wl.cap_dec;
+  a.cap_pf = (int32_t)wl.cap_pf;
   a.S = S;
   a.T = T;
   a.Hq = Hq;
@@ -225,19 +291,22 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.max_query_len = max_query_len;
   a.max_seq_len = max_seq_len;
   a.part_tokens = split_tokens(kv_split_tokens, page_size);
-  a.max_parts = max_seq_len > 0 ? (max_seq_len + a.part_tokens - 1) / a.part_tokens : 1;
-  if (a.max_parts < 1) a.max_parts = 1;
+  a.max_parts = wl.max_parts;
   a.scale_log2e = scale * kLog2e;
 
   hipStream_t s = (hipStream_t)stream;
-  const bool token_mode = !use_mfma_prefill(dtype, head_dim, max_query_len);
-  hipError_t e = launch_decode(dtype, a, token_mode, s);
-  if (e != hipSuccess) return PA_ERR_HIP;
-  if (a.max_parts > 1) {
-    e = launch_split_reduce(dtype, a, token_mode, s);
+  hipError_t e;
+  if (!wl.token_mode) {
+    e = launch_plan(a, a.plan, a.cap_dec, a.cap_pf, kPrefillRows / G, s);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
-  if (!token_mode && max_query_len > 1) {
+  e = launch_decode(dtype, a, wl.token_mode, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (a.max_parts > 1) {
+    e = launch_split_reduce(dtype, a, wl.token_mode, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  if (!wl.token_mode && a.cap_pf > 0) {
     e = launch_prefill_mfma(dtype, a, s);
     if (e != hipSuccess) return PA_ERR_HIP;
   }

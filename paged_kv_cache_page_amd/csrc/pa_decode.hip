@@ -4,14 +4,17 @@
 // used by all G query heads of its group (grouped-query attention: Helios blog,
 // "torch.sdpa and Flash Attention"), about 2*G flops per byte. The kernel is
 // written for that bound: VALU dot products (no matrix cores), 16-byte row
-// loads through the page table, many loads in flight per lane, and the
-// softmax kept online in registers.
+// loads through the page table, the next step's loads in flight while the
+// current step computes, and the softmax kept online in registers.
 //
-// Work decomposition. One workgroup (4 waves) per (row, split partition, KV
-// head); the KV head varies fastest across workgroup ids, so the workgroups of
-// one page run together and, with 8 KV heads, each KV head's slices land on
-// one XCD (ids are dealt round-robin to the 8 XCDs) -- the slices of a prefix
-// page shared by many sequences then stay in that XCD's L2.
+// Work decomposition. A work item is (row, split partition, KV head). For the
+// decode rows of a tick the items come from the plan list and a persistent
+// grid walks them (item index w -> KV head w % Hkv, so with a grid that is a
+// multiple of 8 each workgroup keeps one KV head, and with 8 KV heads each
+// XCD serves one head: the slices of a prefix page shared by many sequences
+// then stay in that XCD's L2). The per-token mode (prefill rows without a
+// matrix-core kernel, i.e. float32) uses a plain grid over (token, partition,
+// KV head).
 //
 // Inside a wave, LPK lanes hold one key row (16 or 32 bytes each), so a wave
 // covers 64 / LPK keys per step and UNROLL steps per iteration. Each lane
@@ -41,7 +44,7 @@ struct DecodeShape {
   static constexpr int DPL = D / LPK;            // head dims held by a lane
   static constexpr int EPV = 16 / EB;            // elements per 16-byte vector
   static constexpr int KPW = 64 / LPK;           // keys per wave step (slots)
-  static constexpr int UNROLL = 4;
+  static constexpr int UNROLL = 2;               // steps per buffer; two buffers alternate
   static constexpr int KPI = KPW * UNROLL;       // keys per wave iteration
   static_assert(LANE_BYTES == 16 || LANE_BYTES == 32, "lane row share must be 16 or 32 bytes");
   // Head-dim index of the lane's local dim i (sub = lane % LPK).
@@ -50,7 +53,7 @@ struct DecodeShape {
   }
 };
 
-// Which row a workgroup serves, and that row's key limit.
+// Which row a work item serves, and that row's key limit.
 struct RowInfo {
   int seq;      // sequence index
   int token;    // row of q / out
@@ -92,22 +95,109 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
   return r;
 }
 
+template <typename ET, int D, int G>
+struct DecodeSmem {
+  int pages[kMaxPartPages];
+  float o[kWaves][G][D];
+  float m[kWaves][G];
+  float l[kWaves][G];
+};
+
+// Issue the loads of one buffer: UNROLL steps of KPW keys starting at `base`.
+template <typename SH>
+__device__ __forceinline__ void load_step(uint32_t (&kr)[SH::UNROLL][SH::WORDS],
+                                          uint32_t (&vr)[SH::UNROLL][SH::WORDS],
+                                          const char* kbase, const char* vbase,
+                                          const int* pages, int pg0, int P, size_t slot_stride,
+                                          int base, int kbeg, int kend, int slot) {
+#pragma unroll
+  for (int u = 0; u < SH::UNROLL; ++u) {
+    const int j = base + u * SH::KPW + slot;
+    const int jj = j < kend ? j : kbeg;  // invalid keys read a valid row and are masked later
+    const int page = pages[jj / P - pg0];
+    const size_t off = ((size_t)page * P + (jj % P)) * slot_stride;
+#pragma unroll
+    for (int l = 0; l < SH::LOADS; ++l) {
+      const uint4 x = *reinterpret_cast<const uint4*>(kbase + off + l * SH::LPK * 16);
+      kr[u][4 * l] = x.x; kr[u][4 * l + 1] = x.y; kr[u][4 * l + 2] = x.z; kr[u][4 * l + 3] = x.w;
+    }
+#pragma unroll
+    for (int l = 0; l < SH::LOADS; ++l) {
+      const uint4 x = *reinterpret_cast<const uint4*>(vbase + off + l * SH::LPK * 16);
+      vr[u][4 * l] = x.x; vr[u][4 * l + 1] = x.y; vr[u][4 * l + 2] = x.z; vr[u][4 * l + 3] = x.w;
+    }
+  }
+}
+
+// Scores, online softmax and P.V for one buffer.
+template <typename SH, int G>
+__device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH::WORDS],
+                                             const uint32_t (&vr)[SH::UNROLL][SH::WORDS],
+                                             const uint32_t (&qw)[G][SH::WORDS], float (&m)[G],
+                                             float (&lsum)[G], float (&o)[G][SH::DPL], int base,
+                                             int kend, int slot, float sl2e) {
+  constexpr int UNROLL = SH::UNROLL, WORDS = SH::WORDS, DPL = SH::DPL;
+  float sc[UNROLL][G];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const bool valid = base + u * SH::KPW + slot < kend;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float acc = 0.f;
+      if constexpr (SH::EB == 2) {
+        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
+                                                __builtin_bit_cast(bf16x2, kr[u][w]), acc, false);
+      } else {
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w)
+          acc = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kr[u][w]), acc);
+      }
+      acc = group_sum<SH::LPK>(acc);
+      sc[u][g] = valid ? acc * sl2e : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mb = sc[0][g];
+#pragma unroll
+    for (int u = 1; u < UNROLL; ++u) mb = fmaxf(mb, sc[u][g]);
+    // Rescale only when some lane's running max grows (rare after the first keys).
+    if (__any(mb > m[g])) {
+      const float mn = fmaxf(m[g], mb);
+      const float corr = fast_exp2(m[g] - mn);
+      m[g] = mn;
+      lsum[g] *= corr;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[g][i] *= corr;
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const float p = fast_exp2(sc[u][g] - m[g]);
+      lsum[g] += p;
+      if constexpr (SH::EB == 2) {
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w) {
+          o[g][2 * w] = fmaf(p, bf16_lo(vr[u][w]), o[g][2 * w]);
+          o[g][2 * w + 1] = fmaf(p, bf16_hi(vr[u][w]), o[g][2 * w + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w) o[g][w] = fmaf(p, __uint_as_float(vr[u][w]), o[g][w]);
+      }
+    }
+  }
+}
+
+// One work item: keys [part * PT, min(n_eff, (part + 1) * PT)) of one row, one KV head.
 template <typename ET, int D, int G, bool TOKEN_MODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+__device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D, G>& sm, int row,
+                                            int part, int kvh) {
   typedef DecodeShape<ET, D> SH;
   constexpr int LPK = SH::LPK, WORDS = SH::WORDS, LOADS = SH::LOADS, DPL = SH::DPL;
-  constexpr int KPW = SH::KPW, UNROLL = SH::UNROLL, KPI = SH::KPI;
-
-  __shared__ int s_pages[kMaxPartPages];
-  __shared__ float s_o[kWaves][G][D];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-
-  const int bid = blockIdx.x;
-  const int kvh = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
-  const int part = rest % a.max_parts;
-  const int row = rest / a.max_parts;
+  constexpr int KPI = SH::KPI;
 
   const RowInfo ri = row_info<TOKEN_MODE>(a, row);
   if (!ri.active) return;
@@ -122,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   const int npg = (kend - 1) / P - pg0 + 1;
   const int* bt_row = a.block_tables + (size_t)ri.seq * a.max_blocks;
   for (int i = threadIdx.x; i < npg; i += kThreads)
-    s_pages[i] = clampi(bt_row[pg0 + i], 0, a.num_pages - 1);
+    sm.pages[i] = clampi(bt_row[pg0 + i], 0, a.num_pages - 1);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -150,85 +240,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < DPL; ++i) o[g][i] = 0.f;
   }
-  __syncthreads();  // s_pages ready
+  __syncthreads();  // pages ready
 
   const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes + sub * 16;
   const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes + sub * 16;
   const size_t slot_stride = (size_t)a.Hkv * row_bytes;  // bytes between consecutive slots
   const float sl2e = a.scale_log2e;
+  constexpr int STEP = kWaves * KPI;
 
-  for (int base = kbeg + wave * KPI; base < kend; base += kWaves * KPI) {
-    uint32_t kr[UNROLL][WORDS], vr[UNROLL][WORDS];
-    bool valid[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = base + u * KPW + slot;
-      valid[u] = j < kend;
-      const int jj = valid[u] ? j : kbeg;
-      const int page = s_pages[jj / P - pg0];
-      const size_t off = ((size_t)page * P + (jj % P)) * slot_stride;
-#pragma unroll
-      for (int l = 0; l < LOADS; ++l) {
-        const uint4 x = *reinterpret_cast<const uint4*>(kbase + off + l * LPK * 16);
-        kr[u][4 * l] = x.x; kr[u][4 * l + 1] = x.y; kr[u][4 * l + 2] = x.z; kr[u][4 * l + 3] = x.w;
-      }
-#pragma unroll
-      for (int l = 0; l < LOADS; ++l) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vbase + off + l * LPK * 16);
-        vr[u][4 * l] = x.x; vr[u][4 * l + 1] = x.y; vr[u][4 * l + 2] = x.z; vr[u][4 * l + 3] = x.w;
-      }
-    }
-
-    float sc[UNROLL][G];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.f;
-        if constexpr (SH::EB == 2) {
-          typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-#pragma unroll
-          for (int w = 0; w < WORDS; ++w)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
-                                                  __builtin_bit_cast(bf16x2, kr[u][w]), acc,
-                                                  false);
-        } else {
-#pragma unroll
-          for (int w = 0; w < WORDS; ++w)
-            acc = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kr[u][w]), acc);
-        }
-        acc = group_sum<LPK>(acc);
-        sc[u][g] = valid[u] ? acc * sl2e : -INFINITY;
-      }
-    }
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mb = sc[0][g];
-#pragma unroll
-      for (int u = 1; u < UNROLL; ++u) mb = fmaxf(mb, sc[u][g]);
-      const float mn = fmaxf(m[g], mb);
-      const float corr = fast_exp2(m[g] - mn);
-      m[g] = mn;
-      lsum[g] *= corr;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o[g][i] *= corr;
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const float p = fast_exp2(sc[u][g] - mn);
-        lsum[g] += p;
-        if constexpr (SH::EB == 2) {
-#pragma unroll
-          for (int w = 0; w < WORDS; ++w) {
-            o[g][2 * w] = fmaf(p, bf16_lo(vr[u][w]), o[g][2 * w]);
-            o[g][2 * w + 1] = fmaf(p, bf16_hi(vr[u][w]), o[g][2 * w + 1]);
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < WORDS; ++w) o[g][w] = fmaf(p, __uint_as_float(vr[u][w]), o[g][w]);
-        }
-      }
-    }
+  uint32_t kA[SH::UNROLL][WORDS], vA[SH::UNROLL][WORDS];
+  uint32_t kB[SH::UNROLL][WORDS], vB[SH::UNROLL][WORDS];
+  int base = kbeg + wave * KPI;
+  if (base < kend)
+    load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, base, kbeg, kend, slot);
+  while (base < kend) {
+    int nb = base + STEP;
+    if (nb < kend)
+      load_step<SH>(kB, vB, kbase, vbase, sm.pages, pg0, P, slot_stride, nb, kbeg, kend, slot);
+    compute_step<SH, G>(kA, vA, qw, m, lsum, o, base, kend, slot, sl2e);
+    base = nb;
+    if (base >= kend) break;
+    nb = base + STEP;
+    if (nb < kend)
+      load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, nb, kbeg, kend, slot);
+    compute_step<SH, G>(kB, vB, qw, m, lsum, o, base, kend, slot, sl2e);
+    base = nb;
   }
 
   // Merge the slots of this wave (lanes sub, sub + LPK, ...).
@@ -254,10 +290,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) s_o[wave][g][SH::dim_of(sub, i)] = o[g][i];
+      for (int i = 0; i < DPL; ++i) sm.o[wave][g][SH::dim_of(sub, i)] = o[g][i];
       if (sub == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = lsum[g];
+        sm.m[wave][g] = m[g];
+        sm.l[wave][g] = lsum[g];
       }
     }
   }
@@ -267,15 +303,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int g = idx / D;
     const int e = idx % D;
-    float mn = s_m[0][g];
+    float mn = sm.m[0][g];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mn = fmaxf(mn, s_m[w][g]);
+    for (int w = 1; w < kWaves; ++w) mn = fmaxf(mn, sm.m[w][g]);
     float lt = 0.f, ot = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float c = fast_exp2(s_m[w][g] - mn);
-      lt = fmaf(s_l[w][g], c, lt);
-      ot = fmaf(s_o[w][g][e], c, ot);
+      const float c = fast_exp2(sm.m[w][g] - mn);
+      lt = fmaf(sm.l[w][g], c, lt);
+      ot = fmaf(sm.o[w][g][e], c, ot);
     }
     const int h = kvh * G + g;
     if (nparts == 1) {
@@ -293,6 +329,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
         ml[2 * pi] = mn;
         ml[2 * pi + 1] = lt;
       }
+    }
+  }
+}
+
+template <typename ET, int D, int G, bool TOKEN_MODE>
+__global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+  __shared__ DecodeSmem<ET, D, G> sm;
+  if constexpr (TOKEN_MODE) {
+    const int bid = blockIdx.x;
+    const int kvh = bid % a.Hkv;
+    const int rest = bid / a.Hkv;
+    decode_item<ET, D, G, true>(a, sm, rest / a.max_parts, rest % a.max_parts, kvh);
+  } else {
+    const int* items = a.plan + kPlanHeaderInts;
+    const int total = a.plan[0] * a.Hkv;
+    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+      const int it = w / a.Hkv;
+      decode_item<ET, D, G, false>(a, sm, items[2 * it], items[2 * it + 1], w % a.Hkv);
+      __syncthreads();  // LDS is reused by the next item
     }
   }
 }
@@ -335,16 +390,24 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(AttnArgs a, int 
 // ------------------------------------------------------------ dispatch -----
 template <typename ET, int D, int G>
 static hipError_t launch_decode_t(const AttnArgs& a, bool token_mode, hipStream_t s) {
-  const long rows = token_mode ? a.T : a.S;
-  const long blocks = rows * a.max_parts * a.Hkv;
-  if (blocks == 0) return hipSuccess;
-  profile_before(token_mode ? "decode_attention_tokens" : "decode_attention", s);
-  if (token_mode)
+  if (token_mode) {
+    const long blocks = (long)a.T * a.max_parts * a.Hkv;
+    if (blocks == 0) return hipSuccess;
+    profile_before("decode_attention_tokens", s);
     hipLaunchKernelGGL((decode_kernel<ET, D, G, true>), dim3((unsigned)blocks), dim3(kThreads),
                        0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<ET, D, G, false>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, s, a);
+    profile_after(s);
+    return hipGetLastError();
+  }
+  const long items = (long)a.cap_dec * a.Hkv;
+  if (items == 0) return hipSuccess;
+  const int resident = persistent_grid((const void*)decode_kernel<ET, D, G, false>, kThreads);
+  // a multiple of 8 (and of Hkv when Hkv divides 8) keeps each workgroup on one KV head
+  long grid = items < resident ? items : resident;
+  if (grid > 8) grid -= grid % 8;
+  profile_before("decode_attention", s);
+  hipLaunchKernelGGL((decode_kernel<ET, D, G, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     s, a);
   profile_after(s);
   return hipGetLastError();
 }

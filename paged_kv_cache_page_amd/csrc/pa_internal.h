@@ -20,12 +20,25 @@ struct AttnArgs {
   const int32_t* qsl;
   void* out;
   float* ws;           // split-KV partials: o [rows*max_parts*Hq*D], then (m, l) pairs
+  int* plan;           // work lists written by the plan kernel (see pa_plan.hip)
+  int32_t cap_dec, cap_pf;  // capacities of the two lists
   int32_t S, T, Hq, Hkv, D, P, num_pages, max_blocks;
   int32_t max_query_len, max_seq_len;
   int32_t part_tokens;  // keys per split-KV partition
   int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / part_tokens))
   float scale_log2e;    // scale * log2(e): weights are exp2(s * scale_log2e - m)
 };
+
+// Plan layout: header [decode item count, prefill item count, 0, 0], then
+// cap_dec (sequence, partition) pairs, then cap_pf (sequence, row tile) pairs.
+constexpr int kPlanHeaderInts = 4;
+// Query rows per prefill workgroup; a tile holds kPrefillRows / G tokens.
+constexpr int kPrefillRows = 128;
+
+// Workgroups of `func` (launched with `threads` threads) that the current
+// device holds at once: compute units x resident workgroups per unit. Cached
+// per (device, kernel). Used to size persistent grids.
+int persistent_grid(const void* func, int threads);
 
 // Kernel timing hook (pa_api.hip): called around every launch.
 void profile_before(const char* name, hipStream_t stream);
@@ -40,6 +53,10 @@ hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* 
                                    const int32_t* pos, const int32_t* slots, const float* cs,
                                    void* k_pool, void* v_pool, int T, int Hq, int Hkv, int D,
                                    int P, int num_pages, int max_pos, hipStream_t s);
+
+// Work lists (pa_plan.hip). TM = tokens per prefill tile.
+hipError_t launch_plan(const AttnArgs& a, int* plan, int cap_dec, int cap_pf, int TM,
+                       hipStream_t s);
 
 // K2 + K3 (pa_decode.hip). token_mode = false: one row per decode sequence
 // (query length 1; other sequences skipped). token_mode = true: one row per

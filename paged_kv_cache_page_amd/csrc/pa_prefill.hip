@@ -33,6 +33,7 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWg = kPfWaves * kRowsPerWave;  // 128
+static_assert(kRowsPerWg == kPrefillRows, "plan and kernel disagree on the tile height");
 constexpr int kBN = 32;                                // keys per tile
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
@@ -40,114 +41,77 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(AttnArgs a, int n_mtiles) {
-  constexpr int TM = kRowsPerWg / G;    // tokens per workgroup
-  constexpr int DSTEPS = D / 32;        // k-steps of the QK^T product
-  constexpr int DBLK = D / 16;          // 16-dim output blocks
-  constexpr int KSTR = D + 8;           // LDS row stride of K (elements), 16-byte pad
-  constexpr int VSTR = kBN + 4;         // LDS row stride of V^T (elements), 8-byte pad
-  constexpr int C16 = D / 8;            // 16-byte chunks per head row
+// Global -> register staging of one 32-key tile: K as 16-byte row chunks,
+// V as pairs of keys (so V^T can be written two keys per 32-bit LDS word).
+template <int D>
+struct TileRegs {
+  static constexpr int C16 = D / 8;                                    // 16-byte chunks per row
+  static constexpr int KCH = (kBN * C16 + kPfThreads - 1) / kPfThreads;        // K chunks per thread
+  static constexpr int VCH = ((kBN / 2) * C16 + kPfThreads - 1) / kPfThreads;  // V pair tasks per thread
+  uint4 k[KCH];
+  uint4 va[VCH], vb[VCH];
+};
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VSTR];
-
-  const int bid = blockIdx.x;
-  const int kvh = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
-  const int mt = rest % n_mtiles;
-  const int s = rest / n_mtiles;
-
-  const int q0 = a.qsl[s];
-  const int L = a.qsl[s + 1] - q0;
-  if (L <= 1) return;                   // decode rows belong to the decode kernel
-  const int i0 = mt * TM;
-  if (i0 >= L || q0 < 0 || q0 + L > a.T) return;
-  const int i1 = min(L, i0 + TM);
-  int n = a.seq_lens[s];
-  n = min(n, a.max_blocks * a.P);
-  if (n < L) return;                    // malformed row: nothing sensible to compute
-  const int kmax = n - L + i1;          // keys visible to the tile's last row
-  const int ntiles = (kmax + kBN - 1) / kBN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 15;            // query row within a 16-row block
-  const int grp = lane >> 4;            // 0..3
-
-  const size_t row_bytes = (size_t)D * 2;
-  const int Hq = a.Hq;
-
-  // Q^T operand: rows of this lane, 8 dims per k-step.
-  uint4 qop[2][DSTEPS];
-  int tok[2], head[2];
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D>& r, const char* kpool, const char* vpool,
+                                          const int* bt_row, int num_pages, int P,
+                                          size_t slot_stride, int kb0, int kmax, int tid) {
+  constexpr int C16 = TileRegs<D>::C16;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int r = wave * kRowsPerWave + mb * 16 + col;
-    tok[mb] = i0 + r / G;
-    head[mb] = kvh * G + r % G;
-    const bool ok = tok[mb] < i1;
-    const char* qrow = (const char*)a.q + ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * row_bytes;
-#pragma unroll
-    for (int ds = 0; ds < DSTEPS; ++ds) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (ok) x = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
-      qop[mb][ds] = x;
+  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    const int c = tid + i * kPfThreads;
+    const int key = c / C16, d8 = c % C16;
+    const int j = kb0 + key;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (c < kBN * C16 && j < kmax) {
+      const int page = clampi(bt_row[j / P], 0, num_pages - 1);
+      x = *reinterpret_cast<const uint4*>(kpool + ((size_t)page * P + j % P) * slot_stride +
+                                          d8 * 16);
     }
+    r.k[i] = x;
   }
-
-  f32x4_t acc_o[2][DBLK];
-  float m_run[2], l_run[2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    m_run[mb] = kNegBig;
-    l_run[mb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) acc_o[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
-  const char* kpool = (const char*)a.k_pool + (size_t)kvh * row_bytes;
-  const char* vpool = (const char*)a.v_pool + (size_t)kvh * row_bytes;
-  const size_t slot_stride = (size_t)a.Hkv * row_bytes;
-  const int P = a.P;
-  const float sl2e = a.scale_log2e;
-  const int last_key = n - L;           // row i sees keys <= last_key + i
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int kb0 = kt * kBN;
-    // ---- stage K (row-major) ----
-    for (int c = tid; c < kBN * C16; c += kPfThreads) {
-      const int key = c / C16;
-      const int d8 = c % C16;
-      const int j = kb0 + key;
-      uint4 x = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < TileRegs<D>::VCH; ++i) {
+    const int c = tid + i * kPfThreads;
+    const int kp = c % (kBN / 2), d8 = c / (kBN / 2);
+    const int j = kb0 + 2 * kp;
+    uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+    if (c < (kBN / 2) * C16) {
       if (j < kmax) {
-        const int page = clampi(bt_row[j / P], 0, a.num_pages - 1);
-        x = *reinterpret_cast<const uint4*>(kpool + ((size_t)page * P + j % P) * slot_stride +
-                                            d8 * 16);
-      }
-      *reinterpret_cast<uint4*>(&s_k[key * KSTR + d8 * 8]) = x;
-    }
-    // ---- stage V transposed: two keys per 32-bit LDS word ----
-    for (int c = tid; c < (kBN / 2) * C16; c += kPfThreads) {
-      const int kp = c % (kBN / 2);
-      const int d8 = c / (kBN / 2);
-      const int j = kb0 + 2 * kp;
-      uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-      if (j < kmax) {
-        const int page = clampi(bt_row[j / P], 0, a.num_pages - 1);
+        const int page = clampi(bt_row[j / P], 0, num_pages - 1);
         xa = *reinterpret_cast<const uint4*>(vpool + ((size_t)page * P + j % P) * slot_stride +
                                              d8 * 16);
       }
       if (j + 1 < kmax) {
-        const int page = clampi(bt_row[(j + 1) / P], 0, a.num_pages - 1);
+        const int page = clampi(bt_row[(j + 1) / P], 0, num_pages - 1);
         xb = *reinterpret_cast<const uint4*>(vpool + ((size_t)page * P + (j + 1) % P) *
                                                          slot_stride + d8 * 16);
       }
-      const uint32_t* wa = reinterpret_cast<const uint32_t*>(&xa);
-      const uint32_t* wb = reinterpret_cast<const uint32_t*>(&xb);
+    }
+    r.va[i] = xa;
+    r.vb[i] = xb;
+  }
+}
+
+template <int D, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_store(const TileRegs<D>& r, uint16_t* s_k, uint16_t* s_vt,
+                                           int tid) {
+  constexpr int C16 = TileRegs<D>::C16;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    const int c = tid + i * kPfThreads;
+    if (c < kBN * C16) {
+      const int key = c / C16, d8 = c % C16;
+      *reinterpret_cast<uint4*>(&s_k[key * KSTR + d8 * 8]) = r.k[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::VCH; ++i) {
+    const int c = tid + i * kPfThreads;
+    if (c < (kBN / 2) * C16) {
+      const int kp = c % (kBN / 2), d8 = c / (kBN / 2);
+      const uint32_t* wa = reinterpret_cast<const uint32_t*>(&r.va[i]);
+      const uint32_t* wb = reinterpret_cast<const uint32_t*>(&r.vb[i]);
       uint32_t* vt = reinterpret_cast<uint32_t*>(s_vt);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -156,107 +120,203 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(AttnArgs a, in
         vt[((d + 1) * VSTR) / 2 + kp] = (wa[w] >> 16) | (wb[w] & 0xFFFF0000u);
       }
     }
-    __syncthreads();
+  }
+}
 
-    // ---- S^T = K Q^T for this wave's two row blocks ----
-    f32x4_t st[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) st[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ds = 0; ds < DSTEPS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kop =
-            *reinterpret_cast<const uint4*>(&s_k[(kb * 16 + col) * KSTR + ds * 32 + grp * 8]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) st[mb][kb] = mfma16x16x32(kop, qop[mb][ds], st[mb][kb]);
-      }
-    }
+template <int D, int G>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(AttnArgs a) {
+  constexpr int TM = kRowsPerWg / G;    // tokens per workgroup
+  constexpr int DSTEPS = D / 32;        // k-steps of the QK^T product
+  constexpr int DBLK = D / 16;          // 16-dim output blocks
+  constexpr int KSTR = D + 8;           // LDS row stride of K (elements), 16-byte pad
+  constexpr int VSTR = kBN + 4;         // LDS row stride of V^T (elements), 8-byte pad
 
-    // ---- online softmax per query row (this lane's column) ----
-    uint4 pop[2];
+  // double-buffered tiles: the next tile is written while the current one is read
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kBN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;            // query row within a 16-row block
+  const int grp = lane >> 4;            // 0..3
+  const size_t row_bytes = (size_t)D * 2;
+  const int Hq = a.Hq;
+  const int P = a.P;
+  const float sl2e = a.scale_log2e;
+  const size_t slot_stride = (size_t)a.Hkv * row_bytes;
+  const int* items = a.plan + kPlanHeaderInts + 2 * (size_t)a.cap_dec;
+  const int total = a.plan[1] * a.Hkv;
+  const int nwg = gridDim.x;
+
+  // Items are sorted by decreasing cost; rounds alternate direction (snake) so
+  // the workgroups that took the longest items take the shortest next.
+  for (int r = 0;; ++r) {
+    const int w = r * nwg + ((r & 1) ? (nwg - 1 - (int)blockIdx.x) : (int)blockIdx.x);
+    if (w >= total) break;
+    const int it = w / a.Hkv;
+    const int kvh = w % a.Hkv;
+    const int s = items[2 * it];
+    const int mt = items[2 * it + 1];
+
+    const int q0 = a.qsl[s];
+    const int L = a.qsl[s + 1] - q0;
+    const int i0 = mt * TM;
+    int n = a.seq_lens[s];
+    n = min(n, a.max_blocks * a.P);
+    if (L <= 1 || i0 >= L || q0 < 0 || q0 + L > a.T || n < L) continue;  // uniform per item
+    const int i1 = min(L, i0 + TM);
+    const int kmax = n - L + i1;          // keys visible to the tile's last row
+    const int ntiles = (kmax + kBN - 1) / kBN;
+    const int last_key = n - L;           // row i sees keys <= last_key + i
+
+    // Q^T operand: rows of this lane, 8 dims per k-step.
+    uint4 qop[2][DSTEPS];
+    int tok[2], head[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int limit = min(last_key + tok[mb], n - 1);
-      float sv[8];
-      float tmax = -INFINITY;
+      const int rr = wave * kRowsPerWave + mb * 16 + col;
+      tok[mb] = i0 + rr / G;
+      head[mb] = kvh * G + rr % G;
+      const bool ok = tok[mb] < i1;
+      const char* qrow =
+          (const char*)a.q + ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * row_bytes;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int ds = 0; ds < DSTEPS; ++ds) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (ok) x = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
+        qop[mb][ds] = x;
+      }
+    }
+
+    f32x4_t acc_o[2][DBLK];
+    float m_run[2], l_run[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kb0 + kb * 16 + grp * 4 + i;
-          const float x = (j <= limit) ? st[mb][kb][i] * sl2e : -INFINITY;
-          sv[kb * 4 + i] = x;
-          tmax = fmaxf(tmax, x);
+    for (int mb = 0; mb < 2; ++mb) {
+      m_run[mb] = kNegBig;
+      l_run[mb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) acc_o[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
+    const char* kpool = (const char*)a.k_pool + (size_t)kvh * row_bytes;
+    const char* vpool = (const char*)a.v_pool + (size_t)kvh * row_bytes;
+
+    TileRegs<D> regs;
+    tile_load<D>(regs, kpool, vpool, bt_row, a.num_pages, P, slot_stride, 0, kmax, tid);
+
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int buf = kt & 1;
+      const int kb0 = kt * kBN;
+      tile_store<D, KSTR, VSTR>(regs, s_k[buf], s_vt[buf], tid);
+      if (kt + 1 < ntiles)
+        tile_load<D>(regs, kpool, vpool, bt_row, a.num_pages, P, slot_stride, kb0 + kBN, kmax,
+                     tid);
+      __syncthreads();
+      const uint16_t* sk = s_k[buf];
+      const uint16_t* svt = s_vt[buf];
+
+      // ---- S^T = K Q^T for this wave's two row blocks ----
+      f32x4_t st[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) st[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DSTEPS; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint4 kop =
+              *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KSTR + ds * 32 + grp * 8]);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) st[mb][kb] = mfma16x16x32(kop, qop[mb][ds], st[mb][kb]);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m_run[mb], tmax);
-      const float corr = fast_exp2(m_run[mb] - mn);
-      m_run[mb] = mn;
-      float psum = 0.f;
-      float pv[8];
+
+      // ---- online softmax per query row (this lane's column) ----
+      uint4 pop[2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pv[k] = fast_exp2(sv[k] - mn);
-        psum += pv[k];
+      for (int mb = 0; mb < 2; ++mb) {
+        const int limit = min(last_key + tok[mb], n - 1);
+        float sv[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = kb0 + kb * 16 + grp * 4 + i;
+            const float x = (j <= limit) ? st[mb][kb][i] * sl2e : -INFINITY;
+            sv[kb * 4 + i] = x;
+            tmax = fmaxf(tmax, x);
+          }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mn = fmaxf(m_run[mb], tmax);
+        const float corr = fast_exp2(m_run[mb] - mn);
+        m_run[mb] = mn;
+        float psum = 0.f;
+        float pv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          pv[k] = fast_exp2(sv[k] - mn);
+          psum += pv[k];
+        }
+        l_run[mb] = l_run[mb] * corr + psum;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          acc_o[mb][db][0] *= corr;
+          acc_o[mb][db][1] *= corr;
+          acc_o[mb][db][2] *= corr;
+          acc_o[mb][db][3] *= corr;
+        }
+        pop[mb] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                             pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
       }
-      l_run[mb] = l_run[mb] * corr + psum;
+
+      // ---- O^T += V^T P^T ----
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        acc_o[mb][db][0] *= corr;
-        acc_o[mb][db][1] *= corr;
-        acc_o[mb][db][2] *= corr;
-        acc_o[mb][db][3] *= corr;
+        const int d = db * 16 + col;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&svt[d * VSTR + grp * 4]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&svt[d * VSTR + 16 + grp * 4]);
+        const uint4 vop = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc_o[mb][db] = mfma16x16x32(vop, pop[mb], acc_o[mb][db]);
       }
-      pop[mb] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
     }
+    __syncthreads();  // the next item's first store reuses buffer 0
 
-    // ---- O^T += V^T P^T ----
+    // ---- normalise and store ----
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const int d = db * 16 + col;
-      const uint2 lo = *reinterpret_cast<const uint2*>(&s_vt[d * VSTR + grp * 4]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&s_vt[d * VSTR + 16 + grp * 4]);
-      const uint4 vop = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    for (int mb = 0; mb < 2; ++mb) {
+      float lt = l_run[mb];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      if (tok[mb] >= i1) continue;
+      const float inv = 1.f / lt;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
+                       ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * D;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc_o[mb][db] = mfma16x16x32(vop, pop[mb], acc_o[mb][db]);
-    }
-    __syncthreads();  // tiles consumed before the next staging overwrites them
-  }
-
-  // ---- normalise and store ----
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    float lt = l_run[mb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (tok[mb] >= i1) continue;
-    const float inv = 1.f / lt;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
-                     ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * D;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const uint2 w = make_uint2(pack_bf16x2(acc_o[mb][db][0] * inv, acc_o[mb][db][1] * inv),
-                                 pack_bf16x2(acc_o[mb][db][2] * inv, acc_o[mb][db][3] * inv));
-      *reinterpret_cast<uint2*>(orow + db * 16 + grp * 4) = w;
+      for (int db = 0; db < DBLK; ++db) {
+        const uint2 wv = make_uint2(pack_bf16x2(acc_o[mb][db][0] * inv, acc_o[mb][db][1] * inv),
+                                    pack_bf16x2(acc_o[mb][db][2] * inv, acc_o[mb][db][3] * inv));
+        *reinterpret_cast<uint2*>(orow + db * 16 + grp * 4) = wv;
+      }
     }
   }
 }
 
 template <int D, int G>
 hipError_t launch_pf(const AttnArgs& a, hipStream_t s) {
-  constexpr int TM = kRowsPerWg / G;
-  const int n_mtiles = (a.max_query_len + TM - 1) / TM;
-  const long blocks = (long)a.S * n_mtiles * a.Hkv;
-  if (blocks == 0) return hipSuccess;
+  const long items = (long)a.cap_pf * a.Hkv;
+  if (items == 0) return hipSuccess;
+  const int resident = persistent_grid((const void*)prefill_mfma_kernel<D, G>, kPfThreads);
+  const long grid = items < resident ? items : resident;
   profile_before("prefill_attention_mfma", s);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3((unsigned)blocks), dim3(kPfThreads), 0,
-                     s, a, n_mtiles);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kPfThreads), 0, s,
+                     a);
   profile_after(s);
   return hipGetLastError();
 }

@@ -102,19 +102,26 @@ def test_attention_empty_tick_is_ok_without_touching_memory():
     assert attn(S=0, T=0) == OK
 
 
+def _plan_bytes(cap_dec, cap_pf):
+    return -(-(4 + 2 * (cap_dec + cap_pf)) * 4 // 256) * 256
+
+
 def test_workspace_size_query():
     lib = pa.lib()
-    # one partition: no scratch
-    assert lib.pa_paged_attention_workspace_size(64, 64, 32, 128, 1, 512, 256, 0, BF16) == 0
+    ws = lib.pa_paged_attention_workspace_size
+    # one partition: only the plan lists (64 decode items)
+    assert ws(64, 64, 32, 128, 1, 512, 256, 0, BF16) == _plan_bytes(64, 0)
     # 4096 keys in 512-key partitions: 8 partials of (D + 2) floats per (row, head)
-    n = lib.pa_paged_attention_workspace_size(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
-    assert n == 64 * 8 * 32 * 130 * 4
-    # explicit split of 1024 keys halves it
-    assert lib.pa_paged_attention_workspace_size(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == n // 2
-    # fp32 with prefill rows takes the per-token path: one row per token
-    m = lib.pa_paged_attention_workspace_size(4, 40, 4, 16, 20, 1024, 16, 0, F32)
-    assert m == 40 * 2 * 4 * 18 * 4
-    assert lib.pa_paged_attention_workspace_size(-1, 4, 4, 16, 1, 64, 16, 0, F32) == 0
+    n = ws(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
+    assert n == _plan_bytes(64 * 8, 0) + 64 * 8 * 32 * 130 * 4
+    # an explicit split of 1024 keys halves the partials
+    assert ws(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == _plan_bytes(64 * 4, 0) + 64 * 4 * 32 * 130 * 4
+    # prefill rows: at most min(S * ceil(Lmax / 16), T / 16 + S) row tiles are planned
+    assert ws(51, 2096, 32, 128, 1024, 4096, 256, 0, BF16) == (
+        _plan_bytes(51 * 8, min(51 * 64, 2096 // 16 + 51)) + 51 * 8 * 32 * 130 * 4)
+    # fp32 with prefill rows takes the per-token path: one row per token, no plan
+    assert ws(4, 40, 4, 16, 20, 1024, 16, 0, F32) == 40 * 2 * 4 * 18 * 4
+    assert ws(-1, 4, 4, 16, 1, 64, 16, 0, F32) == 0
 
 
 def cache_write(**kw):
