@@ -215,7 +215,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D,
     sm.pages[i] = clampi(bt_row[pg0 + i], 0, a.num_pages - 1);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int sub = lane % LPK;
   const int slot = lane / LPK;
 
@@ -248,23 +248,27 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D,
   const float sl2e = a.scale_log2e;
   constexpr int STEP = kWaves * KPI;
 
+  // Two register buffers alternate: while one step computes, the next step's
+  // loads are in flight. The loads are issued unconditionally (past the end
+  // they re-read a valid row and are masked), so the number of outstanding
+  // loads is the same on every path and the compiler waits only for the
+  // buffer being consumed.
   uint32_t kA[SH::UNROLL][WORDS], vA[SH::UNROLL][WORDS];
   uint32_t kB[SH::UNROLL][WORDS], vB[SH::UNROLL][WORDS];
   int base = kbeg + wave * KPI;
-  if (base < kend)
-    load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, base, kbeg, kend, slot);
-  while (base < kend) {
-    int nb = base + STEP;
-    if (nb < kend)
-      load_step<SH>(kB, vB, kbase, vbase, sm.pages, pg0, P, slot_stride, nb, kbeg, kend, slot);
+  const int nsteps = base < kend ? (kend - base + STEP - 1) / STEP : 0;  // wave-uniform
+  load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, base, kbeg, kend, slot);
+  for (int it = 0; it < nsteps; it += 2) {
+    load_step<SH>(kB, vB, kbase, vbase, sm.pages, pg0, P, slot_stride, base + STEP, kbeg, kend,
+                  slot);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next step's loads ahead of this compute
     compute_step<SH, G>(kA, vA, qw, m, lsum, o, base, kend, slot, sl2e);
-    base = nb;
-    if (base >= kend) break;
-    nb = base + STEP;
-    if (nb < kend)
-      load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, nb, kbeg, kend, slot);
-    compute_step<SH, G>(kB, vB, qw, m, lsum, o, base, kend, slot, sl2e);
-    base = nb;
+    base += STEP;
+    load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, base + STEP, kbeg, kend,
+                  slot);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < nsteps) compute_step<SH, G>(kB, vB, qw, m, lsum, o, base, kend, slot, sl2e);
+    base += STEP;
   }
 
   // Merge the slots of this wave (lanes sub, sub + LPK, ...).

@@ -100,14 +100,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   __syncthreads();
 
   // ---- bin offsets in decreasing cost: bin b starts after all bins > b ----
+  int pf_total = 0;
   // (kCostBins = 2 * kPlanThreads: each thread owns bins 2t and 2t+1 of the
   // reversed order)
   {
     const int r0 = 2 * tid, r1 = 2 * tid + 1;  // positions in decreasing-cost order
     const int b0 = kCostBins - 1 - r0, b1 = kCostBins - 1 - r1;
     const int h0 = s_hist[b0], h1 = s_hist[b1];
-    int total;
-    const int off = block_exclusive_scan(h0 + h1, s_buf, &total);
+    const int off = block_exclusive_scan(h0 + h1, s_buf, &pf_total);
     s_cur[b0] = off;
     s_cur[b1] = off + h0;
   }
@@ -132,10 +132,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   }
   __syncthreads();
   if (tid == 0) {
-    int npf = 0;
-    for (int b = 0; b < kCostBins; ++b) npf += s_hist[b];
     plan[0] = min(dec_base, cap_dec);
-    plan[1] = min(npf, cap_pf);
+    plan[1] = min(pf_total, cap_pf);
     plan[2] = 0;
     plan[3] = 0;
   }

@@ -52,72 +52,78 @@ struct TileRegs {
   uint4 va[VCH], vb[VCH];
 };
 
+// Page id of key j from the LDS copy of the sequence's page table (the host
+// guarantees that a sequence's pages fit: ceil(max_seq_len / P) <= kItemPages).
+__device__ __forceinline__ int page_of(int j, int P, const int* s_pt) { return s_pt[j / P]; }
+
+// Component-wise select (a select of whole structs can become a select of
+// addresses, which forces the registers into scratch memory).
+__device__ __forceinline__ uint4 keep_if(const uint4& v, bool ok) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+// Issue the global loads of one 32-key tile. Every lane always issues the same
+// loads (keys past kmax re-read key kmax - 1 and are zeroed at the store), so
+// the count of outstanding loads never depends on the data.
 template <int D>
 __device__ __forceinline__ void tile_load(TileRegs<D>& r, const char* kpool, const char* vpool,
-                                          const int* bt_row, int num_pages, int P,
-                                          size_t slot_stride, int kb0, int kmax, int tid) {
+                                          const int* s_pt, int P, size_t slot_stride, int kb0,
+                                          int kmax, int tid) {
   constexpr int C16 = TileRegs<D>::C16;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-    const int c = tid + i * kPfThreads;
+    const int c = min(tid + i * kPfThreads, kBN * C16 - 1);
     const int key = c / C16, d8 = c % C16;
-    const int j = kb0 + key;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (c < kBN * C16 && j < kmax) {
-      const int page = clampi(bt_row[j / P], 0, num_pages - 1);
-      x = *reinterpret_cast<const uint4*>(kpool + ((size_t)page * P + j % P) * slot_stride +
-                                          d8 * 16);
-    }
-    r.k[i] = x;
+    const int j = min(kb0 + key, kmax - 1);
+    const int page = page_of(j, P, s_pt);
+    r.k[i] = *reinterpret_cast<const uint4*>(kpool + ((size_t)page * P + j % P) * slot_stride +
+                                             d8 * 16);
   }
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::VCH; ++i) {
-    const int c = tid + i * kPfThreads;
+    const int c = min(tid + i * kPfThreads, (kBN / 2) * C16 - 1);
     const int kp = c % (kBN / 2), d8 = c / (kBN / 2);
-    const int j = kb0 + 2 * kp;
-    uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-    if (c < (kBN / 2) * C16) {
-      if (j < kmax) {
-        const int page = clampi(bt_row[j / P], 0, num_pages - 1);
-        xa = *reinterpret_cast<const uint4*>(vpool + ((size_t)page * P + j % P) * slot_stride +
-                                             d8 * 16);
-      }
-      if (j + 1 < kmax) {
-        const int page = clampi(bt_row[(j + 1) / P], 0, num_pages - 1);
-        xb = *reinterpret_cast<const uint4*>(vpool + ((size_t)page * P + (j + 1) % P) *
-                                                         slot_stride + d8 * 16);
-      }
-    }
-    r.va[i] = xa;
-    r.vb[i] = xb;
+    const int ja = min(kb0 + 2 * kp, kmax - 1);
+    const int jb = min(kb0 + 2 * kp + 1, kmax - 1);
+    const int pa = page_of(ja, P, s_pt);
+    const int pb = page_of(jb, P, s_pt);
+    r.va[i] = *reinterpret_cast<const uint4*>(vpool + ((size_t)pa * P + ja % P) * slot_stride +
+                                              d8 * 16);
+    r.vb[i] = *reinterpret_cast<const uint4*>(vpool + ((size_t)pb * P + jb % P) * slot_stride +
+                                              d8 * 16);
   }
 }
 
 template <int D, int KSTR, int VSTR>
 __device__ __forceinline__ void tile_store(const TileRegs<D>& r, uint16_t* s_k, uint16_t* s_vt,
-                                           int tid) {
+                                           int kb0, int kmax, int tid) {
   constexpr int C16 = TileRegs<D>::C16;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KCH; ++i) {
     const int c = tid + i * kPfThreads;
     if (c < kBN * C16) {
       const int key = c / C16, d8 = c % C16;
-      *reinterpret_cast<uint4*>(&s_k[key * KSTR + d8 * 8]) = r.k[i];
+      *reinterpret_cast<uint4*>(&s_k[key * KSTR + d8 * 8]) = keep_if(r.k[i], kb0 + key < kmax);
     }
   }
+  uint32_t* vt = reinterpret_cast<uint32_t*>(s_vt);
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::VCH; ++i) {
     const int c = tid + i * kPfThreads;
     if (c < (kBN / 2) * C16) {
       const int kp = c % (kBN / 2), d8 = c / (kBN / 2);
-      const uint32_t* wa = reinterpret_cast<const uint32_t*>(&r.va[i]);
-      const uint32_t* wb = reinterpret_cast<const uint32_t*>(&r.vb[i]);
-      uint32_t* vt = reinterpret_cast<uint32_t*>(s_vt);
+      const uint4 xa = keep_if(r.va[i], kb0 + 2 * kp < kmax);
+      const uint4 xb = keep_if(r.vb[i], kb0 + 2 * kp + 1 < kmax);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
+        const uint32_t wa = word_of(xa, w), wb = word_of(xb, w);
         const int d = d8 * 8 + 2 * w;
-        vt[(d * VSTR) / 2 + kp] = (wa[w] & 0xFFFFu) | (wb[w] << 16);
-        vt[((d + 1) * VSTR) / 2 + kp] = (wa[w] >> 16) | (wb[w] & 0xFFFF0000u);
+        vt[(d * VSTR) / 2 + kp] = (wa & 0xFFFFu) | (wb << 16);
+        vt[((d + 1) * VSTR) / 2 + kp] = (wa >> 16) | (wb & 0xFFFF0000u);
       }
     }
   }
@@ -134,10 +140,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // double-buffered tiles: the next tile is written while the current one is read
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kBN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * VSTR];
+  __shared__ int s_pt[kPrefillMaxPages];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int col = lane & 15;            // query row within a 16-row block
   const int grp = lane >> 4;            // 0..3
   const size_t row_bytes = (size_t)D * 2;
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int L = a.qsl[s + 1] - q0;
     const int i0 = mt * TM;
     int n = a.seq_lens[s];
-    n = min(n, a.max_blocks * a.P);
+    n = min(n, min(a.max_blocks, kPrefillMaxPages) * a.P);  // staged page table bound
     if (L <= 1 || i0 >= L || q0 < 0 || q0 + L > a.T || n < L) continue;  // uniform per item
     const int i1 = min(L, i0 + TM);
     const int kmax = n - L + i1;          // keys visible to the tile's last row
@@ -179,13 +186,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       tok[mb] = i0 + rr / G;
       head[mb] = kvh * G + rr % G;
       const bool ok = tok[mb] < i1;
-      const char* qrow =
-          (const char*)a.q + ((size_t)(q0 + tok[mb]) * Hq + head[mb]) * row_bytes;
+      const int tq = ok ? tok[mb] : i1 - 1;  // rows past the chunk read a valid row, zeroed
+      const char* qrow = (const char*)a.q + ((size_t)(q0 + tq) * Hq + head[mb]) * row_bytes;
 #pragma unroll
       for (int ds = 0; ds < DSTEPS; ++ds) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (ok) x = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
-        qop[mb][ds] = x;
+        const uint4 x = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
+        qop[mb][ds] = keep_if(x, ok);
       }
     }
 
@@ -203,16 +209,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const char* kpool = (const char*)a.k_pool + (size_t)kvh * row_bytes;
     const char* vpool = (const char*)a.v_pool + (size_t)kvh * row_bytes;
 
+    const int npg = min((kmax + P - 1) / P, kPrefillMaxPages);
+    for (int i = tid; i < npg; i += kPfThreads) s_pt[i] = clampi(bt_row[i], 0, a.num_pages - 1);
+    __syncthreads();
+
     TileRegs<D> regs;
-    tile_load<D>(regs, kpool, vpool, bt_row, a.num_pages, P, slot_stride, 0, kmax, tid);
+    tile_load<D>(regs, kpool, vpool, s_pt, P, slot_stride, 0, kmax, tid);
 
     for (int kt = 0; kt < ntiles; ++kt) {
       const int buf = kt & 1;
       const int kb0 = kt * kBN;
-      tile_store<D, KSTR, VSTR>(regs, s_k[buf], s_vt[buf], tid);
-      if (kt + 1 < ntiles)
-        tile_load<D>(regs, kpool, vpool, bt_row, a.num_pages, P, slot_stride, kb0 + kBN, kmax,
-                     tid);
+      tile_store<D, KSTR, VSTR>(regs, s_k[buf], s_vt[buf], kb0, kmax, tid);
+      // next tile's loads, issued unconditionally (past the end they are discarded)
+      tile_load<D>(regs, kpool, vpool, s_pt, P, slot_stride, kb0 + kBN, kmax, tid);
       __syncthreads();
       const uint16_t* sk = s_k[buf];
       const uint16_t* svt = s_vt[buf];
