@@ -32,7 +32,8 @@
  * - dtype PA_F32 = float32 storage, PA_BF16 = bfloat16 storage; all
  *   arithmetic accumulates in float32.
  * - Supported shapes: D in {16, 64, 128} for PA_F32, {64, 128} for PA_BF16;
- *   Hq / Hkv in {1, 2, 4, 8}; P a multiple of 16. Others: PA_ERR_UNSUPPORTED.
+ *   Hq / Hkv in {1, 2, 4, 8}; P (page size) a power of two >= 16. Others:
+ *   PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
 #define PA_H

@@ -251,7 +251,8 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
     return PA_ERR_INVALID_ARG;
   if ((long)num_pages * page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
-  if (page_size % 16 || !decode_supported(dtype, head_dim, G)) return PA_ERR_UNSUPPORTED;
+  if (page_size < 16 || (page_size & (page_size - 1)) || !decode_supported(dtype, head_dim, G))
+    return PA_ERR_UNSUPPORTED;  // pages: a power of two of at least 16 tokens
   if (T == 0 || S == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc || !out)
     return PA_ERR_INVALID_ARG;
@@ -288,6 +289,8 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.Hkv = Hkv;
   a.D = head_dim;
   a.P = page_size;
+  a.p_shift = 0;
+  while ((1 << a.p_shift) < page_size) ++a.p_shift;
   a.num_pages = num_pages;
   a.max_blocks = max_blocks_per_seq;
   a.max_query_len = max_query_len;

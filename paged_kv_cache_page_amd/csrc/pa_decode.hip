@@ -44,9 +44,13 @@ struct DecodeShape {
   static constexpr int DPL = D / LPK;            // head dims held by a lane
   static constexpr int EPV = 16 / EB;            // elements per 16-byte vector
   static constexpr int KPW = 64 / LPK;           // keys per wave step (slots)
-  static constexpr int UNROLL = 2;               // steps per buffer; two buffers alternate
-  static constexpr int KPI = KPW * UNROLL;       // keys per wave iteration
+  // steps per buffer: a buffer always covers 16 consecutive keys, so with pages
+  // of >= 16 keys (a power of two) and 16-aligned starts it never crosses a page
+  static constexpr int UNROLL = 16 / KPW;
+  static constexpr int KPI = KPW * UNROLL;       // keys per buffer (16)
   static_assert(LANE_BYTES == 16 || LANE_BYTES == 32, "lane row share must be 16 or 32 bytes");
+  static_assert(KPI == 16, "a buffer covers 16 keys");
+  static_assert(EB == 4 || UNROLL == 2, "bf16 P.V pairs the two steps of a buffer");
   // Head-dim index of the lane's local dim i (sub = lane % LPK).
   __device__ static int dim_of(int sub, int i) {
     return ((i / EPV) * LPK + sub) * EPV + (i % EPV);
@@ -103,60 +107,95 @@ struct DecodeSmem {
   float l[kWaves][G];
 };
 
-// Issue the loads of one buffer: UNROLL steps of KPW keys starting at `base`.
+// Issue the loads of one buffer: the 16 keys starting at `base` (wave-uniform,
+// a multiple of 16), all in one page. The page and the row of `base` are
+// wave-uniform, so the address is a scalar base plus a per-lane 32-bit offset
+// fixed for the whole item; past the end of the range the buffer re-reads the
+// range's first keys (its values are then masked).
 template <typename SH>
 __device__ __forceinline__ void load_step(uint32_t (&kr)[SH::UNROLL][SH::WORDS],
                                           uint32_t (&vr)[SH::UNROLL][SH::WORDS],
                                           const char* kbase, const char* vbase,
-                                          const int* pages, int pg0, int P, size_t slot_stride,
-                                          int base, int kbeg, int kend, int slot) {
+                                          const int* pages, int pg0, int p_shift,
+                                          size_t slot_stride, int base, int kbeg, int kend,
+                                          uint32_t lane_off) {
+  const int bb = base < kend ? base : kbeg;
+  const int page = __builtin_amdgcn_readfirstlane(pages[(bb >> p_shift) - pg0]);
+  const int row0 = bb & ((1 << p_shift) - 1);
+  const size_t step_off = (((size_t)page << p_shift) + row0) * slot_stride;
 #pragma unroll
   for (int u = 0; u < SH::UNROLL; ++u) {
-    const int j = base + u * SH::KPW + slot;
-    const int jj = j < kend ? j : kbeg;  // invalid keys read a valid row and are masked later
-    const int page = pages[jj / P - pg0];
-    const size_t off = ((size_t)page * P + (jj % P)) * slot_stride;
+    const size_t uoff = step_off + (size_t)u * SH::KPW * slot_stride;  // uniform
+    const char* kp = kbase + uoff;
+    const char* vp = vbase + uoff;
 #pragma unroll
     for (int l = 0; l < SH::LOADS; ++l) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kbase + off + l * SH::LPK * 16);
+      const uint4 x = *reinterpret_cast<const uint4*>(kp + lane_off + l * SH::LPK * 16);
       kr[u][4 * l] = x.x; kr[u][4 * l + 1] = x.y; kr[u][4 * l + 2] = x.z; kr[u][4 * l + 3] = x.w;
     }
 #pragma unroll
     for (int l = 0; l < SH::LOADS; ++l) {
-      const uint4 x = *reinterpret_cast<const uint4*>(vbase + off + l * SH::LPK * 16);
+      const uint4 x = *reinterpret_cast<const uint4*>(vp + lane_off + l * SH::LPK * 16);
       vr[u][4 * l] = x.x; vr[u][4 * l + 1] = x.y; vr[u][4 * l + 2] = x.z; vr[u][4 * l + 3] = x.w;
     }
   }
 }
 
-// Scores, online softmax and P.V for one buffer.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Scores, online softmax and P.V for one buffer (16 keys of the wave).
 template <typename SH, int G>
 __device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH::WORDS],
-                                             const uint32_t (&vr)[SH::UNROLL][SH::WORDS],
+                                             uint32_t (&vr)[SH::UNROLL][SH::WORDS],
                                              const uint32_t (&qw)[G][SH::WORDS], float (&m)[G],
                                              float (&lsum)[G], float (&o)[G][SH::DPL], int base,
                                              int kend, int slot, float sl2e) {
   constexpr int UNROLL = SH::UNROLL, WORDS = SH::WORDS, DPL = SH::DPL;
+  bool valid[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) valid[u] = base + u * SH::KPW + slot < kend;
+  // Rows past the end may hold anything (NaN included); zero their V so that
+  // a zero weight times them stays zero. Only the last buffer of a range is
+  // partial, and the test is wave-uniform.
+  if (base + SH::KPI > kend) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int w = 0; w < WORDS; ++w) vr[u][w] = valid[u] ? vr[u][w] : 0u;
+  }
   float sc[UNROLL][G];
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const bool valid = base + u * SH::KPW + slot < kend;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float acc = 0.f;
       if constexpr (SH::EB == 2) {
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 #pragma unroll
-        for (int w = 0; w < WORDS; ++w)
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
-                                                __builtin_bit_cast(bf16x2, kr[u][w]), acc, false);
+        for (int w = 0; w < WORDS; ++w) acc = dot2_bf16(qw[g][w], kr[u][w], acc);
       } else {
 #pragma unroll
         for (int w = 0; w < WORDS; ++w)
           acc = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kr[u][w]), acc);
       }
       acc = group_sum<SH::LPK>(acc);
-      sc[u][g] = valid ? acc * sl2e : -INFINITY;
+      sc[u][g] = valid[u] ? acc * sl2e : -INFINITY;
+    }
+  }
+  // bf16: the two steps' V rows interleaved per dim, (v_u0[d], v_u1[d]), so
+  // that one v_dot2 adds both keys' contributions to one output dim.
+  uint32_t vlo[SH::EB == 2 ? WORDS : 1], vhi[SH::EB == 2 ? WORDS : 1];
+  if constexpr (SH::EB == 2) {
+#pragma unroll
+    for (int w = 0; w < WORDS; ++w) {
+      vlo[w] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u);
+      vhi[w] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u);
     }
   }
 #pragma unroll
@@ -173,17 +212,21 @@ __device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH
 #pragma unroll
       for (int i = 0; i < DPL; ++i) o[g][i] *= corr;
     }
+    if constexpr (SH::EB == 2) {
+      // weights rounded to bf16 once; the sum uses the same rounded values
+      const f32x2_t pf = {fast_exp2(sc[0][g] - m[g]), fast_exp2(sc[1][g] - m[g])};
+      const uint32_t pp = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2e_t));
+      lsum[g] += bf16_lo(pp) + bf16_hi(pp);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const float p = fast_exp2(sc[u][g] - m[g]);
-      lsum[g] += p;
-      if constexpr (SH::EB == 2) {
+      for (int w = 0; w < WORDS; ++w) {
+        o[g][2 * w] = dot2_bf16(pp, vlo[w], o[g][2 * w]);
+        o[g][2 * w + 1] = dot2_bf16(pp, vhi[w], o[g][2 * w + 1]);
+      }
+    } else {
 #pragma unroll
-        for (int w = 0; w < WORDS; ++w) {
-          o[g][2 * w] = fmaf(p, bf16_lo(vr[u][w]), o[g][2 * w]);
-          o[g][2 * w + 1] = fmaf(p, bf16_hi(vr[u][w]), o[g][2 * w + 1]);
-        }
-      } else {
+      for (int u = 0; u < UNROLL; ++u) {
+        const float p = fast_exp2(sc[u][g] - m[g]);
+        lsum[g] += p;
 #pragma unroll
         for (int w = 0; w < WORDS; ++w) o[g][w] = fmaf(p, __uint_as_float(vr[u][w]), o[g][w]);
       }
@@ -207,9 +250,8 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D,
   const int kend = min(ri.n_eff, kbeg + PT);
   const int nparts = (ri.n_eff + PT - 1) / PT;
 
-  const int P = a.P;
-  const int pg0 = kbeg / P;
-  const int npg = (kend - 1) / P - pg0 + 1;
+  const int pg0 = kbeg >> a.p_shift;
+  const int npg = ((kend - 1) >> a.p_shift) - pg0 + 1;
   const int* bt_row = a.block_tables + (size_t)ri.seq * a.max_blocks;
   for (int i = threadIdx.x; i < npg; i += kThreads)
     sm.pages[i] = clampi(bt_row[pg0 + i], 0, a.num_pages - 1);
@@ -242,30 +284,32 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D,
   }
   __syncthreads();  // pages ready
 
-  const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes + sub * 16;
-  const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes + sub * 16;
+  const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes;
+  const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes;
   const size_t slot_stride = (size_t)a.Hkv * row_bytes;  // bytes between consecutive slots
+  const uint32_t lane_off = (uint32_t)(slot * slot_stride) + sub * 16;
   const float sl2e = a.scale_log2e;
+  const int p_shift = a.p_shift;
   constexpr int STEP = kWaves * KPI;
 
-  // Two register buffers alternate: while one step computes, the next step's
-  // loads are in flight. The loads are issued unconditionally (past the end
-  // they re-read a valid row and are masked), so the number of outstanding
-  // loads is the same on every path and the compiler waits only for the
-  // buffer being consumed.
+  // Two register buffers alternate: while one computes, the other's loads are
+  // in flight. The loads are issued unconditionally, so the number of
+  // outstanding loads is the same on every path and the compiler waits only
+  // for the buffer being consumed.
   uint32_t kA[SH::UNROLL][WORDS], vA[SH::UNROLL][WORDS];
   uint32_t kB[SH::UNROLL][WORDS], vB[SH::UNROLL][WORDS];
   int base = kbeg + wave * KPI;
   const int nsteps = base < kend ? (kend - base + STEP - 1) / STEP : 0;  // wave-uniform
-  load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, base, kbeg, kend, slot);
+  load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, p_shift, slot_stride, base, kbeg, kend,
+                lane_off);
   for (int it = 0; it < nsteps; it += 2) {
-    load_step<SH>(kB, vB, kbase, vbase, sm.pages, pg0, P, slot_stride, base + STEP, kbeg, kend,
-                  slot);
-    __builtin_amdgcn_sched_barrier(0);  // keep the next step's loads ahead of this compute
+    load_step<SH>(kB, vB, kbase, vbase, sm.pages, pg0, p_shift, slot_stride, base + STEP, kbeg,
+                  kend, lane_off);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next buffer's loads ahead of this compute
     compute_step<SH, G>(kA, vA, qw, m, lsum, o, base, kend, slot, sl2e);
     base += STEP;
-    load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, P, slot_stride, base + STEP, kbeg, kend,
-                  slot);
+    load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, p_shift, slot_stride, base + STEP, kbeg,
+                  kend, lane_off);
     __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < nsteps) compute_step<SH, G>(kB, vB, qw, m, lsum, o, base, kend, slot, sl2e);
     base += STEP;

@@ -23,6 +23,7 @@ struct AttnArgs {
   int* plan;           // work lists written by the plan kernel (see pa_plan.hip)
   int32_t cap_dec, cap_pf;  // capacities of the two lists
   int32_t S, T, Hq, Hkv, D, P, num_pages, max_blocks;
+  int32_t p_shift;      // log2(P); P is a power of two
   int32_t max_query_len, max_seq_len;
   int32_t part_tokens;  // keys per split-KV partition
   int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / part_tokens))

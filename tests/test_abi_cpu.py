@@ -84,6 +84,8 @@ def attn(**kw):
     (dict(D=96), UNSUPPORTED),
     (dict(D=16), UNSUPPORTED),                # bf16 needs D in {64, 128}
     (dict(P=24), UNSUPPORTED),
+    (dict(P=48), UNSUPPORTED),                # pages must be a power of two
+    (dict(P=8), UNSUPPORTED),
     (dict(Hq=32, Hkv=2), UNSUPPORTED),        # group 16
     (dict(q=None), INVALID),
     (dict(bt=None), INVALID),
