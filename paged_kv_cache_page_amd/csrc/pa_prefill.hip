@@ -28,6 +28,8 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * 64;
@@ -129,6 +131,90 @@ __device__ __forceinline__ void tile_store(const TileRegs<D>& r, uint16_t* s_k, 
   }
 }
 
+// One 32-key tile: S^T = K Q^T, online softmax per query row, O^T += V^T P^T.
+template <int D, int G, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t* svt, int kb0,
+                                         const uint4 (&qop)[2][D / 32], const int (&tok)[2],
+                                         int last_key, int n, float sl2e, int col, int grp,
+                                         float (&m_run)[2], float (&l_run)[2],
+                                         f32x4_t (&acc_o)[2][D / 16]) {
+  constexpr int DSTEPS = D / 32;
+  constexpr int DBLK = D / 16;
+
+  // ---- S^T = K Q^T for this wave's two row blocks ----
+  f32x4_t st[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) st[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < DSTEPS; ++ds) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4 kop =
+          *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KSTR + ds * 32 + grp * 8]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) st[mb][kb] = mfma16x16x32(kop, qop[mb][ds], st[mb][kb]);
+    }
+  }
+
+  // ---- online softmax per query row (this lane's column) ----
+  uint4 pop[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int limit = min(last_key + tok[mb], n - 1);
+    float sv[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = kb0 + kb * 16 + grp * 4 + i;
+        const float x = (j <= limit) ? st[mb][kb][i] * sl2e : -INFINITY;
+        sv[kb * 4 + i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // rescale only when some row's running max grows (wave-uniform test)
+    if (__any(tmax > m_run[mb])) {
+      const float mn = fmaxf(m_run[mb], tmax);
+      const float corr = fast_exp2(m_run[mb] - mn);
+      m_run[mb] = mn;
+      l_run[mb] *= corr;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        acc_o[mb][db][0] *= corr;
+        acc_o[mb][db][1] *= corr;
+        acc_o[mb][db][2] *= corr;
+        acc_o[mb][db][3] *= corr;
+      }
+    }
+    // weights rounded once to bf16 (hardware round-to-nearest-even); the row
+    // sum adds the same rounded values the MFMA multiplies
+    uint32_t pw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x2_t pf = {fast_exp2(sv[2 * k] - m_run[mb]), fast_exp2(sv[2 * k + 1] - m_run[mb])};
+      pw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2e_t));
+      l_run[mb] += bf16_lo(pw[k]) + bf16_hi(pw[k]);
+    }
+    pop[mb] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+  }
+
+  // ---- O^T += V^T P^T ----
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    const int d = db * 16 + col;
+    const uint2 lo = *reinterpret_cast<const uint2*>(&svt[d * VSTR + grp * 4]);
+    const uint2 hi = *reinterpret_cast<const uint2*>(&svt[d * VSTR + 16 + grp * 4]);
+    const uint4 vop = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc_o[mb][db] = mfma16x16x32(vop, pop[mb], acc_o[mb][db]);
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(AttnArgs a) {
   constexpr int TM = kRowsPerWg / G;    // tokens per workgroup
@@ -213,87 +299,23 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int i = tid; i < npg; i += kPfThreads) s_pt[i] = clampi(bt_row[i], 0, a.num_pages - 1);
     __syncthreads();
 
-    TileRegs<D> regs;
-    tile_load<D>(regs, kpool, vpool, s_pt, P, slot_stride, 0, kmax, tid);
-
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int buf = kt & 1;
-      const int kb0 = kt * kBN;
-      tile_store<D, KSTR, VSTR>(regs, s_k[buf], s_vt[buf], kb0, kmax, tid);
-      // next tile's loads, issued unconditionally (past the end they are discarded)
-      tile_load<D>(regs, kpool, vpool, s_pt, P, slot_stride, kb0 + kBN, kmax, tid);
+    // Two register tiles alternate, each loaded two tiles ahead of its use, so
+    // a tile's global loads have two tiles of compute to arrive.
+    TileRegs<D> rA, rB;
+    tile_load<D>(rA, kpool, vpool, s_pt, P, slot_stride, 0, kmax, tid);
+    tile_load<D>(rB, kpool, vpool, s_pt, P, slot_stride, kBN, kmax, tid);
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile_store<D, KSTR, VSTR>(rA, s_k[0], s_vt[0], kt * kBN, kmax, tid);
+      tile_load<D>(rA, kpool, vpool, s_pt, P, slot_stride, (kt + 2) * kBN, kmax, tid);
       __syncthreads();
-      const uint16_t* sk = s_k[buf];
-      const uint16_t* svt = s_vt[buf];
-
-      // ---- S^T = K Q^T for this wave's two row blocks ----
-      f32x4_t st[2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) st[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < DSTEPS; ++ds) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint4 kop =
-              *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KSTR + ds * 32 + grp * 8]);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) st[mb][kb] = mfma16x16x32(kop, qop[mb][ds], st[mb][kb]);
-        }
-      }
-
-      // ---- online softmax per query row (this lane's column) ----
-      uint4 pop[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int limit = min(last_key + tok[mb], n - 1);
-        float sv[8];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = kb0 + kb * 16 + grp * 4 + i;
-            const float x = (j <= limit) ? st[mb][kb][i] * sl2e : -INFINITY;
-            sv[kb * 4 + i] = x;
-            tmax = fmaxf(tmax, x);
-          }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m_run[mb], tmax);
-        const float corr = fast_exp2(m_run[mb] - mn);
-        m_run[mb] = mn;
-        float psum = 0.f;
-        float pv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pv[k] = fast_exp2(sv[k] - mn);
-          psum += pv[k];
-        }
-        l_run[mb] = l_run[mb] * corr + psum;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          acc_o[mb][db][0] *= corr;
-          acc_o[mb][db][1] *= corr;
-          acc_o[mb][db][2] *= corr;
-          acc_o[mb][db][3] *= corr;
-        }
-        pop[mb] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                             pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
-      }
-
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int d = db * 16 + col;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&svt[d * VSTR + grp * 4]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&svt[d * VSTR + 16 + grp * 4]);
-        const uint4 vop = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc_o[mb][db] = mfma16x16x32(vop, pop[mb], acc_o[mb][db]);
-      }
+      tile_compute<D, G, KSTR, VSTR>(s_k[0], s_vt[0], kt * kBN, qop, tok, last_key, n, sl2e, col,
+                                     grp, m_run, l_run, acc_o);
+      if (kt + 1 >= ntiles) break;
+      tile_store<D, KSTR, VSTR>(rB, s_k[1], s_vt[1], (kt + 1) * kBN, kmax, tid);
+      tile_load<D>(rB, kpool, vpool, s_pt, P, slot_stride, (kt + 3) * kBN, kmax, tid);
+      __syncthreads();
+      tile_compute<D, G, KSTR, VSTR>(s_k[1], s_vt[1], (kt + 1) * kBN, qop, tok, last_key, n,
+                                     sl2e, col, grp, m_run, l_run, acc_o);
     }
     __syncthreads();  // the next item's first store reuses buffer 0
 
