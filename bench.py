@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--kv-split", type=int, default=0)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -116,6 +118,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        # a plain copy of known size: the traffic counters' reading for it gives the
+        # scale factor from counter units to bytes
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "reads": n, "writes": n}))
+        return
     pa.lib()
     dev = "cuda:0"
     cfg = WORKLOADS[args.workload]

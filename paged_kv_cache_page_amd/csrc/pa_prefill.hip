@@ -54,10 +54,6 @@ struct TileRegs {
   uint4 va[VCH], vb[VCH];
 };
 
-// Page id of key j from the LDS copy of the sequence's page table (the host
-// guarantees that a sequence's pages fit: ceil(max_seq_len / P) <= kItemPages).
-__device__ __forceinline__ int page_of(int j, int P, const int* s_pt) { return s_pt[j / P]; }
-
 // Component-wise select (a select of whole structs can become a select of
 // addresses, which forces the registers into scratch memory).
 __device__ __forceinline__ uint4 keep_if(const uint4& v, bool ok) {
@@ -68,22 +64,29 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
   return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
 }
 
-// Issue the global loads of one 32-key tile. Every lane always issues the same
-// loads (keys past kmax re-read key kmax - 1 and are zeroed at the store), so
-// the count of outstanding loads never depends on the data.
+// Issue the global loads of one 32-key tile starting at kb0 (a multiple of 32).
+// Pages hold a power of two >= 16 keys, so the tile's keys 0-15 lie in one page
+// and keys 16-31 in one page (the same page when P >= 32): two wave-uniform page
+// bases, and a 32-bit per-lane offset. Keys past kmax re-read key kmax - 1 (and
+// are zeroed at the store), so every lane always issues the same loads and the
+// count of outstanding loads never depends on the data.
 template <int D>
 __device__ __forceinline__ void tile_load(TileRegs<D>& r, const char* kpool, const char* vpool,
-                                          const int* s_pt, int P, size_t slot_stride, int kb0,
-                                          int kmax, int tid) {
+                                          const int* s_pt, int p_shift, size_t page_bytes,
+                                          uint32_t slot_stride, int kb0, int kmax, int tid) {
   constexpr int C16 = TileRegs<D>::C16;
+  const int jA = min(kb0, kmax - 1), jB = min(kb0 + 16, kmax - 1);
+  const size_t offA = (size_t)__builtin_amdgcn_readfirstlane(s_pt[jA >> p_shift]) * page_bytes;
+  const size_t offB = (size_t)__builtin_amdgcn_readfirstlane(s_pt[jB >> p_shift]) * page_bytes;
+  const int rmask = (1 << p_shift) - 1;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KCH; ++i) {
     const int c = min(tid + i * kPfThreads, kBN * C16 - 1);
     const int key = c / C16, d8 = c % C16;
     const int j = min(kb0 + key, kmax - 1);
-    const int page = page_of(j, P, s_pt);
-    r.k[i] = *reinterpret_cast<const uint4*>(kpool + ((size_t)page * P + j % P) * slot_stride +
-                                             d8 * 16);
+    const uint32_t off = (uint32_t)(j & rmask) * slot_stride + d8 * 16;
+    const char* base = kpool + (key < 16 ? offA : offB);
+    r.k[i] = *reinterpret_cast<const uint4*>(base + off);
   }
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::VCH; ++i) {
@@ -91,12 +94,9 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& r, const char* kpool, con
     const int kp = c % (kBN / 2), d8 = c / (kBN / 2);
     const int ja = min(kb0 + 2 * kp, kmax - 1);
     const int jb = min(kb0 + 2 * kp + 1, kmax - 1);
-    const int pa = page_of(ja, P, s_pt);
-    const int pb = page_of(jb, P, s_pt);
-    r.va[i] = *reinterpret_cast<const uint4*>(vpool + ((size_t)pa * P + ja % P) * slot_stride +
-                                              d8 * 16);
-    r.vb[i] = *reinterpret_cast<const uint4*>(vpool + ((size_t)pb * P + jb % P) * slot_stride +
-                                              d8 * 16);
+    const char* base = vpool + (2 * kp < 16 ? offA : offB);  // keys 2kp and 2kp+1 share a half
+    r.va[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)(ja & rmask) * slot_stride + d8 * 16);
+    r.vb[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)(jb & rmask) * slot_stride + d8 * 16);
   }
 }
 
@@ -134,10 +134,10 @@ __device__ __forceinline__ void tile_store(const TileRegs<D>& r, uint16_t* s_k, 
 // One 32-key tile: S^T = K Q^T, online softmax per query row, O^T += V^T P^T.
 template <int D, int G, int KSTR, int VSTR>
 __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t* svt, int kb0,
-                                         const uint4 (&qop)[2][D / 32], const int (&tok)[2],
-                                         int last_key, int n, float sl2e, int col, int grp,
-                                         float (&m_run)[2], float (&l_run)[2],
-                                         f32x4_t (&acc_o)[2][D / 16]) {
+                                             const uint4 (&qop)[2][D / 32], const int (&tok)[2],
+                                             int last_key, int n, bool masked, float sl2e,
+                                             int col, int grp, float (&m_run)[2],
+                                             float (&l_run)[2], f32x4_t (&acc_o)[2][D / 16]) {
   constexpr int DSTEPS = D / 32;
   constexpr int DBLK = D / 16;
 
@@ -159,24 +159,32 @@ __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t*
   }
 
   // ---- online softmax per query row (this lane's column) ----
+  // Running max m is kept in log2 units (scores * scale * log2 e); a weight is
+  // exp2(s * sl2e - m), one fma and one exp2. Only tiles that reach past some
+  // row's last visible key (the diagonal, and the ragged end) need the mask;
+  // `masked` is wave-uniform.
   uint4 pop[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int limit = min(last_key + tok[mb], n - 1);
     float sv[8];
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kb0 + kb * 16 + grp * 4 + i;
-        const float x = (j <= limit) ? st[mb][kb][i] * sl2e : -INFINITY;
-        sv[kb * 4 + i] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int i = 0; i < 4; ++i) sv[kb * 4 + i] = st[mb][kb][i];
+    if (masked) {
+      const int limit = min(last_key + tok[mb], n - 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb0 + kb * 16 + grp * 4 + i > limit) sv[kb * 4 + i] = -INFINITY;
     }
+    float tmax = sv[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, sv[k]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax *= sl2e;
     // rescale only when some row's running max grows (wave-uniform test)
     if (__any(tmax > m_run[mb])) {
       const float mn = fmaxf(m_run[mb], tmax);
@@ -191,14 +199,15 @@ __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t*
         acc_o[mb][db][3] *= corr;
       }
     }
-    // weights rounded once to bf16 (hardware round-to-nearest-even); the row
-    // sum adds the same rounded values the MFMA multiplies
+    const float neg_m = -m_run[mb];
     uint32_t pw[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const f32x2_t pf = {fast_exp2(sv[2 * k] - m_run[mb]), fast_exp2(sv[2 * k + 1] - m_run[mb])};
+      const float p0 = fast_exp2(fmaf(sv[2 * k], sl2e, neg_m));
+      const float p1 = fast_exp2(fmaf(sv[2 * k + 1], sl2e, neg_m));
+      l_run[mb] += p0 + p1;
+      const f32x2_t pf = {p0, p1};  // rounded once to bf16 (round to nearest even)
       pw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2e_t));
-      l_run[mb] += bf16_lo(pw[k]) + bf16_hi(pw[k]);
     }
     pop[mb] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
   }
@@ -238,6 +247,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int P = a.P;
   const float sl2e = a.scale_log2e;
   const size_t slot_stride = (size_t)a.Hkv * row_bytes;
+  const uint32_t slot_stride32 = (uint32_t)slot_stride;  // a page is far below 4 GiB
+  const int p_shift = a.p_shift;
+  const size_t page_bytes = slot_stride << p_shift;
   const int* items = a.plan + kPlanHeaderInts + 2 * (size_t)a.cap_dec;
   const int total = a.plan[1] * a.Hkv;
   const int nwg = gridDim.x;
@@ -262,6 +274,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int kmax = n - L + i1;          // keys visible to the tile's last row
     const int ntiles = (kmax + kBN - 1) / kBN;
     const int last_key = n - L;           // row i sees keys <= last_key + i
+    // the smallest key limit among this wave's rows: tiles ending at or below it
+    // need no mask (wave-uniform)
+    const int min_limit = last_key + i0 + (wave * kRowsPerWave) / G;
 
     // Q^T operand: rows of this lane, 8 dims per k-step.
     uint4 qop[2][DSTEPS];
@@ -302,20 +317,24 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // Two register tiles alternate, each loaded two tiles ahead of its use, so
     // a tile's global loads have two tiles of compute to arrive.
     TileRegs<D> rA, rB;
-    tile_load<D>(rA, kpool, vpool, s_pt, P, slot_stride, 0, kmax, tid);
-    tile_load<D>(rB, kpool, vpool, s_pt, P, slot_stride, kBN, kmax, tid);
+    tile_load<D>(rA, kpool, vpool, s_pt, p_shift, page_bytes, slot_stride32, 0, kmax, tid);
+    tile_load<D>(rB, kpool, vpool, s_pt, p_shift, page_bytes, slot_stride32, kBN, kmax, tid);
     for (int kt = 0; kt < ntiles; kt += 2) {
       tile_store<D, KSTR, VSTR>(rA, s_k[0], s_vt[0], kt * kBN, kmax, tid);
-      tile_load<D>(rA, kpool, vpool, s_pt, P, slot_stride, (kt + 2) * kBN, kmax, tid);
+      tile_load<D>(rA, kpool, vpool, s_pt, p_shift, page_bytes, slot_stride32, (kt + 2) * kBN,
+                   kmax, tid);
       __syncthreads();
-      tile_compute<D, G, KSTR, VSTR>(s_k[0], s_vt[0], kt * kBN, qop, tok, last_key, n, sl2e, col,
-                                     grp, m_run, l_run, acc_o);
+      tile_compute<D, G, KSTR, VSTR>(s_k[0], s_vt[0], kt * kBN, qop, tok, last_key, n,
+                                     kt * kBN + kBN - 1 > min_limit, sl2e, col, grp, m_run, l_run,
+                                     acc_o);
       if (kt + 1 >= ntiles) break;
       tile_store<D, KSTR, VSTR>(rB, s_k[1], s_vt[1], (kt + 1) * kBN, kmax, tid);
-      tile_load<D>(rB, kpool, vpool, s_pt, P, slot_stride, (kt + 3) * kBN, kmax, tid);
+      tile_load<D>(rB, kpool, vpool, s_pt, p_shift, page_bytes, slot_stride32, (kt + 3) * kBN,
+                   kmax, tid);
       __syncthreads();
       tile_compute<D, G, KSTR, VSTR>(s_k[1], s_vt[1], (kt + 1) * kBN, qop, tok, last_key, n,
-                                     sl2e, col, grp, m_run, l_run, acc_o);
+                                     (kt + 1) * kBN + kBN - 1 > min_limit, sl2e, col, grp, m_run,
+                                     l_run, acc_o);
     }
     __syncthreads();  // the next item's first store reuses buffer 0
 
