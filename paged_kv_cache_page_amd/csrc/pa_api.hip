@@ -104,10 +104,8 @@ int split_tokens(int requested, int P) {
 
 // Whether prefill rows (L > 1) go to the MFMA kernel; otherwise every row of
 // the tick takes the per-token VALU path.
-bool use_mfma_prefill(pa_dtype_t dt, int D, int max_query_len, int max_seq_len, int P) {
-  if (max_query_len <= 1) return true;
-  const long pages = ((long)max_seq_len + P - 1) / P;
-  return prefill_mfma_supported(dt, D, 1) && pages <= kPrefillMaxPages;
+bool use_mfma_prefill(pa_dtype_t dt, int D, int max_query_len) {
+  return max_query_len <= 1 || prefill_mfma_supported(dt, D, 1);
 }
 
 // Workspace layout: the plan lists (seq mode), padded to 256 bytes, then the
@@ -125,7 +123,7 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
   const int pt = split_tokens(kv_split, P);
   const long max_parts = max_seq_len > 0 ? ((long)max_seq_len + pt - 1) / pt : 1;
   w.max_parts = (int)(max_parts < 1 ? 1 : max_parts);
-  w.token_mode = !use_mfma_prefill(dt, D, max_query_len, max_seq_len, P);
+  w.token_mode = !use_mfma_prefill(dt, D, max_query_len);
   w.cap_dec = 0;
   w.cap_pf = 0;
   w.plan_bytes = 0;

@@ -34,10 +34,7 @@ struct AttnArgs {
 // cap_dec (sequence, partition) pairs, then cap_pf (sequence, row tile) pairs.
 constexpr int kPlanHeaderInts = 4;
 // Query rows per prefill workgroup; a tile holds kPrefillRows / G tokens.
-constexpr int kPrefillRows = 128;
-// Page-table entries of one prefill sequence staged in LDS; the host routes
-// ticks whose ceil(max_seq_len / P) exceeds it away from the MFMA kernel.
-constexpr int kPrefillMaxPages = 4096;
+constexpr int kPrefillRows = 64;
 
 // Workgroups of `func` (launched with `threads` threads) that the current
 // device holds at once: compute units x resident workgroups per unit. Cached

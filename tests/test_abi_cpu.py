@@ -118,9 +118,10 @@ def test_workspace_size_query():
     assert n == _plan_bytes(64 * 8, 0) + 64 * 8 * 32 * 130 * 4
     # an explicit split of 1024 keys halves the partials
     assert ws(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == _plan_bytes(64 * 4, 0) + 64 * 4 * 32 * 130 * 4
-    # prefill rows: at most min(S * ceil(Lmax / 16), T / 16 + S) row tiles are planned
+    # prefill rows: a row tile holds at least 8 tokens (64 rows, group <= 8), so at most
+    # min(S * ceil(Lmax / 8), T / 8 + S) row tiles are planned
     assert ws(51, 2096, 32, 128, 1024, 4096, 256, 0, BF16) == (
-        _plan_bytes(51 * 8, min(51 * 64, 2096 // 16 + 51)) + 51 * 8 * 32 * 130 * 4)
+        _plan_bytes(51 * 8, min(51 * 128, 2096 // 8 + 51)) + 51 * 8 * 32 * 130 * 4)
     # fp32 with prefill rows takes the per-token path: one row per token, no plan
     assert ws(4, 40, 4, 16, 20, 1024, 16, 0, F32) == 40 * 2 * 4 * 18 * 4
     assert ws(-1, 4, 4, 16, 1, 64, 16, 0, F32) == 0
