@@ -79,8 +79,8 @@ int persistent_grid(const void* func, int threads) {
 // ------------------------------------------------------------- helpers -----
 namespace {
 
-constexpr int kDefaultSplitTokens = 512;
-constexpr int kMaxPartPages = 256;  // must match the decode kernel's page staging
+constexpr int kTokenModeSplitTokens = 512;  // partition size of the per-token path
+constexpr int kAutoMinSplitTokens = 256;    // smallest partition the plan kernel picks
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -93,13 +93,25 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-// Keys per split-KV partition actually used for these arguments.
-int split_tokens(int requested, int P) {
-  int pt = requested > 0 ? requested : kDefaultSplitTokens;
-  // the decode kernel stages the page ids of one partition in LDS
-  const int cap = ((kMaxPartPages - 2) * P) / 16 * 16;
-  if (pt > cap) pt = cap;
-  return pt;
+// Largest partition: the decode kernel holds a partition's page ids in one
+// VGPR (64 lanes), and a partition of 63 * P keys spans at most 64 pages.
+int split_max(int P) {
+  const long cap = 63L * P;
+  return (int)((cap < 65536 ? cap : 65536) / 16 * 16);
+}
+
+int split_min(int P) {
+  const int mx = split_max(P);
+  return kAutoMinSplitTokens < mx ? kAutoMinSplitTokens : mx;
+}
+
+// Keys per split-KV partition for these arguments: the request (capped), or
+// 0 = chosen on the device by the plan kernel (per-sequence rows only).
+int split_tokens(int requested, int P, bool token_mode) {
+  const int mx = split_max(P);
+  if (requested > 0) return requested < mx ? requested : mx;
+  if (token_mode) return kTokenModeSplitTokens < mx ? kTokenModeSplitTokens : mx;
+  return 0;
 }
 
 // Whether prefill rows (L > 1) go to the MFMA kernel; otherwise every row of
@@ -120,10 +132,19 @@ struct WsLayout {
 WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int max_seq_len, int P,
                           int kv_split, pa_dtype_t dt) {
   WsLayout w;
-  const int pt = split_tokens(kv_split, P);
-  const long max_parts = max_seq_len > 0 ? ((long)max_seq_len + pt - 1) / pt : 1;
-  w.max_parts = (int)(max_parts < 1 ? 1 : max_parts);
   w.token_mode = !use_mfma_prefill(dt, D, max_query_len);
+  const int pt = split_tokens(kv_split, P, w.token_mode);
+  long max_parts;
+  if (pt > 0) {
+    // fixed partitions of pt keys, aligned to the row start
+    max_parts = max_seq_len > 0 ? ((long)max_seq_len + pt - 1) / pt : 1;
+  } else {
+    // equal chunks of the concatenated key axis, at least split_min keys each:
+    // a row may straddle one chunk boundary more than its length needs
+    const int c = split_min(P);
+    max_parts = max_seq_len > 0 ? ((long)max_seq_len + c - 1) / c + 1 : 1;
+  }
+  w.max_parts = (int)(max_parts < 1 ? 1 : max_parts);
   w.cap_dec = 0;
   w.cap_pf = 0;
   w.plan_bytes = 0;
@@ -136,8 +157,7 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
       const long by_tok = (long)T / tm + S;
       w.cap_pf = by_seq < by_tok ? by_seq : by_tok;
     }
-    w.plan_bytes = ((size_t)(kPlanHeaderInts + 2 * (w.cap_dec + w.cap_pf)) * sizeof(int) + 255) /
-                   256 * 256;
+    w.plan_bytes = (plan_offsets(S, w.cap_dec, w.cap_pf).total * sizeof(int) + 255) / 256 * 256;
   }
   const long rows = w.token_mode ? T : S;
   w.partial_bytes = w.max_parts > 1 ? (size_t)rows * (size_t)w.max_parts * (size_t)Hq *
@@ -268,6 +288,12 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && ((uintptr_t)workspace & 255u)) return PA_ERR_INVALID_ARG;
   if (wl.cap_dec > INT32_MAX / 2 || wl.cap_pf > INT32_MAX / 2) return PA_ERR_INVALID_ARG;
+  // decode rows are laid end to end on one int32 key axis (rows padded to at
+  // most one partition)
+  if (!wl.token_mode &&
+      (long)S * ((long)max_seq_len + split_tokens(kv_split_tokens, page_size, false) + 16) >
+          INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
 
   AttnArgs a;
   a.q = q;
@@ -293,8 +319,11 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.max_blocks = max_blocks_per_seq;
   a.max_query_len = max_query_len;
   a.max_seq_len = max_seq_len;
-  a.part_tokens = split_tokens(kv_split_tokens, page_size);
+  a.part_tokens = split_tokens(kv_split_tokens, page_size, wl.token_mode);
+  a.part_min = split_min(page_size);
+  a.part_max = split_max(page_size);
   a.max_parts = wl.max_parts;
+  a.dec_grid = wl.token_mode ? 0 : decode_grid(dtype, head_dim, G);
   a.scale_log2e = scale * kLog2e;
 
   hipStream_t s = (hipStream_t)stream;

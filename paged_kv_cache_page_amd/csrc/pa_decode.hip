@@ -4,25 +4,33 @@
 // used by all G query heads of its group (grouped-query attention: Helios blog,
 // "torch.sdpa and Flash Attention"), about 2*G flops per byte. The kernel is
 // written for that bound: VALU dot products (no matrix cores), 16-byte row
-// loads through the page table, the next step's loads in flight while the
-// current step computes, and the softmax kept online in registers.
+// loads through the page table, the next buffer's loads in flight while the
+// current one computes, and the softmax kept online in registers.
 //
-// Work decomposition. A work item is (row, split partition, KV head). For the
-// decode rows of a tick the items come from the plan list and a persistent
-// grid walks them (item index w -> KV head w % Hkv, so with a grid that is a
-// multiple of 8 each workgroup keeps one KV head, and with 8 KV heads each
-// XCD serves one head: the slices of a prefix page shared by many sequences
-// then stay in that XCD's L2). The per-token mode (prefill rows without a
-// matrix-core kernel, i.e. float32) uses a plain grid over (token, partition,
-// KV head).
+// Work decomposition. A work item is a key range of one row for one KV head
+// and is owned by ONE wave: no LDS, no workgroup barrier, so a wave never
+// waits for its neighbours. The range's page ids sit in one VGPR (lane i holds
+// the i-th page of the range, at most 64 pages) and each buffer takes its page
+// with a lane read into a scalar register.
+//
+// For the decode rows of a tick the plan kernel lays all rows end to end on
+// one key axis and cuts it into equal chunks, one per wave (see pa_plan.hip):
+// a wave walks the rows its chunk covers, one range per row, so every wave
+// gets the same number of keys whatever the spread of lengths. Workgroup b
+// serves KV head b % Hkv (the grid is a multiple of 8, so each XCD keeps the
+// same KV heads and the slices of a prefix page shared by many sequences stay
+// in that XCD's L2); its four waves take successive chunks. The per-token
+// mode (prefill rows without a matrix-core kernel, i.e. float32) maps waves to
+// (token, fixed partition, KV head) directly.
 //
 // Inside a wave, LPK lanes hold one key row (16 or 32 bytes each), so a wave
-// covers 64 / LPK keys per step and UNROLL steps per iteration. Each lane
-// keeps its own running (max, sum, output) over the keys of its slot; slots
-// are merged with cross-lane shuffles at the end, waves through LDS.
+// covers 64 / LPK keys per step (its "slots") and UNROLL steps per buffer.
+// Each lane keeps its own running (max, sum, output) over the keys of its
+// slot; at the end the slots are merged with a register butterfly
+// (permlane16/32 swaps, DPP below 16 lanes).
 //
-// A partition's result is either final (the row has one partition) or a
-// partial (m, l, o) in the workspace, merged by K3:
+// A range's result is either final (the row has one range) or a partial
+// (m, l, o) in the workspace, merged by K3:
 //   m* = max_k m_k,  o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k.
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -31,26 +39,25 @@ namespace pa {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxPartPages = 256;
 
 template <typename ET, int D>
 struct DecodeShape {
   static constexpr int EB = ET::kBytes;
   static constexpr int ROWB = D * EB;  // bytes of one head row
-  static constexpr int LPK = ROWB >= 256 ? (ROWB / 32 > 16 ? 16 : ROWB / 32) : ROWB / 16;
+  static constexpr int LPK = ROWB / 16 > 16 ? 16 : ROWB / 16;  // lanes per key row
   static constexpr int LANE_BYTES = ROWB / LPK;  // 16 or 32
   static constexpr int LOADS = LANE_BYTES / 16;  // 16-byte loads per lane per row
   static constexpr int WORDS = LANE_BYTES / 4;   // 32-bit words per lane per row
   static constexpr int DPL = D / LPK;            // head dims held by a lane
   static constexpr int EPV = 16 / EB;            // elements per 16-byte vector
   static constexpr int KPW = 64 / LPK;           // keys per wave step (slots)
-  // steps per buffer: a buffer always covers 16 consecutive keys, so with pages
-  // of >= 16 keys (a power of two) and 16-aligned starts it never crosses a page
-  static constexpr int UNROLL = 16 / KPW;
-  static constexpr int KPI = KPW * UNROLL;       // keys per buffer (16)
+  // A buffer covers KPI consecutive keys starting at a multiple of KPI; pages
+  // hold a power of two >= 16 keys, so a buffer never crosses a page.
+  static constexpr int KPI = EB == 2 || KPW > 8 ? 16 : 8;
+  static constexpr int UNROLL = KPI / KPW;       // steps per buffer
   static_assert(LANE_BYTES == 16 || LANE_BYTES == 32, "lane row share must be 16 or 32 bytes");
-  static_assert(KPI == 16, "a buffer covers 16 keys");
-  static_assert(EB == 4 || UNROLL == 2, "bf16 P.V pairs the two steps of a buffer");
+  static_assert(UNROLL >= 1 && KPW * UNROLL == KPI, "a buffer is whole steps");
+  static_assert(EB == 4 || UNROLL % 2 == 0, "bf16 P.V pairs the steps of a buffer");
   // Head-dim index of the lane's local dim i (sub = lane % LPK).
   __device__ static int dim_of(int sub, int i) {
     return ((i / EPV) * LPK + sub) * EPV + (i % EPV);
@@ -90,38 +97,39 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
     r.token = q0;
     if (L != 1 || q0 < 0 || q0 >= a.T) return r;
   }
+  // Keys beyond the block table or beyond max_seq_len are never read (the
+  // caller promised neither happens; this keeps every index in range if not).
   int n = a.seq_lens[s];
-  const int cap = a.max_blocks * a.P;
-  n = n < cap ? n : cap;
+  n = min(n, a.max_blocks * a.P);
+  n = min(n, a.max_seq_len);
   r.seq = s;
   r.n_eff = n - L + i + 1;
   r.active = r.n_eff > 0;
   return r;
 }
 
-template <typename ET, int D, int G>
-struct DecodeSmem {
-  int pages[kMaxPartPages];
-  float o[kWaves][G][D];
-  float m[kWaves][G];
-  float l[kWaves][G];
-};
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
 
-// Issue the loads of one buffer: the 16 keys starting at `base` (wave-uniform,
-// a multiple of 16), all in one page. The page and the row of `base` are
-// wave-uniform, so the address is a scalar base plus a per-lane 32-bit offset
-// fixed for the whole item; past the end of the range the buffer re-reads the
-// range's first keys (its values are then masked).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Issue the loads of one buffer: the KPI keys starting at `kb` (wave-uniform,
+// a multiple of KPI, inside the partition). The page id comes from lane
+// `page index` of the page VGPR, so the address is a scalar base plus the
+// lane's fixed 32-bit offset. Slots past the partition end read rows of the
+// same page (in bounds; masked in compute_step).
 template <typename SH>
-__device__ __forceinline__ void load_step(uint32_t (&kr)[SH::UNROLL][SH::WORDS],
-                                          uint32_t (&vr)[SH::UNROLL][SH::WORDS],
-                                          const char* kbase, const char* vbase,
-                                          const int* pages, int pg0, int p_shift,
-                                          size_t slot_stride, int base, int kbeg, int kend,
-                                          uint32_t lane_off) {
-  const int bb = base < kend ? base : kbeg;
-  const int page = __builtin_amdgcn_readfirstlane(pages[(bb >> p_shift) - pg0]);
-  const int row0 = bb & ((1 << p_shift) - 1);
+__device__ __forceinline__ void load_buf(uint32_t (&kr)[SH::UNROLL][SH::WORDS],
+                                         uint32_t (&vr)[SH::UNROLL][SH::WORDS],
+                                         const char* kbase, const char* vbase, int page_reg,
+                                         int pg0, int p_shift, size_t slot_stride, int kb,
+                                         uint32_t lane_off) {
+  const int page = __builtin_amdgcn_readlane(page_reg, (kb >> p_shift) - pg0);
+  const int row0 = kb & ((1 << p_shift) - 1);
   const size_t step_off = (((size_t)page << p_shift) + row0) * slot_stride;
 #pragma unroll
   for (int u = 0; u < SH::UNROLL; ++u) {
@@ -141,30 +149,21 @@ __device__ __forceinline__ void load_step(uint32_t (&kr)[SH::UNROLL][SH::WORDS],
   }
 }
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// Scores, online softmax and P.V for one buffer (16 keys of the wave).
+// Scores, online softmax and P.V for one buffer (KPI keys of the wave).
 template <typename SH, int G>
-__device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH::WORDS],
-                                             uint32_t (&vr)[SH::UNROLL][SH::WORDS],
-                                             const uint32_t (&qw)[G][SH::WORDS], float (&m)[G],
-                                             float (&lsum)[G], float (&o)[G][SH::DPL], int base,
-                                             int kend, int slot, float sl2e) {
+__device__ __forceinline__ void compute_buf(const uint32_t (&kr)[SH::UNROLL][SH::WORDS],
+                                            uint32_t (&vr)[SH::UNROLL][SH::WORDS],
+                                            const uint32_t (&qw)[G][SH::WORDS], float (&m)[G],
+                                            float (&lsum)[G], float (&o)[G][SH::DPL], int kb,
+                                            int kend, int slot, float sl2e) {
   constexpr int UNROLL = SH::UNROLL, WORDS = SH::WORDS, DPL = SH::DPL;
   bool valid[UNROLL];
 #pragma unroll
-  for (int u = 0; u < UNROLL; ++u) valid[u] = base + u * SH::KPW + slot < kend;
+  for (int u = 0; u < UNROLL; ++u) valid[u] = kb + u * SH::KPW + slot < kend;
   // Rows past the end may hold anything (NaN included); zero their V so that
-  // a zero weight times them stays zero. Only the last buffer of a range is
-  // partial, and the test is wave-uniform.
-  if (base + SH::KPI > kend) {
+  // a zero weight times them stays zero. Only the last buffer of a partition
+  // is partial, and the test is wave-uniform.
+  if (kb + SH::KPI > kend) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
@@ -188,15 +187,18 @@ __device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH
       sc[u][g] = valid[u] ? acc * sl2e : -INFINITY;
     }
   }
-  // bf16: the two steps' V rows interleaved per dim, (v_u0[d], v_u1[d]), so
-  // that one v_dot2 adds both keys' contributions to one output dim.
-  uint32_t vlo[SH::EB == 2 ? WORDS : 1], vhi[SH::EB == 2 ? WORDS : 1];
+  // bf16: V rows of steps (2j, 2j+1) interleaved per dim, (v_2j[d], v_2j+1[d]),
+  // so that one v_dot2 adds both keys' contributions to one output dim.
+  constexpr int NPAIR = SH::EB == 2 ? UNROLL / 2 : 1;
+  uint32_t vlo[NPAIR][WORDS], vhi[NPAIR][WORDS];
   if constexpr (SH::EB == 2) {
 #pragma unroll
-    for (int w = 0; w < WORDS; ++w) {
-      vlo[w] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u);
-      vhi[w] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u);
-    }
+    for (int j = 0; j < NPAIR; ++j)
+#pragma unroll
+      for (int w = 0; w < WORDS; ++w) {
+        vlo[j][w] = __builtin_amdgcn_perm(vr[2 * j + 1][w], vr[2 * j][w], 0x05040100u);
+        vhi[j][w] = __builtin_amdgcn_perm(vr[2 * j + 1][w], vr[2 * j][w], 0x07060302u);
+      }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -213,14 +215,17 @@ __device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH
       for (int i = 0; i < DPL; ++i) o[g][i] *= corr;
     }
     if constexpr (SH::EB == 2) {
-      // weights rounded to bf16 once; the sum uses the same rounded values
-      const f32x2_t pf = {fast_exp2(sc[0][g] - m[g]), fast_exp2(sc[1][g] - m[g])};
-      const uint32_t pp = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2e_t));
-      lsum[g] += bf16_lo(pp) + bf16_hi(pp);
 #pragma unroll
-      for (int w = 0; w < WORDS; ++w) {
-        o[g][2 * w] = dot2_bf16(pp, vlo[w], o[g][2 * w]);
-        o[g][2 * w + 1] = dot2_bf16(pp, vhi[w], o[g][2 * w + 1]);
+      for (int j = 0; j < NPAIR; ++j) {
+        // weights rounded to bf16 once; the sum uses the same rounded values
+        const f32x2_t pf = {fast_exp2(sc[2 * j][g] - m[g]), fast_exp2(sc[2 * j + 1][g] - m[g])};
+        const uint32_t pp = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2e_t));
+        lsum[g] += bf16_lo(pp) + bf16_hi(pp);
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w) {
+          o[g][2 * w] = dot2_bf16(pp, vlo[j][w], o[g][2 * w]);
+          o[g][2 * w + 1] = dot2_bf16(pp, vhi[j][w], o[g][2 * w + 1]);
+        }
       }
     } else {
 #pragma unroll
@@ -234,36 +239,80 @@ __device__ __forceinline__ void compute_step(const uint32_t (&kr)[SH::UNROLL][SH
   }
 }
 
-// One work item: keys [part * PT, min(n_eff, (part + 1) * PT)) of one row, one KV head.
+// The two values of x held by this lane and by lane ^ OFF, in an order that
+// is the same on both lanes (lower lane's value first), so that a symmetric
+// combination of them gives identical bits on both.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+  if constexpr (OFF == 16 || OFF == 32) {
+    // permlane swaps return (even block's value, odd block's value) on both lanes
+    auto r = OFF == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                          false, false)
+                       : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                          false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    float other;
+    if constexpr (OFF == 8)
+      other = dpp_f<0x128>(x);  // row_ror:8 within a 16-lane row = lane ^ 8
+    else
+      other = __shfl_xor(x, OFF);
+    const bool upper = (threadIdx.x & OFF) != 0;
+    lo = upper ? other : x;
+    hi = upper ? x : other;
+  }
+}
+
+// Merge the running (m, l, o) of the slots that differ in lane bit OFF.
+template <typename SH, int G, int OFF>
+__device__ __forceinline__ void merge_slots(float (&m)[G], float (&lsum)[G],
+                                            float (&o)[G][SH::DPL]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m0, m1, l0, l1;
+    lane_pair<OFF>(m[g], m0, m1);
+    lane_pair<OFF>(lsum[g], l0, l1);
+    const float mn = fmaxf(m0, m1);
+    const float c0 = fast_exp2(m0 - mn);
+    const float c1 = fast_exp2(m1 - mn);
+    m[g] = mn;
+    lsum[g] = l0 * c0 + l1 * c1;
+#pragma unroll
+    for (int i = 0; i < SH::DPL; ++i) {
+      float o0, o1;
+      lane_pair<OFF>(o[g][i], o0, o1);
+      o[g][i] = o0 * c0 + o1 * c1;
+    }
+  }
+}
+
+// One work item, run by one wave: keys [kbeg, kend) (kbeg a multiple of 16,
+// kend > kbeg) of sequence `seq` for query row `token`, one KV head. Range
+// `part` of the row's `nparts`; partials go to workspace row `wrow`.
 template <typename ET, int D, int G, bool TOKEN_MODE>
-__device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D, G>& sm, int row,
-                                            int part, int kvh) {
+__device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int token, int wrow,
+                                               int kbeg, int kend, int part, int nparts,
+                                               int kvh) {
   typedef DecodeShape<ET, D> SH;
   constexpr int LPK = SH::LPK, WORDS = SH::WORDS, LOADS = SH::LOADS, DPL = SH::DPL;
-  constexpr int KPI = SH::KPI;
-
-  const RowInfo ri = row_info<TOKEN_MODE>(a, row);
-  if (!ri.active) return;
-  const int PT = a.part_tokens;
-  const int kbeg = part * PT;
-  if (kbeg >= ri.n_eff) return;
-  const int kend = min(ri.n_eff, kbeg + PT);
-  const int nparts = (ri.n_eff + PT - 1) / PT;
-
-  const int pg0 = kbeg >> a.p_shift;
-  const int npg = ((kend - 1) >> a.p_shift) - pg0 + 1;
-  const int* bt_row = a.block_tables + (size_t)ri.seq * a.max_blocks;
-  for (int i = threadIdx.x; i < npg; i += kThreads)
-    sm.pages[i] = clampi(bt_row[pg0 + i], 0, a.num_pages - 1);
+  constexpr int KPI = SH::KPI, NSLOT = SH::KPW;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int sub = lane % LPK;
   const int slot = lane / LPK;
+  const int p_shift = a.p_shift;
+
+  // Page ids of the partition: lane i holds page pg0 + i (a partition spans
+  // at most 64 pages: PT <= 63 * P).
+  const int pg0 = kbeg >> p_shift;
+  const int npg = ((kend - 1) >> p_shift) - pg0 + 1;
+  const int* bt_row = a.block_tables + (size_t)seq * a.max_blocks;
+  const int page_reg = lane < npg ? clampi(bt_row[pg0 + lane], 0, a.num_pages - 1) : 0;
 
   // The group's query rows, in the lane's dims.
   const size_t row_bytes = (size_t)D * SH::EB;
-  const char* qrow = (const char*)a.q + ((size_t)ri.token * a.Hq + (size_t)kvh * G) * row_bytes;
+  const char* qrow = (const char*)a.q + ((size_t)token * a.Hq + (size_t)kvh * G) * row_bytes;
   uint32_t qw[G][WORDS];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -282,100 +331,85 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D,
 #pragma unroll
     for (int i = 0; i < DPL; ++i) o[g][i] = 0.f;
   }
-  __syncthreads();  // pages ready
 
   const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes;
   const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes;
   const size_t slot_stride = (size_t)a.Hkv * row_bytes;  // bytes between consecutive slots
   const uint32_t lane_off = (uint32_t)(slot * slot_stride) + sub * 16;
   const float sl2e = a.scale_log2e;
-  const int p_shift = a.p_shift;
-  constexpr int STEP = kWaves * KPI;
 
   // Two register buffers alternate: while one computes, the other's loads are
-  // in flight. The loads are issued unconditionally, so the number of
-  // outstanding loads is the same on every path and the compiler waits only
-  // for the buffer being consumed.
+  // in flight. Every iteration issues the same loads, so the compiler waits
+  // only for the buffer being consumed; the last one or two buffers are
+  // peeled so that no load is issued past the partition.
   uint32_t kA[SH::UNROLL][WORDS], vA[SH::UNROLL][WORDS];
   uint32_t kB[SH::UNROLL][WORDS], vB[SH::UNROLL][WORDS];
-  int base = kbeg + wave * KPI;
-  const int nsteps = base < kend ? (kend - base + STEP - 1) / STEP : 0;  // wave-uniform
-  load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, p_shift, slot_stride, base, kbeg, kend,
-                lane_off);
-  for (int it = 0; it < nsteps; it += 2) {
-    load_step<SH>(kB, vB, kbase, vbase, sm.pages, pg0, p_shift, slot_stride, base + STEP, kbeg,
-                  kend, lane_off);
+  const int nbuf = (kend - kbeg + KPI - 1) / KPI;  // >= 1, wave-uniform
+  int kb = kbeg;
+  load_buf<SH>(kA, vA, kbase, vbase, page_reg, pg0, p_shift, slot_stride, kb, lane_off);
+  int j = 0;
+  for (; j + 2 < nbuf; j += 2) {
+    load_buf<SH>(kB, vB, kbase, vbase, page_reg, pg0, p_shift, slot_stride, kb + KPI, lane_off);
     __builtin_amdgcn_sched_barrier(0);  // keep the next buffer's loads ahead of this compute
-    compute_step<SH, G>(kA, vA, qw, m, lsum, o, base, kend, slot, sl2e);
-    base += STEP;
-    load_step<SH>(kA, vA, kbase, vbase, sm.pages, pg0, p_shift, slot_stride, base + STEP, kbeg,
-                  kend, lane_off);
+    compute_buf<SH, G>(kA, vA, qw, m, lsum, o, kb, kend, slot, sl2e);
+    load_buf<SH>(kA, vA, kbase, vbase, page_reg, pg0, p_shift, slot_stride, kb + 2 * KPI,
+                 lane_off);
     __builtin_amdgcn_sched_barrier(0);
-    if (it + 1 < nsteps) compute_step<SH, G>(kB, vB, qw, m, lsum, o, base, kend, slot, sl2e);
-    base += STEP;
+    compute_buf<SH, G>(kB, vB, qw, m, lsum, o, kb + KPI, kend, slot, sl2e);
+    kb += 2 * KPI;
+  }
+  if (j + 1 < nbuf) {
+    load_buf<SH>(kB, vB, kbase, vbase, page_reg, pg0, p_shift, slot_stride, kb + KPI, lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_buf<SH, G>(kA, vA, qw, m, lsum, o, kb, kend, slot, sl2e);
+    compute_buf<SH, G>(kB, vB, qw, m, lsum, o, kb + KPI, kend, slot, sl2e);
+  } else {
+    compute_buf<SH, G>(kA, vA, qw, m, lsum, o, kb, kend, slot, sl2e);
   }
 
-  // Merge the slots of this wave (lanes sub, sub + LPK, ...).
-#pragma unroll
-  for (int off = LPK; off < 64; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m2 = __shfl_xor(m[g], off);
-      const float l2 = __shfl_xor(lsum[g], off);
-      const float mn = fmaxf(m[g], m2);
-      const float ca = fast_exp2(m[g] - mn);
-      const float cb = fast_exp2(m2 - mn);
-      m[g] = mn;
-      lsum[g] = lsum[g] * ca + l2 * cb;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const float o2 = __shfl_xor(o[g][i], off);
-        o[g][i] = o[g][i] * ca + o2 * cb;
-      }
-    }
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) sm.o[wave][g][SH::dim_of(sub, i)] = o[g][i];
-      if (sub == 0) {
-        sm.m[wave][g] = m[g];
-        sm.l[wave][g] = lsum[g];
-      }
-    }
-  }
-  __syncthreads();
+  // Merge the slots (lanes sub, sub + LPK, ...): after the butterfly every
+  // slot holds the merged state.
+  if constexpr (LPK <= 4) merge_slots<SH, G, 4>(m, lsum, o);
+  if constexpr (LPK <= 8) merge_slots<SH, G, 8>(m, lsum, o);
+  if constexpr (LPK <= 16) merge_slots<SH, G, 16>(m, lsum, o);
+  merge_slots<SH, G, 32>(m, lsum, o);
+  static_assert(LPK >= 4, "at most 16 slots");
 
-  // Merge the waves; write the final row or this partition's partial.
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D;
-    const int e = idx % D;
-    float mn = sm.m[0][g];
+  // Slot s writes the heads g with g % NSLOT == s.
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mn = fmaxf(mn, sm.m[w][g]);
-    float lt = 0.f, ot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float c = fast_exp2(sm.m[w][g] - mn);
-      lt = fmaf(sm.l[w][g], c, lt);
-      ot = fmaf(sm.o[w][g][e], c, ot);
-    }
+  for (int g = 0; g < G; ++g) {
+    if (g % NSLOT != slot) continue;
     const int h = kvh * G + g;
     if (nparts == 1) {
-      const float val = ot / lt;
-      const size_t oi = ((size_t)ri.token * a.Hq + h) * D + e;
-      if constexpr (SH::EB == 2)
-        reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16(val);
-      else
-        reinterpret_cast<float*>(a.out)[oi] = val;
+      const float inv = 1.f / lsum[g];
+      char* orow = (char*)a.out + ((size_t)token * a.Hq + h) * row_bytes;
+      if constexpr (SH::EB == 2) {
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            wv[w] = pack_bf16x2(o[g][8 * l + 2 * w] * inv, o[g][8 * l + 2 * w + 1] * inv);
+          *reinterpret_cast<uint4*>(orow + (l * LPK + sub) * 16) =
+              make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+      } else {
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l)
+          *reinterpret_cast<float4*>(orow + (l * LPK + sub) * 16) =
+              make_float4(o[g][4 * l] * inv, o[g][4 * l + 1] * inv, o[g][4 * l + 2] * inv,
+                          o[g][4 * l + 3] * inv);
+      }
     } else {
-      const size_t pi = ((size_t)row * a.max_parts + part) * a.Hq + h;
-      a.ws[pi * D + e] = ot;
-      if (e == 0) {
+      const size_t pi = ((size_t)wrow * a.max_parts + part) * a.Hq + h;
+      float* po = a.ws + pi * D;
+#pragma unroll
+      for (int i = 0; i < DPL; i += 4)
+        *reinterpret_cast<float4*>(po + SH::dim_of(sub, i)) =
+            make_float4(o[g][i], o[g][i + 1], o[g][i + 2], o[g][i + 3]);
+      if (sub == 0) {
         float* ml = a.ws + (size_t)(TOKEN_MODE ? a.T : a.S) * a.max_parts * a.Hq * D;
-        ml[2 * pi] = mn;
-        ml[2 * pi + 1] = lt;
+        *reinterpret_cast<float2*>(ml + 2 * pi) = make_float2(m[g], lsum[g]);
       }
     }
   }
@@ -383,63 +417,112 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, DecodeSmem<ET, D,
 
 template <typename ET, int D, int G, bool TOKEN_MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
-  __shared__ DecodeSmem<ET, D, G> sm;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (TOKEN_MODE) {
-    const int bid = blockIdx.x;
-    const int kvh = bid % a.Hkv;
-    const int rest = bid / a.Hkv;
-    decode_item<ET, D, G, true>(a, sm, rest / a.max_parts, rest % a.max_parts, kvh);
+    const long unit = (long)blockIdx.x * kWaves + wave;
+    const int kvh = (int)(unit % a.Hkv);
+    const long rest = unit / a.Hkv;
+    if (rest >= (long)a.T * a.max_parts) return;
+    const int row = (int)(rest / a.max_parts), part = (int)(rest % a.max_parts);
+    const RowInfo ri = row_info<true>(a, row);
+    if (!ri.active) return;
+    const int PT = a.part_tokens;
+    const int nparts = (ri.n_eff + PT - 1) / PT;
+    if (part >= nparts) return;
+    const int kbeg = part * PT;
+    decode_segment<ET, D, G, true>(a, ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part,
+                                   nparts, kvh);
   } else {
-    const int* items = a.plan + kPlanHeaderInts;
-    const int total = a.plan[0] * a.Hkv;
-    for (int w = blockIdx.x; w < total; w += gridDim.x) {
-      const int it = w / a.Hkv;
-      decode_item<ET, D, G, false>(a, sm, items[2 * it], items[2 * it + 1], w % a.Hkv);
-      __syncthreads();  // LDS is reused by the next item
+    const PlanOffsets po = plan_offsets(a.S, a.cap_dec, a.cap_pf);
+    const int4* rows = reinterpret_cast<const int4*>(a.plan + po.rows);
+    const int* first_row = a.plan + po.first_row;
+    const int n_rows = a.plan[0], C = a.plan[2], n_chunks = a.plan[3], A = a.plan[4];
+    const int kvh = blockIdx.x % a.Hkv;
+    const int stride = (gridDim.x / a.Hkv) * kWaves;  // waves serving this KV head
+    for (int chunk = (blockIdx.x / a.Hkv) * kWaves + wave; chunk < n_chunks; chunk += stride) {
+      const int c0 = chunk * C, c1 = c0 + C;
+      for (int i = first_row[chunk];; ++i) {
+        const int4 r = rows[i];  // (sequence, offset, keys, token)
+        const int off = r.y, n = r.z;
+        const int pad = (n + A - 1) / A * A;
+        const int kbeg = max(c0, off) - off;
+        const int kend = min(min(c1, off + pad) - off, n);
+        const int j0 = off / C;
+        const int nparts = (off + pad - 1) / C - j0 + 1;
+        if (kbeg < kend)
+          decode_segment<ET, D, G, false>(a, r.x, r.w, r.x, kbeg, kend, chunk - j0, nparts, kvh);
+        if (off + pad >= c1 || i + 1 >= n_rows) break;
+      }
     }
   }
 }
 
+// K3: one thread per (row, query head, 4 consecutive dims).
 template <typename ET, bool TOKEN_MODE>
-__global__ __launch_bounds__(kThreads) void split_reduce_kernel(AttnArgs a, int G) {
-  const int kvh = blockIdx.x % a.Hkv;
-  const int row = blockIdx.x / a.Hkv;
-  const RowInfo ri = row_info<TOKEN_MODE>(a, row);
-  if (!ri.active) return;
-  const int PT = a.part_tokens;
-  int nparts = (ri.n_eff + PT - 1) / PT;
-  if (nparts <= 1) return;
-  nparts = nparts < a.max_parts ? nparts : a.max_parts;
+__global__ __launch_bounds__(256) void split_reduce_kernel(AttnArgs a) {
   const int D = a.D;
-  const float* ml = a.ws + (size_t)(TOKEN_MODE ? a.T : a.S) * a.max_parts * a.Hq * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D;
-    const int e = idx % D;
-    const int h = kvh * G + g;
-    const size_t p0 = (size_t)row * a.max_parts * a.Hq + h;  // partial index of part 0
-    float mn = kNegBig;
-    for (int k = 0; k < nparts; ++k) mn = fmaxf(mn, ml[2 * (p0 + (size_t)k * a.Hq)]);
-    float lt = 0.f, ot = 0.f;
-    for (int k = 0; k < nparts; ++k) {
-      const size_t pi = p0 + (size_t)k * a.Hq;
-      const float c = fast_exp2(ml[2 * pi] - mn);
-      lt = fmaf(ml[2 * pi + 1], c, lt);
-      ot = fmaf(a.ws[pi * D + e], c, ot);
-    }
-    const float val = ot / lt;
-    const size_t oi = ((size_t)ri.token * a.Hq + h) * D + e;
-    if constexpr (ET::kBytes == 2)
-      reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16(val);
-    else
-      reinterpret_cast<float*>(a.out)[oi] = val;
+  const int quads = D / 4;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int d4 = (int)(idx % quads);
+  const long rh = idx / quads;
+  const int h = (int)(rh % a.Hq);
+  const long row = rh / a.Hq;
+  if (row >= (TOKEN_MODE ? a.T : a.S)) return;
+  int nparts, token;
+  if constexpr (TOKEN_MODE) {
+    const RowInfo ri = row_info<true>(a, (int)row);
+    if (!ri.active) return;
+    nparts = (ri.n_eff + a.part_tokens - 1) / a.part_tokens;
+    token = (int)row;
+  } else {
+    nparts = a.plan[plan_offsets(a.S, a.cap_dec, a.cap_pf).nparts + row];
+    if (nparts <= 1) return;
+    token = a.qsl[row];
+  }
+  if (nparts <= 1) return;
+  nparts = min(nparts, a.max_parts);
+  const long rows = TOKEN_MODE ? a.T : a.S;
+  const float* ml = a.ws + (size_t)rows * a.max_parts * a.Hq * D;
+  const size_t p0 = (size_t)row * a.max_parts * a.Hq + h;  // partial index of part 0
+  float mn = kNegBig;
+  for (int k = 0; k < nparts; ++k) mn = fmaxf(mn, ml[2 * (p0 + (size_t)k * a.Hq)]);
+  float lt = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = 0; k < nparts; ++k) {
+    const size_t pi = p0 + (size_t)k * a.Hq;
+    const float2 mlk = *reinterpret_cast<const float2*>(ml + 2 * pi);
+    const float4 ok = *reinterpret_cast<const float4*>(a.ws + pi * D + 4 * d4);
+    const float c = fast_exp2(mlk.x - mn);
+    lt = fmaf(mlk.y, c, lt);
+    acc.x = fmaf(ok.x, c, acc.x);
+    acc.y = fmaf(ok.y, c, acc.y);
+    acc.z = fmaf(ok.z, c, acc.z);
+    acc.w = fmaf(ok.w, c, acc.w);
+  }
+  const float inv = 1.f / lt;
+  const size_t oi = ((size_t)token * a.Hq + h) * D + 4 * d4;
+  if constexpr (ET::kBytes == 2) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
 // ------------------------------------------------------------ dispatch -----
 template <typename ET, int D, int G>
+static int decode_grid_t() {
+  const int resident = persistent_grid((const void*)decode_kernel<ET, D, G, false>, kThreads);
+  return resident > 8 ? resident - resident % 8 : 8;
+}
+
+template <typename ET, int D, int G>
 static hipError_t launch_decode_t(const AttnArgs& a, bool token_mode, hipStream_t s) {
   if (token_mode) {
-    const long blocks = (long)a.T * a.max_parts * a.Hkv;
+    const long units = (long)a.T * a.max_parts * a.Hkv;
+    const long blocks = (units + kWaves - 1) / kWaves;
     if (blocks == 0) return hipSuccess;
     profile_before("decode_attention_tokens", s);
     hipLaunchKernelGGL((decode_kernel<ET, D, G, true>), dim3((unsigned)blocks), dim3(kThreads),
@@ -447,17 +530,25 @@ static hipError_t launch_decode_t(const AttnArgs& a, bool token_mode, hipStream_
     profile_after(s);
     return hipGetLastError();
   }
-  const long items = (long)a.cap_dec * a.Hkv;
-  if (items == 0) return hipSuccess;
-  const int resident = persistent_grid((const void*)decode_kernel<ET, D, G, false>, kThreads);
-  // a multiple of 8 (and of Hkv when Hkv divides 8) keeps each workgroup on one KV head
-  long grid = items < resident ? items : resident;
-  if (grid > 8) grid -= grid % 8;
+  if (a.cap_dec == 0) return hipSuccess;
+  // a multiple of 8 (so of Hkv): workgroup b keeps KV head b % Hkv
+  const int grid = a.dec_grid;
   profile_before("decode_attention", s);
   hipLaunchKernelGGL((decode_kernel<ET, D, G, false>), dim3((unsigned)grid), dim3(kThreads), 0,
                      s, a);
   profile_after(s);
   return hipGetLastError();
+}
+
+template <typename ET, int D>
+static int decode_grid_d(int G) {
+  switch (G) {
+    case 1: return decode_grid_t<ET, D, 1>();
+    case 2: return decode_grid_t<ET, D, 2>();
+    case 4: return decode_grid_t<ET, D, 4>();
+    case 8: return decode_grid_t<ET, D, 8>();
+  }
+  return 8;
 }
 
 template <typename ET, int D>
@@ -476,6 +567,22 @@ bool decode_supported(pa_dtype_t dt, int D, int G) {
   if (dt == PA_F32) return g_ok && (D == 16 || D == 64 || D == 128);
   if (dt == PA_BF16) return g_ok && (D == 64 || D == 128);
   return false;
+}
+
+int decode_grid(pa_dtype_t dt, int D, int G) {
+  if (dt == PA_F32) {
+    switch (D) {
+      case 16: return decode_grid_d<F32, 16>(G);
+      case 64: return decode_grid_d<F32, 64>(G);
+      case 128: return decode_grid_d<F32, 128>(G);
+    }
+  } else {
+    switch (D) {
+      case 64: return decode_grid_d<BF16, 64>(G);
+      case 128: return decode_grid_d<BF16, 128>(G);
+    }
+  }
+  return 8;
 }
 
 hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipStream_t s) {
@@ -498,24 +605,20 @@ hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipS
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s) {
   const long rows = token_mode ? a.T : a.S;
-  const long blocks = rows * a.Hkv;
-  if (blocks == 0 || a.max_parts <= 1) return hipSuccess;
-  const int G = a.Hq / a.Hkv;
+  const long threads = rows * a.Hq * (a.D / 4);
+  if (threads == 0 || a.max_parts <= 1) return hipSuccess;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
   profile_before(token_mode ? "split_reduce_tokens" : "split_reduce", s);
   if (dt == PA_BF16) {
     if (token_mode)
-      hipLaunchKernelGGL((split_reduce_kernel<BF16, true>), dim3((unsigned)blocks),
-                         dim3(kThreads), 0, s, a, G);
+      hipLaunchKernelGGL((split_reduce_kernel<BF16, true>), dim3(blocks), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((split_reduce_kernel<BF16, false>), dim3((unsigned)blocks),
-                         dim3(kThreads), 0, s, a, G);
+      hipLaunchKernelGGL((split_reduce_kernel<BF16, false>), dim3(blocks), dim3(256), 0, s, a);
   } else {
     if (token_mode)
-      hipLaunchKernelGGL((split_reduce_kernel<F32, true>), dim3((unsigned)blocks),
-                         dim3(kThreads), 0, s, a, G);
+      hipLaunchKernelGGL((split_reduce_kernel<F32, true>), dim3(blocks), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((split_reduce_kernel<F32, false>), dim3((unsigned)blocks),
-                         dim3(kThreads), 0, s, a, G);
+      hipLaunchKernelGGL((split_reduce_kernel<F32, false>), dim3(blocks), dim3(256), 0, s, a);
   }
   profile_after(s);
   return hipGetLastError();

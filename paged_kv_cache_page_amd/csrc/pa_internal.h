@@ -21,18 +21,38 @@ struct AttnArgs {
   void* out;
   float* ws;           // split-KV partials: o [rows*max_parts*Hq*D], then (m, l) pairs
   int* plan;           // work lists written by the plan kernel (see pa_plan.hip)
-  int32_t cap_dec, cap_pf;  // capacities of the two lists
+  int32_t cap_dec, cap_pf;  // capacities of the decode chunk and prefill item lists
   int32_t S, T, Hq, Hkv, D, P, num_pages, max_blocks;
   int32_t p_shift;      // log2(P); P is a power of two
   int32_t max_query_len, max_seq_len;
-  int32_t part_tokens;  // keys per split-KV partition
-  int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / part_tokens))
+  int32_t part_tokens;  // keys per split-KV partition (at most); 0 = chosen by the plan kernel
+  int32_t part_min, part_max;  // bounds of a chosen partition size (multiples of 16)
+  int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / smallest size))
+  int32_t dec_grid;     // workgroups of the decode kernel (a multiple of 8)
   float scale_log2e;    // scale * log2(e): weights are exp2(s * scale_log2e - m)
 };
 
-// Plan layout: header [decode item count, prefill item count, 0, 0], then
-// cap_dec (sequence, partition) pairs, then cap_pf (sequence, row tile) pairs.
-constexpr int kPlanHeaderInts = 4;
+// Plan layout, in ints from the start of the workspace:
+//   header [kPlanHeaderInts]: [0] decode rows R, [1] prefill items,
+//     [2] chunk keys C, [3] chunks, [4] row alignment A, [5..7] unused
+//   decode rows: S x (sequence, key offset, keys, token); row i's keys occupy
+//     [offset, offset + round_up(keys, A)) of the concatenated key axis
+//   partitions per sequence: S ints (0 = no decode row)
+//   first decode row of each chunk: cap_dec ints
+//   prefill items: cap_pf x (sequence, row tile)
+constexpr int kPlanHeaderInts = 8;
+struct PlanOffsets {
+  size_t rows, nparts, first_row, pf, total;
+};
+__host__ __device__ inline PlanOffsets plan_offsets(long S, long cap_dec, long cap_pf) {
+  PlanOffsets o;
+  o.rows = kPlanHeaderInts;
+  o.nparts = o.rows + 4 * (size_t)S;
+  o.first_row = o.nparts + (size_t)S;
+  o.pf = o.first_row + (size_t)cap_dec;
+  o.total = o.pf + 2 * (size_t)cap_pf;
+  return o;
+}
 // Query rows per prefill workgroup; a tile holds kPrefillRows / G tokens.
 constexpr int kPrefillRows = 64;
 
@@ -63,6 +83,8 @@ hipError_t launch_plan(const AttnArgs& a, int* plan, int cap_dec, int cap_pf, in
 // (query length 1; other sequences skipped). token_mode = true: one row per
 // query token of every sequence (the VALU path for prefill rows).
 bool decode_supported(pa_dtype_t dt, int D, int G);
+// Workgroups of the persistent decode grid (resident count, a multiple of 8).
+int decode_grid(pa_dtype_t dt, int D, int G);
 hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipStream_t s);
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s);

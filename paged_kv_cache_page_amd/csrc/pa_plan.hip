@@ -5,8 +5,14 @@
 // every (sequence, tile) pair and letting most workgroups exit, one small
 // workgroup reads query_start_loc and seq_lens once and writes two compact
 // lists into the workspace:
-//   decode items  (sequence, split partition) for every row with query length 1;
-//   prefill items (sequence, 128-row tile) for every sequence with query length > 1,
+//   decode rows   every row with query length 1, laid end to end on one key
+//                 axis (each row padded to a multiple of A keys), cut into
+//                 equal chunks of C keys, one per decode wave: every wave gets
+//                 the same work however the lengths are spread (split-KV for
+//                 long rows, several short rows per chunk); with a fixed
+//                 partition size A = C = that size, so a chunk never spans
+//                 two rows and a row's partitions depend on the row alone;
+//   prefill items (sequence, row tile) for every sequence with query length > 1,
 //                 ordered by decreasing number of key tiles, so that the longest
 //                 tiles start first (longest-processing-time-first scheduling).
 // The persistent attention kernels then walk these lists.
@@ -19,6 +25,7 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kCostBins = 2048;
+constexpr int kCachedSeqs = 4096;  // sequence shapes kept in LDS between the passes
 
 // Exclusive scan of one int per thread over the workgroup; returns the
 // thread's offset and writes the total to *total (uniform).
@@ -39,16 +46,17 @@ __device__ int block_exclusive_scan(int v, int* s_buf, int* total) {
 }
 
 struct SeqShape {
-  int L, n;
+  int L, n, q0;
 };
 
 __device__ __forceinline__ SeqShape seq_shape(const AttnArgs& a, int s) {
   SeqShape r;
   const int q0 = a.qsl[s];
+  r.q0 = q0;
   r.L = a.qsl[s + 1] - q0;
   int n = a.seq_lens[s];
-  const int cap = a.max_blocks * a.P;
-  r.n = n < cap ? n : cap;
+  n = min(n, a.max_blocks * a.P);
+  r.n = min(n, a.max_seq_len);  // the attention kernels clamp the same way
   if (q0 < 0 || q0 + r.L > a.T || r.L < 0) r.L = 0;  // malformed rows are skipped
   return r;
 }
@@ -63,41 +71,90 @@ __device__ __forceinline__ int tile_cost(const SeqShape& sh, int mt, int TM) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* plan, int cap_dec,
                                                             int cap_pf, int TM) {
   __shared__ int s_buf[kPlanThreads];
+  __shared__ long long s_keys[kPlanThreads];
   __shared__ int s_hist[kCostBins];
   __shared__ int s_cur[kCostBins];
+  __shared__ int s_L[kCachedSeqs], s_n[kCachedSeqs], s_q0[kCachedSeqs];
   const int tid = threadIdx.x;
-  int* dec_items = plan + kPlanHeaderInts;
-  int* pf_items = dec_items + 2 * (size_t)cap_dec;
-  const int PT = a.part_tokens;
+  const PlanOffsets po = plan_offsets(a.S, cap_dec, cap_pf);
+  int4* dec_rows = reinterpret_cast<int4*>(plan + po.rows);
+  int* nparts_of = plan + po.nparts;
+  int* first_row = plan + po.first_row;
+  int* pf_items = plan + po.pf;
+  // fixed partitions: rows padded to whole partitions; otherwise to 16 keys
+  const int A = a.part_tokens > 0 ? a.part_tokens : 16;
+  auto shape = [&](int s) {
+    return s < kCachedSeqs ? SeqShape{s_L[s], s_n[s], s_q0[s]} : seq_shape(a, s);
+  };
 
   for (int i = tid; i < kCostBins; i += kPlanThreads) s_hist[i] = 0;
+  __syncthreads();
 
-  // ---- decode items (sequence order) and the prefill cost histogram ----
-  int dec_base = 0;
+  // ---- pass 1: shapes, padded decode keys, prefill cost histogram ----
+  long long my_keys = 0;
+  for (int s = tid; s < a.S; s += kPlanThreads) {
+    const SeqShape sh = seq_shape(a, s);
+    if (s < kCachedSeqs) {
+      s_L[s] = sh.L;
+      s_n[s] = sh.n;
+      s_q0[s] = sh.q0;
+    }
+    if (sh.L == 1 && sh.n >= 1) my_keys += (sh.n + A - 1) / A * A;
+    if (sh.L > 1 && sh.n >= sh.L) {
+      const int ntiles = (sh.L + TM - 1) / TM;
+      for (int mt = 0; mt < ntiles; ++mt) atomicAdd(&s_hist[tile_cost(sh, mt, TM)], 1);
+    }
+  }
+  s_keys[tid] = my_keys;
+  __syncthreads();
+  for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) s_keys[tid] += s_keys[tid + off];
+    __syncthreads();
+  }
+  const long long total_keys = s_keys[0];  // length of the concatenated key axis
+  __syncthreads();
+
+  // ---- chunk size ----
+  int C = a.part_tokens;
+  if (C <= 0) {
+    const long long waves = (long long)(a.dec_grid / a.Hkv) * 4;  // decode waves per KV head
+    long long c = (total_keys + waves - 1) / waves;
+    c = (c + 15) / 16 * 16;
+    C = (int)(c < a.part_min ? a.part_min : (c > a.part_max ? a.part_max : c));
+  }
+  const long long chunks = (total_keys + C - 1) / C;
+
+  // ---- pass 2: decode rows, their offsets on the key axis, chunk starts ----
+  int row_base = 0, off_base = 0;
   for (int c0 = 0; c0 < a.S; c0 += kPlanThreads) {
     const int s = c0 + tid;
-    int nd = 0;
-    SeqShape sh{0, 0};
+    SeqShape sh{0, 0, 0};
+    int is_dec = 0, pad = 0;
     if (s < a.S) {
-      sh = seq_shape(a, s);
-      if (sh.L == 1 && sh.n >= 1) nd = min((sh.n + PT - 1) / PT, a.max_parts);
-      if (sh.L > 1 && sh.n >= sh.L) {
-        const int ntiles = (sh.L + TM - 1) / TM;
-        for (int mt = 0; mt < ntiles; ++mt) atomicAdd(&s_hist[tile_cost(sh, mt, TM)], 1);
+      sh = shape(s);
+      if (sh.L == 1 && sh.n >= 1) {
+        is_dec = 1;
+        pad = (sh.n + A - 1) / A * A;
       }
     }
-    int total;
-    const int off = block_exclusive_scan(nd, s_buf, &total);
-    for (int p = 0; p < nd; ++p) {
-      const int idx = dec_base + off + p;
-      if (idx < cap_dec) {
-        dec_items[2 * idx] = s;
-        dec_items[2 * idx + 1] = p;
+    int nrows, npad;
+    const int ri = row_base + block_exclusive_scan(is_dec, s_buf, &nrows);
+    const int off = off_base + block_exclusive_scan(pad, s_buf, &npad);
+    if (s < a.S) {
+      int np = 0;
+      if (is_dec) {
+        const int j0 = off / C, j1 = (off + pad - 1) / C;
+        np = j1 - j0 + 1;
+        dec_rows[ri] = make_int4(s, off, sh.n, sh.q0);
+        // chunks whose first key falls in this row start here
+        for (int j = (off + C - 1) / C; j <= j1; ++j)
+          if (j < cap_dec) first_row[j] = ri;
       }
+      nparts_of[s] = np;
     }
-    dec_base += total;
+    row_base += nrows;
+    off_base += npad;
   }
-  __syncthreads();
 
   // ---- bin offsets in decreasing cost: bin b starts after all bins > b ----
   int pf_total = 0;
@@ -113,29 +170,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   }
   __syncthreads();
 
-  // ---- scatter prefill items into their bins ----
-  for (int c0 = 0; c0 < a.S; c0 += kPlanThreads) {
-    const int s = c0 + tid;
-    if (s < a.S) {
-      const SeqShape sh = seq_shape(a, s);
-      if (sh.L > 1 && sh.n >= sh.L) {
-        const int ntiles = (sh.L + TM - 1) / TM;
-        for (int mt = ntiles - 1; mt >= 0; --mt) {
-          const int idx = atomicAdd(&s_cur[tile_cost(sh, mt, TM)], 1);
-          if (idx < cap_pf) {
-            pf_items[2 * idx] = s;
-            pf_items[2 * idx + 1] = mt;
-          }
+  // ---- pass 3: scatter prefill items into their bins ----
+  for (int s = tid; s < a.S; s += kPlanThreads) {
+    const SeqShape sh = shape(s);
+    if (sh.L > 1 && sh.n >= sh.L) {
+      const int ntiles = (sh.L + TM - 1) / TM;
+      for (int mt = ntiles - 1; mt >= 0; --mt) {
+        const int idx = atomicAdd(&s_cur[tile_cost(sh, mt, TM)], 1);
+        if (idx < cap_pf) {
+          pf_items[2 * idx] = s;
+          pf_items[2 * idx + 1] = mt;
         }
       }
     }
   }
-  __syncthreads();
   if (tid == 0) {
-    plan[0] = min(dec_base, cap_dec);
+    plan[0] = row_base;
     plan[1] = min(pf_total, cap_pf);
-    plan[2] = 0;
-    plan[3] = 0;
+    plan[2] = C;
+    plan[3] = (int)(chunks < cap_dec ? chunks : cap_dec);
+    plan[4] = A;
+    plan[5] = plan[6] = plan[7] = 0;
   }
 }
 

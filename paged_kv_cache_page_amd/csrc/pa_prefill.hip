@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int p_shift = a.p_shift;
   const int rmask = (1 << p_shift) - 1;
   const size_t page_bytes = slot_stride << p_shift;
-  const int* items = a.plan + kPlanHeaderInts + 2 * (size_t)a.cap_dec;
+  const int* items = a.plan + plan_offsets(a.S, a.cap_dec, a.cap_pf).pf;
   const int total = a.plan[1] * a.Hkv;
   const int nwg = gridDim.x;
 

@@ -104,25 +104,32 @@ def test_attention_empty_tick_is_ok_without_touching_memory():
     assert attn(S=0, T=0) == OK
 
 
-def _plan_bytes(cap_dec, cap_pf):
-    return -(-(4 + 2 * (cap_dec + cap_pf)) * 4 // 256) * 256
+def _plan_bytes(S, cap_dec, cap_pf):
+    # header 8, decode rows 4 * S, partitions per sequence S, chunk starts cap_dec,
+    # prefill items 2 * cap_pf (ints), padded to 256 bytes
+    return -(-(8 + 5 * S + cap_dec + 2 * cap_pf) * 4 // 256) * 256
 
 
 def test_workspace_size_query():
     lib = pa.lib()
     ws = lib.pa_paged_attention_workspace_size
-    # one partition: only the plan lists (64 decode items)
-    assert ws(64, 64, 32, 128, 1, 512, 256, 0, BF16) == _plan_bytes(64, 0)
-    # 4096 keys in 512-key partitions: 8 partials of (D + 2) floats per (row, head)
+    # automatic split: decode rows share one key axis cut into chunks of at least 256
+    # keys (P = 256), so a row of n keys has at most ceil(n / 256) + 1 partials
+    assert ws(64, 64, 32, 128, 1, 256, 256, 0, BF16) == (
+        _plan_bytes(64, 64 * 2, 0) + 64 * 2 * 32 * 130 * 4)
     n = ws(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
-    assert n == _plan_bytes(64 * 8, 0) + 64 * 8 * 32 * 130 * 4
-    # an explicit split of 1024 keys halves the partials
-    assert ws(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == _plan_bytes(64 * 4, 0) + 64 * 4 * 32 * 130 * 4
+    assert n == _plan_bytes(64, 64 * 17, 0) + 64 * 17 * 32 * 130 * 4
+    # an explicit split of 1024 keys: partitions aligned to the row start, 4 partials
+    assert ws(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == (
+        _plan_bytes(64, 64 * 4, 0) + 64 * 4 * 32 * 130 * 4)
+    # a partition spans at most 64 pages: with P = 16 an explicit 4096 is capped at 63 * 16
+    assert ws(4, 4, 4, 16, 1, 4096, 16, 4096, F32) == _plan_bytes(4, 4 * 5, 0) + 4 * 5 * 4 * 18 * 4
     # prefill rows: a row tile holds at least 8 tokens (64 rows, group <= 8), so at most
     # min(S * ceil(Lmax / 8), T / 8 + S) row tiles are planned
     assert ws(51, 2096, 32, 128, 1024, 4096, 256, 0, BF16) == (
-        _plan_bytes(51 * 8, min(51 * 128, 2096 // 8 + 51)) + 51 * 8 * 32 * 130 * 4)
-    # fp32 with prefill rows takes the per-token path: one row per token, no plan
+        _plan_bytes(51, 51 * 17, min(51 * 128, 2096 // 8 + 51)) + 51 * 17 * 32 * 130 * 4)
+    # fp32 with prefill rows takes the per-token path (512-key partitions): one row per
+    # token, no plan
     assert ws(4, 40, 4, 16, 20, 1024, 16, 0, F32) == 40 * 2 * 4 * 18 * 4
     assert ws(-1, 4, 4, 16, 1, 64, 16, 0, F32) == 0
 
