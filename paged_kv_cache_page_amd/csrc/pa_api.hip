@@ -57,6 +57,22 @@ std::mutex g_grid_mu;
 std::map<std::pair<int, const void*>, int> g_grid_cache;
 }  // namespace
 
+int cu_count() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
 int persistent_grid(const void* func, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;

@@ -60,6 +60,8 @@ constexpr int kPrefillRows = 64;
 // device holds at once: compute units x resident workgroups per unit. Cached
 // per (device, kernel). Used to size persistent grids.
 int persistent_grid(const void* func, int threads);
+// Compute units of the current device (cached).
+int cu_count();
 
 // Kernel timing hook (pa_api.hip): called around every launch.
 void profile_before(const char* name, hipStream_t stream);
