@@ -27,22 +27,44 @@ constexpr int kPlanThreads = 1024;
 constexpr int kCostBins = 2048;
 constexpr int kCachedSeqs = 4096;  // sequence shapes kept in LDS between the passes
 
-// Exclusive scan of one int per thread over the workgroup; returns the
-// thread's offset and writes the total to *total (uniform).
-__device__ int block_exclusive_scan(int v, int* s_buf, int* total) {
-  const int tid = threadIdx.x;
-  s_buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int add = tid >= off ? s_buf[tid - off] : 0;
-    __syncthreads();
-    s_buf[tid] += add;
-    __syncthreads();
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Exclusive scan of one int per thread over the workgroup (a shuffle scan in
+// each wave, then the wave totals through LDS); returns the thread's offset
+// and writes the workgroup total to *total (uniform).
+__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
   }
-  const int incl = s_buf[tid];
-  *total = s_buf[kPlanThreads - 1];
+  if (lane == 63) s_wave[w] = incl;
   __syncthreads();
-  return incl - v;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) {
+    const int x = s_wave[i];
+    before += i < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();  // s_wave is free again
+  *total = all;
+  return before + incl - v;
+}
+
+// Sum of one 64-bit value per thread over the workgroup (uniform result).
+__device__ long long block_sum(long long v, long long* s_wave) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long all = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) all += s_wave[i];
+  __syncthreads();
+  return all;
 }
 
 struct SeqShape {
@@ -70,8 +92,8 @@ __device__ __forceinline__ int tile_cost(const SeqShape& sh, int mt, int TM) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* plan, int cap_dec,
                                                             int cap_pf, int TM) {
-  __shared__ int s_buf[kPlanThreads];
-  __shared__ long long s_keys[kPlanThreads];
+  __shared__ int s_buf[kPlanWaves];
+  __shared__ long long s_keys[kPlanWaves];
   __shared__ int s_hist[kCostBins];
   __shared__ int s_cur[kCostBins];
   __shared__ int s_L[kCachedSeqs], s_n[kCachedSeqs], s_q0[kCachedSeqs];
@@ -100,19 +122,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
       s_q0[s] = sh.q0;
     }
     if (sh.L == 1 && sh.n >= 1) my_keys += (sh.n + A - 1) / A * A;
+  }
+  const long long total_keys = block_sum(my_keys, s_keys);  // length of the key axis
+  // prefill tile costs: one wave per sequence, lanes over its row tiles
+  const int lane = tid & 63, wid = tid >> 6;
+  for (int s = wid; s < a.S; s += kPlanWaves) {
+    const SeqShape sh = shape(s);
     if (sh.L > 1 && sh.n >= sh.L) {
       const int ntiles = (sh.L + TM - 1) / TM;
-      for (int mt = 0; mt < ntiles; ++mt) atomicAdd(&s_hist[tile_cost(sh, mt, TM)], 1);
+      for (int mt = lane; mt < ntiles; mt += 64) atomicAdd(&s_hist[tile_cost(sh, mt, TM)], 1);
     }
   }
-  s_keys[tid] = my_keys;
-  __syncthreads();
-  for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) s_keys[tid] += s_keys[tid + off];
-    __syncthreads();
-  }
-  const long long total_keys = s_keys[0];  // length of the concatenated key axis
-  __syncthreads();
 
   // ---- chunk size ----
   int C = a.part_tokens;
@@ -170,12 +190,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   }
   __syncthreads();
 
-  // ---- pass 3: scatter prefill items into their bins ----
-  for (int s = tid; s < a.S; s += kPlanThreads) {
+  // ---- pass 3: scatter prefill items into their bins (wave per sequence) ----
+  for (int s = wid; s < a.S; s += kPlanWaves) {
     const SeqShape sh = shape(s);
     if (sh.L > 1 && sh.n >= sh.L) {
       const int ntiles = (sh.L + TM - 1) / TM;
-      for (int mt = ntiles - 1; mt >= 0; --mt) {
+      for (int mt = lane; mt < ntiles; mt += 64) {
         const int idx = atomicAdd(&s_cur[tile_cost(sh, mt, TM)], 1);
         if (idx < cap_pf) {
           pf_items[2 * idx] = s;
