@@ -348,6 +348,16 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
     e = launch_plan(a, a.plan, a.cap_dec, a.cap_pf, kPrefillRows / G, s);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
+  if (!wl.token_mode && a.cap_pf > 0 && tick_supported(dtype, head_dim)) {
+    // a tick that may hold prefill chunks: decode and prefill share one grid
+    e = launch_tick(dtype, a, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+    if (a.max_parts > 1) {
+      e = launch_split_reduce(dtype, a, false, s);
+      if (e != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
+  }
   e = launch_decode(dtype, a, wl.token_mode, s);
   if (e != hipSuccess) return PA_ERR_HIP;
   if (a.max_parts > 1) {

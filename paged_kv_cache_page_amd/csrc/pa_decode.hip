@@ -32,20 +32,12 @@
 // A range's result is either final (the row has one range) or a partial
 // (m, l, o) in the workspace, merged by K3:
 //   m* = max_k m_k,  o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k.
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_decode_mfma.h"
 
 namespace pa {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-// bf16 decode: register buffers per wave (16 keys each) and resident
-// workgroups per CU. One workgroup per CU keeps the waves of a CU the same
-// age: the wave arbiter favours older waves, and with several workgroups per
-// CU the younger ones' loads queue behind the older ones' and the kernel ends
-// on a tail of late waves. The deeper ring keeps enough bytes in flight.
-constexpr int kDecodeBufs = 2;
-constexpr int kDecodeWgPerCu = 1;
 
 template <typename ET, int D>
 struct DecodeShape {
@@ -113,15 +105,6 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
   r.n_eff = n - L + i + 1;
   r.active = r.n_eff > 0;
   return r;
-}
-
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // Issue the loads of one buffer: the KPI keys starting at `kb` (wave-uniform,
@@ -422,317 +405,6 @@ __device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int t
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 work item with the scores on matrix cores. Per 16-key buffer:
-//   S^T[key, head] = K[key, :] . Q[head, :]   v_mfma_f32_16x16x32_bf16, A = K
-//   rows loaded straight into the A layout (lane l: key l % 16, dims 8(l/16) +
-//   32 ks ..), B = Q^T (lane l: head l % 16, zero for heads >= G). Lane (r, c)
-//   (r = l / 16, c = l % 16) then holds the scores of keys 4r .. 4r + 3 for
-//   head c. One running max per head for the whole wave (combined over the
-//   four lanes of a head with permlane swaps), so the per-lane sums and output
-//   accumulators of different lanes can be added without rescaling.
-//   P.V stays on v_dot2: V row (key) slot * UNROLL + u of the buffer sits in
-//   the LPK lanes of `slot`; its weights are the (bf16-packed) scores of lane
-//   (slot * UNROLL / 4, head), broadcast along the 16-lane row with DPP
-//   row_newbcast.
-template <int D, int G>
-struct MfmaDecodeShape {
-  static constexpr int ROWB = D * 2;
-  static constexpr int KSTEPS = D / 32;      // k-steps of the score MFMA
-  static constexpr int LPK = ROWB / 16;      // lanes per V row (16 bytes each)
-  static constexpr int NSLOT = 64 / LPK;     // V rows per step
-  static constexpr int UNROLL = 16 / NSLOT;  // steps per 16-key buffer
-  static constexpr int NPAIR = UNROLL / 2;
-  static_assert(D == 64 || D == 128, "bf16 head dims 64 and 128");
-  static_assert(G >= 1 && G <= 8, "at most 8 query heads per KV head");
-};
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-
-template <int N>
-__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
-}
-
-template <int D, int G>
-struct MfmaBuf {
-  uint4 k[MfmaDecodeShape<D, G>::KSTEPS];
-  uint4 v[MfmaDecodeShape<D, G>::UNROLL];
-};
-
-// Issue the loads of the 16 keys starting at kb (as load_buf).
-template <int D, int G>
-__device__ __forceinline__ void mfma_load(MfmaBuf<D, G>& b, const char* kbase, const char* vbase,
-                                          int page_reg, int pg0, int p_shift, size_t slot_stride,
-                                          int kb, uint32_t k_off, uint32_t v_off) {
-  typedef MfmaDecodeShape<D, G> SH;
-  const int page = __builtin_amdgcn_readlane(page_reg, (kb >> p_shift) - pg0);
-  const int row0 = kb & ((1 << p_shift) - 1);
-  const size_t step_off = (((size_t)page << p_shift) + row0) * slot_stride;
-  const char* kp = kbase + step_off + k_off;
-#pragma unroll
-  for (int ks = 0; ks < SH::KSTEPS; ++ks) b.k[ks] = *reinterpret_cast<const uint4*>(kp + 64 * ks);
-  const char* vp = vbase + step_off + v_off;
-#pragma unroll
-  for (int u = 0; u < SH::UNROLL; ++u)
-    b.v[u] = *reinterpret_cast<const uint4*>(vp + (size_t)u * slot_stride);
-}
-
-__device__ __forceinline__ uint32_t word_of4(const uint4& v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-}
-
-template <int D, int G>
-__device__ __forceinline__ void mfma_compute(MfmaBuf<D, G>& b, const uint4 (&qb)[D / 32],
-                                             float& m_run, float& l_part, float (&o)[G][8],
-                                             int kb, int kend, int rrow, int slot, float sl2e,
-                                             float bias) {
-  typedef MfmaDecodeShape<D, G> SH;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < SH::KSTEPS; ++ks)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[ks]),
-                                                  __builtin_bit_cast(bf16x8_t, qb[ks]), acc, 0,
-                                                  0, 0);
-  // log2-domain scores; bias is -inf in the lanes of heads >= G
-  float s[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = fmaf(acc[i], sl2e, bias);
-  // Keys past the range end (only in the last buffer; wave-uniform test):
-  // no weight, and their V rows (which may hold anything) zeroed.
-  if (kb + 16 > kend) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = kb + 4 * rrow + i < kend ? s[i] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < SH::UNROLL; ++u) {
-      const bool ok = kb + slot * SH::UNROLL + u < kend;
-      b.v[u] = make_uint4(ok ? b.v[u].x : 0u, ok ? b.v[u].y : 0u, ok ? b.v[u].z : 0u,
-                          ok ? b.v[u].w : 0u);
-    }
-  }
-  float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  {
-    auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(mb), __float_as_uint(mb), false,
-                                              false);
-    mb = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
-    auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false,
-                                              false);
-    mb = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
-  }
-  // Rescale only when some head's running max grows (rare after the first keys).
-  if (__any(mb > m_run)) {
-    const float mn = fmaxf(m_run, mb);
-    const float corr = fast_exp2(m_run - mn);
-    m_run = mn;
-    l_part *= corr;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float ch;
-      if constexpr (true) {
-        const uint32_t cu = __float_as_uint(corr);
-        switch (h) {
-          case 0: ch = __uint_as_float(row_bcast<0>(cu)); break;
-          case 1: ch = __uint_as_float(row_bcast<1>(cu)); break;
-          case 2: ch = __uint_as_float(row_bcast<2>(cu)); break;
-          case 3: ch = __uint_as_float(row_bcast<3>(cu)); break;
-          case 4: ch = __uint_as_float(row_bcast<4>(cu)); break;
-          case 5: ch = __uint_as_float(row_bcast<5>(cu)); break;
-          case 6: ch = __uint_as_float(row_bcast<6>(cu)); break;
-          default: ch = __uint_as_float(row_bcast<7>(cu)); break;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[h][i] *= ch;
-    }
-  }
-  // weights rounded to bf16 once; the sum uses the same rounded values
-  const f32x2_t p01 = {fast_exp2(s[0] - m_run), fast_exp2(s[1] - m_run)};
-  const f32x2_t p23 = {fast_exp2(s[2] - m_run), fast_exp2(s[3] - m_run)};
-  const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2e_t));
-  const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2e_t));
-  l_part += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
-
-  // V rows of steps (2j, 2j+1) interleaved per dim for v_dot2
-  uint32_t vlo[SH::NPAIR][4], vhi[SH::NPAIR][4];
-#pragma unroll
-  for (int j = 0; j < SH::NPAIR; ++j)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      vlo[j][w] = __builtin_amdgcn_perm(word_of4(b.v[2 * j + 1], w), word_of4(b.v[2 * j], w),
-                                        0x05040100u);
-      vhi[j][w] = __builtin_amdgcn_perm(word_of4(b.v[2 * j + 1], w), word_of4(b.v[2 * j], w),
-                                        0x07060302u);
-    }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    uint32_t b01, b23;
-    switch (h) {
-      case 0: b01 = row_bcast<0>(w01); b23 = row_bcast<0>(w23); break;
-      case 1: b01 = row_bcast<1>(w01); b23 = row_bcast<1>(w23); break;
-      case 2: b01 = row_bcast<2>(w01); b23 = row_bcast<2>(w23); break;
-      case 3: b01 = row_bcast<3>(w01); b23 = row_bcast<3>(w23); break;
-      case 4: b01 = row_bcast<4>(w01); b23 = row_bcast<4>(w23); break;
-      case 5: b01 = row_bcast<5>(w01); b23 = row_bcast<5>(w23); break;
-      case 6: b01 = row_bcast<6>(w01); b23 = row_bcast<6>(w23); break;
-      default: b01 = row_bcast<7>(w01); b23 = row_bcast<7>(w23); break;
-    }
-    uint32_t pw[SH::NPAIR];
-    if constexpr (SH::UNROLL == 4) {
-      // keys 4 slot + u: elements (0,1) and (2,3) of the row's score lane
-      pw[0] = b01;
-      pw[1] = b23;
-    } else {
-      // keys 2 slot + u: elements (0,1) for even slots, (2,3) for odd ones
-      pw[0] = (slot & 1) ? b23 : b01;
-    }
-#pragma unroll
-    for (int j = 0; j < SH::NPAIR; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        o[h][2 * w] = dot2_bf16(pw[j], vlo[j][w], o[h][2 * w]);
-        o[h][2 * w + 1] = dot2_bf16(pw[j], vhi[j][w], o[h][2 * w + 1]);
-      }
-  }
-}
-
-template <int N>
-__device__ __forceinline__ float lane_sum_xor(float x) {
-  if constexpr (N == 16 || N == 32) {
-    auto r = N == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false)
-                     : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  } else {
-    static_assert(N == 8, "xor 8, 16 or 32");
-    const float other = dpp_f<0x128>(x);  // row_ror:8 = lane ^ 8
-    return (threadIdx.x & 8) ? other + x : x + other;
-  }
-}
-
-template <int D, int G, int NBUF>
-__device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, int seq, int token,
-                                                    int wrow, int kbeg, int kend, int part,
-                                                    int nparts, int kvh, bool token_mode) {
-  typedef MfmaDecodeShape<D, G> SH;
-  constexpr int LPK = SH::LPK, NSLOT = SH::NSLOT;
-  const int lane = threadIdx.x & 63;
-  const int rrow = lane >> 4, col = lane & 15;  // score layout: keys 4 rrow.., head col
-  const int slot = lane / LPK, sub = lane % LPK;  // V layout
-  const int p_shift = a.p_shift;
-
-  const int pg0 = kbeg >> p_shift;
-  const int npg = ((kend - 1) >> p_shift) - pg0 + 1;
-  const int* bt_row = a.block_tables + (size_t)seq * a.max_blocks;
-  const int page_reg = lane < npg ? clampi(bt_row[pg0 + lane], 0, a.num_pages - 1) : 0;
-
-  // Q^T operand: head col's dims 8 rrow + 32 ks ..
-  const size_t row_bytes = (size_t)SH::ROWB;
-  uint4 qb[SH::KSTEPS];
-  {
-    const char* qrow = (const char*)a.q + ((size_t)token * a.Hq + (size_t)kvh * G) * row_bytes;
-    const int hq = col < G ? col : 0;
-#pragma unroll
-    for (int ks = 0; ks < SH::KSTEPS; ++ks) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qrow + hq * row_bytes + 16 * rrow + 64 * ks);
-      qb[ks] = col < G ? x : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  const float bias = col < G ? 0.f : -INFINITY;
-
-  float m_run = kNegBig, l_part = 0.f;
-  float o[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
-
-  const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes;
-  const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes;
-  const size_t slot_stride = (size_t)a.Hkv * row_bytes;
-  const uint32_t k_off = (uint32_t)(col * slot_stride) + 16 * rrow;
-  const uint32_t v_off = (uint32_t)(slot * SH::UNROLL * slot_stride) + 16 * sub;
-  const float sl2e = a.scale_log2e;
-
-  // A ring of NBUF register buffers: the loads of the next NBUF - 1 buffers
-  // are in flight while one computes. Every step issues one buffer's loads
-  // unconditionally, so the compiler waits only for the buffer it consumes;
-  // steps past the range re-read its last buffer (just fetched: an L2 hit)
-  // and skip the compute.
-  MfmaBuf<D, G> buf[NBUF];
-  const int nbuf = (kend - kbeg + 15) / 16;
-  const int kb_last = kbeg + 16 * (nbuf - 1);
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    mfma_load<D, G>(buf[p], kbase, vbase, page_reg, pg0, p_shift, slot_stride,
-                    min(kbeg + 16 * p, kb_last), k_off, v_off);
-  for (int j0 = 0; j0 < nbuf; j0 += NBUF) {
-#pragma unroll
-    for (int p = 0; p < NBUF; ++p) {
-      const int j = j0 + p;
-      mfma_load<D, G>(buf[(p + NBUF - 1) % NBUF], kbase, vbase, page_reg, pg0, p_shift,
-                      slot_stride, min(kbeg + 16 * (j + NBUF - 1), kb_last), k_off, v_off);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this compute
-      if (j < nbuf)
-        mfma_compute<D, G>(buf[p], qb, m_run, l_part, o, kbeg + 16 * j, kend, rrow, slot, sl2e,
-                           bias);
-    }
-  }
-
-  // Sums over the lanes of a head (l) and over the V slots (o): one max for
-  // the whole wave, so no rescaling.
-  float l = lane_sum_xor<16>(l_part);
-  l = lane_sum_xor<32>(l);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = o[h][i];
-      if constexpr (LPK <= 8) x = lane_sum_xor<8>(x);
-      x = lane_sum_xor<16>(x);
-      o[h][i] = lane_sum_xor<32>(x);
-    }
-
-  // Slot s writes the heads h with h % NSLOT == s; the head's l and m come
-  // from lane col = h of the row.
-  const uint32_t lu = __float_as_uint(l), mu = __float_as_uint(m_run);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    uint32_t lh, mh;
-    switch (h) {
-      case 0: lh = row_bcast<0>(lu); mh = row_bcast<0>(mu); break;
-      case 1: lh = row_bcast<1>(lu); mh = row_bcast<1>(mu); break;
-      case 2: lh = row_bcast<2>(lu); mh = row_bcast<2>(mu); break;
-      case 3: lh = row_bcast<3>(lu); mh = row_bcast<3>(mu); break;
-      case 4: lh = row_bcast<4>(lu); mh = row_bcast<4>(mu); break;
-      case 5: lh = row_bcast<5>(lu); mh = row_bcast<5>(mu); break;
-      case 6: lh = row_bcast<6>(lu); mh = row_bcast<6>(mu); break;
-      default: lh = row_bcast<7>(lu); mh = row_bcast<7>(mu); break;
-    }
-    if (h % NSLOT != slot) continue;
-    const int hq = kvh * G + h;
-    if (nparts == 1) {
-      const float inv = 1.f / __uint_as_float(lh);
-      uint32_t wv[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) wv[w] = pack_bf16x2(o[h][2 * w] * inv, o[h][2 * w + 1] * inv);
-      char* orow = (char*)a.out + ((size_t)token * a.Hq + hq) * row_bytes;
-      *reinterpret_cast<uint4*>(orow + 16 * sub) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    } else {
-      const size_t pi = ((size_t)wrow * a.max_parts + part) * a.Hq + hq;
-      float* po = a.ws + pi * D + 8 * sub;
-      *reinterpret_cast<float4*>(po) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-      *reinterpret_cast<float4*>(po + 4) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-      if (sub == 0) {
-        float* ml = a.ws + (size_t)(token_mode ? a.T : a.S) * a.max_parts * a.Hq * D;
-        *reinterpret_cast<float2*>(ml + 2 * pi) =
-            make_float2(__uint_as_float(mh), __uint_as_float(lh));
-      }
-    }
-  }
-}
-
 template <typename ET, int D, int G, bool TOKEN_MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -755,32 +427,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       decode_segment<ET, D, G, true>(a, ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part,
                                      nparts, kvh);
   } else {
-    const PlanOffsets po = plan_offsets(a.S, a.cap_dec, a.cap_pf);
-    const int4* rows = reinterpret_cast<const int4*>(a.plan + po.rows);
-    const int* first_row = a.plan + po.first_row;
-    const int n_rows = a.plan[0], C = a.plan[2], n_chunks = a.plan[3], A = a.plan[4];
-    const int kvh = blockIdx.x % a.Hkv;
-    const int stride = (gridDim.x / a.Hkv) * kWaves;  // waves serving this KV head
-    for (int chunk = (blockIdx.x / a.Hkv) * kWaves + wave; chunk < n_chunks; chunk += stride) {
-      const int c0 = chunk * C, c1 = c0 + C;
-      for (int i = first_row[chunk];; ++i) {
-        const int4 r = rows[i];  // (sequence, offset, keys, token)
-        const int off = r.y, n = r.z;
-        const int pad = (n + A - 1) / A * A;
-        const int kbeg = max(c0, off) - off;
-        const int kend = min(min(c1, off + pad) - off, n);
-        const int j0 = off / C;
-        const int nparts = (off + pad - 1) / C - j0 + 1;
-        if (kbeg < kend) {
-          if constexpr (ET::kBytes == 2)
-            decode_segment_mfma<D, G, kDecodeBufs>(a, r.x, r.w, r.x, kbeg, kend, chunk - j0, nparts, kvh,
-                                      false);
-          else
-            decode_segment<ET, D, G, false>(a, r.x, r.w, r.x, kbeg, kend, chunk - j0, nparts,
-                                            kvh);
-        }
-        if (off + pad >= c1 || i + 1 >= n_rows) break;
-      }
+    if constexpr (ET::kBytes == 2) {
+      decode_chunks_mfma<D, G>(a, blockIdx.x, gridDim.x);
+    } else {
+      decode_walk(a, blockIdx.x, gridDim.x,
+                  [&](int seq, int token, int wrow, int kbeg, int kend, int part, int nparts,
+                      int kvh) {
+                    decode_segment<ET, D, G, false>(a, seq, token, wrow, kbeg, kend, part, nparts,
+                                                    kvh);
+                  });
     }
   }
 }

@@ -70,6 +70,19 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- bf16 vectors for v_dot2 / v_cvt_pk / MFMA operands ----
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo * b.lo + a.hi * b.hi (bf16 pairs, float32 accumulation)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace pa

@@ -33,14 +33,17 @@ struct AttnArgs {
 };
 
 // Plan layout, in ints from the start of the workspace:
-//   header [kPlanHeaderInts]: [0] decode rows R, [1] prefill items,
-//     [2] chunk keys C, [3] chunks, [4] row alignment A, [5..7] unused
+//   header [kPlanHeaderInts]: [0] decode rows R, [1] prefill items (per KV
+//     head), [2] chunk keys C, [3] chunks, [4] row alignment A, [5..7]
+//     unused, [8 + h] cursor of the tick kernel's prefill queue of KV head h
+//     (zeroed)
 //   decode rows: S x (sequence, key offset, keys, token); row i's keys occupy
 //     [offset, offset + round_up(keys, A)) of the concatenated key axis
 //   partitions per sequence: S ints (0 = no decode row)
 //   first decode row of each chunk: cap_dec ints
 //   prefill items: cap_pf x (sequence, row tile)
-constexpr int kPlanHeaderInts = 8;
+constexpr int kPlanHeaderInts = 16;
+constexpr int kPlanCursors = 8;
 struct PlanOffsets {
   size_t rows, nparts, first_row, pf, total;
 };
@@ -90,6 +93,10 @@ int decode_grid(pa_dtype_t dt, int D, int G);
 hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipStream_t s);
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s);
+
+// Fused tick (pa_tick.hip): decode rows and prefill chunks in one grid.
+bool tick_supported(pa_dtype_t dt, int D);
+hipError_t launch_tick(pa_dtype_t dt, const AttnArgs& a, hipStream_t s);
 
 // K4 (pa_prefill.hip): MFMA prefill-chunk attention for sequences with L > 1.
 bool prefill_mfma_supported(pa_dtype_t dt, int D, int G);

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     plan[2] = C;
     plan[3] = (int)(chunks < cap_dec ? chunks : cap_dec);
     plan[4] = A;
-    plan[5] = plan[6] = plan[7] = 0;
+    for (int i = 5; i < kPlanHeaderInts; ++i) plan[i] = 0;
   }
 }
 

@@ -105,9 +105,9 @@ def test_attention_empty_tick_is_ok_without_touching_memory():
 
 
 def _plan_bytes(S, cap_dec, cap_pf):
-    # header 8, decode rows 4 * S, partitions per sequence S, chunk starts cap_dec,
+    # header 16, decode rows 4 * S, partitions per sequence S, chunk starts cap_dec,
     # prefill items 2 * cap_pf (ints), padded to 256 bytes
-    return -(-(8 + 5 * S + cap_dec + 2 * cap_pf) * 4 // 256) * 256
+    return -(-(16 + 5 * S + cap_dec + 2 * cap_pf) * 4 // 256) * 256
 
 
 def test_workspace_size_query():

@@ -200,6 +200,7 @@ def test_profile_hook_records_kernels():
     d.attend()
     rec = pa.pa_profile_stop()
     names = [n for n, _ in rec]
-    assert "decode_attention" in names and "prefill_attention_mfma" in names
+    # a tick that may hold prefill chunks runs decode and prefill in one grid
+    assert "plan" in names and "tick_attention" in names
     assert all(ms > 0 for _, ms in rec)
     pa.pa_profile_reset()
