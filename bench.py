@@ -13,9 +13,11 @@ rotated between steps so no step finds the previous step's pages in the
 256 MB Infinity Cache.
 
 Prints ONE JSON line. `value` = tick tokens per second. `roofline` refers to
-the dominant kernel (decode attention, HBM-bound), timed per launch with HIP
-events recorded on the library's stream. `cpu_baseline` = the CPU oracle
-(RoPE + write + float64 attention) on the same tick.
+the dominant kernel (for a mixed tick the fused decode + prefill kernel, an HBM
+stream), timed per launch with HIP events the library records on its launch
+stream; `legs` times the same tick's decode rows alone and prefill chunks alone
+(attention only). `cpu_baseline` = the CPU oracle (RoPE + write + float64
+attention) on the same tick.
 """
 
 import argparse
@@ -47,7 +49,9 @@ def algorithmic_work(t):
     Decode row of a sequence with n keys: K and V rows n*Hkv*D*e each, the
     query and output rows Hq*D*e each, and 4 bytes per page-table entry used.
     Prefill chunk of L rows after P0 cached keys: 4*D*Hq*pairs flops over the
-    unmasked (row, key) pairs, pairs = L*P0 + L(L+1)/2.
+    unmasked (row, key) pairs, pairs = L*P0 + L(L+1)/2; its bytes are the K and
+    V rows of its n = P0 + L keys read once per KV head, its query and output
+    rows, and its page-table entries.
     """
     e = 2 if t.dtype == "bf16" else 4
     dec_bytes = 0
@@ -64,7 +68,7 @@ def algorithmic_work(t):
             p0 = n - L
             pairs = L * p0 + L * (L + 1) // 2
             flops += 4 * t.D * t.Hq * pairs
-            pf_bytes += 2 * n * t.Hkv * t.D * e + 2 * L * t.Hq * t.D * e
+            pf_bytes += 2 * n * t.Hkv * t.D * e + 2 * L * t.Hq * t.D * e + 4 * math.ceil(n / t.P)
     T = t.T
     k1_bytes = T * ((t.Hq + 2 * t.Hkv) * t.D * e + 8 + t.D * 4) + T * (t.Hq + 3 * t.Hkv) * t.D * e
     return {"decode_bytes": dec_bytes, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
@@ -81,17 +85,69 @@ def cpu_baseline(t, reps):
         threads = 1
     table = oracle.rope_table(t.max_pos, t.D, t.theta) if t.theta is not None else None
     times = []
-    for _ in range(reps):
+    # at least `reps` runs, and more (up to 30) until about 10 s of CPU work
+    while len(times) < reps or (sum(times) < 10.0 and len(times) < 30):
         t0 = time.perf_counter()
         oracle.run_tick(t.dtype, t.q, t.k, t.v, t.positions, t.block_tables, t.qsl, t.seq_lens,
                         t.k_pool, t.v_pool, table, t.scale)
         times.append(time.perf_counter() - t0)
     med = float(np.median(times))
     return {"value": t.T / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the full tick ({t.T} query rows, {t.S} sequences), {reps} runs, median "
+            "sample": f"the full tick ({t.T} query rows, {t.S} sequences), {len(times)} runs, median "
                       f"{med:.2f} s per tick; numpy float32 RoPE + float64 attention",
             "seconds_per_tick": med,
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def sub_tick(t, c, mask, dev):
+    """Device tensors of the tick restricted to the sequences in `mask` (rows,
+    page tables and lengths selected; the pools are shared)."""
+    import torch
+    seqs = np.nonzero(mask)[0]
+    rows = np.concatenate([np.arange(t.qsl[s], t.qsl[s + 1]) for s in seqs]).astype(np.int64)
+    ql = t.query_lens[seqs].astype(np.int64)
+    qsl = np.zeros(len(seqs) + 1, np.int32)
+    qsl[1:] = np.cumsum(ql)
+    ridx = torch.from_numpy(rows).to(dev)
+    sidx = torch.from_numpy(seqs.astype(np.int64)).to(dev)
+    q = c["q"].index_select(0, ridx).contiguous()
+    return {"q": q, "out": torch.empty_like(q),
+            "bt": c["bt"].index_select(0, sidx).contiguous(),
+            "sl": c["sl"].index_select(0, sidx).contiguous(),
+            "qsl": torch.from_numpy(qsl).to(dev), "S": int(len(seqs)), "T": int(qsl[-1]),
+            "mql": int(ql.max()), "msl": int(t.seq_lens[seqs].max())}
+
+
+def kernel_sources_digest():
+    """sha256 over the library's kernel sources (csrc/*.hip, csrc/*.h, include/pa.h)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_page_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(ROOT, "paged_kv_cache_page_amd", "csrc", "*.h")) +
+                   [os.path.join(ROOT, "include", "pa.h")])
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<kernel>_<workload>_traffic.md, a line `traffic-json: {...}`),
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-json:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("sources_sha256") != kernel_sources_digest():
+                    return None
+                return rec.get("bytes_per_launch")
+    return None
 
 
 def main():
@@ -203,25 +259,88 @@ def main():
 
     work = algorithmic_work(t)
     tokens_per_s = t.T / (ms_per_step / 1e3)
+    attn_names = ("tick_attention", "decode_attention", "prefill_attention_mfma")
+    dominant = max((n for n in kernels if n in attn_names), key=lambda n: kernels[n]["avg_ms"],
+                   default=None)
     roof = None
     extra = {}
-    if "decode_attention" in kernels:
-        dms = kernels["decode_attention"]["avg_ms"]
-        gbps = work["decode_bytes"] / (dms / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": "decode_attention", "achieved": round(gbps, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                "traffic": None, "bytes_per_launch": work["decode_bytes"]}
-        extra["kv_read_gbps"] = round(work["decode_kv_bytes"] / (dms / 1e3) / 1e9, 1)
-        extra["kv_hbm_frac"] = round(extra["kv_read_gbps"] / HBM_PEAK_GBPS, 4)
-    if "prefill_attention_mfma" in kernels and work["prefill_flops"]:
-        pms = kernels["prefill_attention_mfma"]["avg_ms"]
-        tf = work["prefill_flops"] / (pms / 1e3) / 1e12
-        extra["prefill_mfma"] = {"achieved_tflops": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                                 "flops_per_launch": work["prefill_flops"]}
+    if dominant is not None:
+        dms = kernels[dominant]["avg_ms"]
+        if dominant == "prefill_attention_mfma":
+            tf = work["prefill_flops"] / (dms / 1e3) / 1e12
+            roof = {"bound": "mfma", "kernel": dominant, "achieved": round(tf, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "flops_per_launch": work["prefill_flops"]}
+        else:
+            # decode rows (and, in the fused tick, the prefill chunks' K/V, Q
+            # and output) are one HBM stream; the chunks' flops would take
+            # prefill_flops / MFMA peak, far below bytes / HBM peak here
+            nbytes = work["decode_bytes"] + (work["prefill_bytes"] if dominant == "tick_attention"
+                                             else 0)
+            gbps = nbytes / (dms / 1e3) / 1e9
+            roof = {"bound": "hbm", "kernel": dominant, "achieved": round(gbps, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                    "bytes_per_launch": nbytes}
+            if dominant == "tick_attention" and work["prefill_flops"]:
+                t_roof = max(nbytes / (HBM_PEAK_GBPS * 1e9),
+                             work["prefill_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                roof["flops_per_launch"] = work["prefill_flops"]
+                roof["time_bound_frac"] = round(t_roof / (dms / 1e3), 4)
+        roof["traffic"] = committed_traffic(dominant, t.name)
     attn_ms = sum(v["avg_ms"] for n, v in kernels.items() if n not in
                   ("slot_mapping", "rope_cache_write"))
     extra["attention_only_tokens_per_s"] = round(t.T / (attn_ms / 1e3), 1) if attn_ms else None
+
+    # the same tick's decode rows alone and prefill chunks alone, attention only
+    # (their K/V are in the pools since the steps above)
+    legs = {}
+    ql = t.query_lens
+    for leg, mask in (("decode_rows_only", ql == 1), ("prefill_chunks_only", ql > 1)):
+        if not mask.any() or mask.all():
+            continue
+        subs = [sub_tick(t, c, mask, dev) for c in copies]
+        sw = torch.empty(max(pa.pa_paged_attention_workspace_size(
+            subs[0]["S"], subs[0]["T"], t.Hq, t.D, subs[0]["mql"], subs[0]["msl"], t.P,
+            args.kv_split, dt), 1), dtype=torch.uint8, device=dev)
+
+        def sub_step(i, subs=subs, sw=sw):
+            c, u = copies[i % ROTATE], subs[i % ROTATE]
+            pa.pa_paged_attention_varlen(u["q"], c["kp"], c["vp"], u["bt"], u["sl"], u["qsl"],
+                                         u["mql"], u["msl"], scale=t.scale,
+                                         kv_split_tokens=args.kv_split, out=u["out"],
+                                         workspace=sw, stream=stream)
+
+        for i in range(args.warmup):
+            sub_step(i)
+        torch.cuda.synchronize()
+        pa.pa_profile_start(16 * args.steps + 16)
+        for i in range(args.steps):
+            sub_step(i)
+        rec = pa.pa_profile_stop()
+        pa.pa_profile_reset()
+        ks = {}
+        for name, ms in rec:
+            ks.setdefault(name, []).append(ms)
+        ks = {n: float(np.mean(v)) for n, v in ks.items()}
+        main_k = max((n for n in ks if n in attn_names), key=lambda n: ks[n])
+        entry = {"kernel": main_k, "avg_ms": round(ks[main_k], 5),
+                 "all_kernels_ms": {n: round(v, 5) for n, v in ks.items()}}
+        if leg == "decode_rows_only":
+            gbps = work["decode_bytes"] / (ks[main_k] / 1e3) / 1e9
+            entry.update({"bound": "hbm", "bytes_per_launch": work["decode_bytes"],
+                          "achieved_gbps": round(gbps, 1),
+                          "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                          "kv_read_gbps": round(work["decode_kv_bytes"] / (ks[main_k] / 1e3) / 1e9,
+                                                1)})
+        else:
+            tf = work["prefill_flops"] / (ks[main_k] / 1e3) / 1e12
+            entry.update({"bound": "mfma", "flops_per_launch": work["prefill_flops"],
+                          "achieved_tflops": round(tf, 1),
+                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        legs[leg] = entry
+    if legs:
+        extra["legs"] = legs
 
     cpu = None
     if not args.no_cpu:
@@ -239,6 +358,7 @@ def main():
                    "heads_q_kv": [t.Hq, t.Hkv], "head_dim": t.D, "page_size": t.P,
                    "pool_pages": t.num_pages, "seed": t.seed, "parallelism": "none (1 GPU)"},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_sources_sha256": kernel_sources_digest(),
         "wall_s_timed_region": round(wall, 4), **extra,
     }
     print(json.dumps(line), flush=True)
