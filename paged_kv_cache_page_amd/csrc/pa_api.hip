@@ -133,15 +133,17 @@ int split_tokens(int requested, int P, bool token_mode) {
 // Whether prefill rows (L > 1) go to the MFMA kernel; otherwise every row of
 // the tick takes the per-token VALU path.
 bool use_mfma_prefill(pa_dtype_t dt, int D, int max_query_len) {
-  return max_query_len <= 1 || prefill_mfma_supported(dt, D, 1);
+  return max_query_len <= 1 || tick_supported(dt, D);
 }
 
 // Workspace layout: the plan lists (seq mode), padded to 256 bytes, then the
-// split-KV partials (o for every (row, partition, head), then (m, l) pairs).
+// split-KV partials (o for every (row, partition, head), then (m, l) pairs),
+// then, for ticks with prefill chunks and automatic partitions, the prefill
+// piece partials and their arrival counters.
 struct WsLayout {
   long cap_dec, cap_pf;
-  size_t plan_bytes, partial_bytes;
-  int max_parts;
+  size_t plan_bytes, partial_bytes, pf_bytes;
+  int max_parts, pf_slots;
   bool token_mode;
 };
 
@@ -164,6 +166,8 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
   w.cap_dec = 0;
   w.cap_pf = 0;
   w.plan_bytes = 0;
+  w.pf_slots = 0;
+  w.pf_bytes = 0;
   if (!w.token_mode) {
     w.cap_dec = (long)S * w.max_parts;
     if (max_query_len > 1) {
@@ -172,12 +176,20 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
       const long by_seq = (long)S * ((max_query_len + tm - 1) / tm);
       const long by_tok = (long)T / tm + S;
       w.cap_pf = by_seq < by_tok ? by_seq : by_tok;
+      if (pt == 0) {
+        // automatic partitions: long items may be cut into pieces, at most one
+        // extra entry per partial slot
+        w.pf_slots = kPrefillSlots;
+        w.cap_pf += kPrefillSlots;
+        w.pf_bytes = ((size_t)kPrefillSlots * kPrefillRows * ((size_t)D + 2) * sizeof(float) +
+                      255) / 256 * 256;
+      }
     }
-    w.plan_bytes = (plan_offsets(S, w.cap_dec, w.cap_pf).total * sizeof(int) + 255) / 256 * 256;
+    w.plan_bytes = (plan_offsets(S, Hq, w.cap_dec, w.cap_pf).total * sizeof(int) + 255) / 256 * 256;
   }
   const long rows = w.token_mode ? T : S;
-  w.partial_bytes = w.max_parts > 1 ? (size_t)rows * (size_t)w.max_parts * (size_t)Hq *
-                                          ((size_t)D + 2) * sizeof(float)
+  w.partial_bytes = w.max_parts > 1 ? ((size_t)rows * (size_t)w.max_parts * (size_t)Hq *
+                                           ((size_t)D + 2) * sizeof(float) + 255) / 256 * 256
                                     : 0;
   return w;
 }
@@ -185,7 +197,7 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
 size_t workspace_bytes_for(int S, int T, int Hq, int D, int max_query_len, int max_seq_len,
                            int P, int kv_split, pa_dtype_t dt) {
   const WsLayout w = workspace_layout(S, T, Hq, D, max_query_len, max_seq_len, P, kv_split, dt);
-  return w.plan_bytes + w.partial_bytes;
+  return w.plan_bytes + w.partial_bytes + w.pf_bytes;
 }
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -300,7 +312,7 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
     return PA_ERR_INVALID_ARG;
   const WsLayout wl = workspace_layout(S, T, Hq, head_dim, max_query_len, max_seq_len,
                                        page_size, kv_split_tokens, dtype);
-  const size_t need = wl.plan_bytes + wl.partial_bytes;
+  const size_t need = wl.plan_bytes + wl.partial_bytes + wl.pf_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && ((uintptr_t)workspace & 255u)) return PA_ERR_INVALID_ARG;
   if (wl.cap_dec > INT32_MAX / 2 || wl.cap_pf > INT32_MAX / 2) return PA_ERR_INVALID_ARG;
@@ -341,6 +353,9 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.max_parts = wl.max_parts;
   a.dec_grid = wl.token_mode ? 0 : decode_grid(dtype, head_dim, G);
   a.scale_log2e = scale * kLog2e;
+  a.pf_slots = wl.pf_slots;
+  a.pf_ws = (float*)((char*)workspace + wl.plan_bytes + wl.partial_bytes);
+  a.pf_workers = (!wl.token_mode && wl.cap_pf > 0) ? tick_grid(dtype, head_dim, G) : 1;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -352,20 +367,12 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
     // a tick that may hold prefill chunks: decode and prefill share one grid
     e = launch_tick(dtype, a, s);
     if (e != hipSuccess) return PA_ERR_HIP;
-    if (a.max_parts > 1) {
-      e = launch_split_reduce(dtype, a, false, s);
-      if (e != hipSuccess) return PA_ERR_HIP;
-    }
-    return PA_OK;
+    return launch_tick_reduce(a, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   e = launch_decode(dtype, a, wl.token_mode, s);
   if (e != hipSuccess) return PA_ERR_HIP;
   if (a.max_parts > 1) {
     e = launch_split_reduce(dtype, a, wl.token_mode, s);
-    if (e != hipSuccess) return PA_ERR_HIP;
-  }
-  if (!wl.token_mode && a.cap_pf > 0) {
-    e = launch_prefill_mfma(dtype, a, s);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;

@@ -14,14 +14,12 @@
 // with a lane read into a scalar register.
 //
 // For the decode rows of a tick the plan kernel lays all rows end to end on
-// one key axis and cuts it into equal chunks, one per wave (see pa_plan.hip):
-// a wave walks the rows its chunk covers, one range per row, so every wave
-// gets the same number of keys whatever the spread of lengths. Workgroup b
-// serves KV head b % Hkv (the grid is a multiple of 8, so each XCD keeps the
-// same KV heads and the slices of a prefix page shared by many sequences stay
-// in that XCD's L2); its four waves take successive chunks. The per-token
-// mode (prefill rows without a matrix-core kernel, i.e. float32) maps waves to
-// (token, fixed partition, KV head) directly.
+// one key axis and cuts it into equal chunks, one per wave (see
+// pa_plan.hip): a wave walks the rows its chunk covers, one range per row, so
+// every wave gets the same number of keys whatever the spread of lengths
+// (decode_walk in pa_decode_mfma.h). The per-token mode (prefill rows without
+// a matrix-core kernel, i.e. float32) maps waves to (token, fixed partition,
+// KV head) directly.
 //
 // Inside a wave, LPK lanes hold one key row (16 or 32 bytes each), so a wave
 // covers 64 / LPK keys per step (its "slots") and UNROLL steps per buffer.
@@ -62,50 +60,6 @@ struct DecodeShape {
     return ((i / EPV) * LPK + sub) * EPV + (i % EPV);
   }
 };
-
-// Which row a work item serves, and that row's key limit.
-struct RowInfo {
-  int seq;      // sequence index
-  int token;    // row of q / out
-  int n_eff;    // keys this row attends: 0 .. n_eff - 1
-  bool active;
-};
-
-template <bool TOKEN_MODE>
-__device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
-  RowInfo r;
-  r.active = false;
-  int s, L, i;
-  if constexpr (TOKEN_MODE) {
-    int lo = 0, hi = a.S;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.qsl[mid] <= row) lo = mid; else hi = mid;
-    }
-    s = lo;
-    const int q0 = a.qsl[s];
-    L = a.qsl[s + 1] - q0;
-    i = row - q0;
-    r.token = row;
-    if (i < 0 || i >= L) return r;
-  } else {
-    s = row;
-    const int q0 = a.qsl[s];
-    L = a.qsl[s + 1] - q0;
-    i = 0;
-    r.token = q0;
-    if (L != 1 || q0 < 0 || q0 >= a.T) return r;
-  }
-  // Keys beyond the block table or beyond max_seq_len are never read (the
-  // caller promised neither happens; this keeps every index in range if not).
-  int n = a.seq_lens[s];
-  n = min(n, a.max_blocks * a.P);
-  n = min(n, a.max_seq_len);
-  r.seq = s;
-  r.n_eff = n - L + i + 1;
-  r.active = r.n_eff > 0;
-  return r;
-}
 
 // Issue the loads of one buffer: the KPI keys starting at `kb` (wave-uniform,
 // a multiple of KPI, inside the partition). The page id comes from lane
@@ -440,58 +394,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   }
 }
 
-// K3: one thread per (row, query head, 4 consecutive dims).
+// K3: one thread per (row, query head, 4 consecutive dims); the body is
+// split_reduce_task (pa_decode_mfma.h), shared with the fused tick's reduce.
 template <typename ET, bool TOKEN_MODE>
 __global__ __launch_bounds__(256) void split_reduce_kernel(AttnArgs a) {
-  const int D = a.D;
-  const int quads = D / 4;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int d4 = (int)(idx % quads);
-  const long rh = idx / quads;
-  const int h = (int)(rh % a.Hq);
-  const long row = rh / a.Hq;
-  if (row >= (TOKEN_MODE ? a.T : a.S)) return;
-  int nparts, token;
-  if constexpr (TOKEN_MODE) {
-    const RowInfo ri = row_info<true>(a, (int)row);
-    if (!ri.active) return;
-    nparts = (ri.n_eff + a.part_tokens - 1) / a.part_tokens;
-    token = (int)row;
-  } else {
-    nparts = a.plan[plan_offsets(a.S, a.cap_dec, a.cap_pf).nparts + row];
-    if (nparts <= 1) return;
-    token = a.qsl[row];
-  }
-  if (nparts <= 1) return;
-  nparts = min(nparts, a.max_parts);
-  const long rows = TOKEN_MODE ? a.T : a.S;
-  const float* ml = a.ws + (size_t)rows * a.max_parts * a.Hq * D;
-  const size_t p0 = (size_t)row * a.max_parts * a.Hq + h;  // partial index of part 0
-  float mn = kNegBig;
-  for (int k = 0; k < nparts; ++k) mn = fmaxf(mn, ml[2 * (p0 + (size_t)k * a.Hq)]);
-  float lt = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int k = 0; k < nparts; ++k) {
-    const size_t pi = p0 + (size_t)k * a.Hq;
-    const float2 mlk = *reinterpret_cast<const float2*>(ml + 2 * pi);
-    const float4 ok = *reinterpret_cast<const float4*>(a.ws + pi * D + 4 * d4);
-    const float c = fast_exp2(mlk.x - mn);
-    lt = fmaf(mlk.y, c, lt);
-    acc.x = fmaf(ok.x, c, acc.x);
-    acc.y = fmaf(ok.y, c, acc.y);
-    acc.z = fmaf(ok.z, c, acc.z);
-    acc.w = fmaf(ok.w, c, acc.w);
-  }
-  const float inv = 1.f / lt;
-  const size_t oi = ((size_t)token * a.Hq + h) * D + 4 * d4;
-  if constexpr (ET::kBytes == 2) {
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
-        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
-  } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  }
+  split_reduce_task<ET, TOKEN_MODE>(a, (long)blockIdx.x * 256 + threadIdx.x);
 }
 
 // ------------------------------------------------------------ dispatch -----

@@ -1,6 +1,6 @@
-// bf16 decode work items on matrix cores, and the walk of a decode worker
-// over its chunks of the decode key axis. Shared by the decode kernel and the
-// fused tick kernel.
+// bf16 decode work items on matrix cores, the walk of a decode worker over its
+// chunks of the decode key axis, and the merge of split-KV partitions. Shared
+// by the decode kernels and the fused tick kernel.
 #pragma once
 
 #include "pa_device.h"
@@ -16,21 +16,125 @@ namespace pa {
 constexpr int kDecodeBufs = 2;
 constexpr int kDecodeWgPerCu = 1;
 
+// Which row a work item serves, and that row's key limit.
+struct RowInfo {
+  int seq;      // sequence index
+  int token;    // row of q / out
+  int n_eff;    // keys this row attends: 0 .. n_eff - 1
+  bool active;
+};
+
+template <bool TOKEN_MODE>
+__device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
+  RowInfo r;
+  r.active = false;
+  int s, L, i;
+  if constexpr (TOKEN_MODE) {
+    int lo = 0, hi = a.S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.qsl[mid] <= row) lo = mid; else hi = mid;
+    }
+    s = lo;
+    const int q0 = a.qsl[s];
+    L = a.qsl[s + 1] - q0;
+    i = row - q0;
+    r.token = row;
+    if (i < 0 || i >= L) return r;
+  } else {
+    s = row;
+    const int q0 = a.qsl[s];
+    L = a.qsl[s + 1] - q0;
+    i = 0;
+    r.token = q0;
+    if (L != 1 || q0 < 0 || q0 >= a.T) return r;
+  }
+  // Keys beyond the block table or beyond max_seq_len are never read (the
+  // caller promised neither happens; this keeps every index in range if not).
+  int n = a.seq_lens[s];
+  n = min(n, a.max_blocks * a.P);
+  n = min(n, a.max_seq_len);
+  r.seq = s;
+  r.n_eff = n - L + i + 1;
+  r.active = r.n_eff > 0;
+  return r;
+}
+
+// K3 task idx = (row, query head, 4 consecutive dims): merge the row's
+// split-KV partitions, m* = max_k m_k,
+// o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k.
+template <typename ET, bool TOKEN_MODE>
+__device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
+  const int D = a.D;
+  const int quads = D / 4;
+  const int d4 = (int)(idx % quads);
+  const long rh = idx / quads;
+  const int h = (int)(rh % a.Hq);
+  const long row = rh / a.Hq;
+  if (row >= (TOKEN_MODE ? a.T : a.S)) return;
+  int nparts, token;
+  if constexpr (TOKEN_MODE) {
+    const RowInfo ri = row_info<true>(a, (int)row);
+    if (!ri.active) return;
+    nparts = (ri.n_eff + a.part_tokens - 1) / a.part_tokens;
+    token = (int)row;
+  } else {
+    nparts = a.plan[plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf).nparts + row];
+    if (nparts <= 1) return;
+    token = a.qsl[row];
+  }
+  if (nparts <= 1) return;
+  nparts = min(nparts, a.max_parts);
+  const long rows = TOKEN_MODE ? a.T : a.S;
+  const float* ml = a.ws + (size_t)rows * a.max_parts * a.Hq * D;
+  const size_t p0 = (size_t)row * a.max_parts * a.Hq + h;  // partial index of part 0
+  float mn = kNegBig;
+  for (int k = 0; k < nparts; ++k) mn = fmaxf(mn, ml[2 * (p0 + (size_t)k * a.Hq)]);
+  float lt = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = 0; k < nparts; ++k) {
+    const size_t pi = p0 + (size_t)k * a.Hq;
+    const float2 mlk = *reinterpret_cast<const float2*>(ml + 2 * pi);
+    const float4 ok = *reinterpret_cast<const float4*>(a.ws + pi * D + 4 * d4);
+    const float c = fast_exp2(mlk.x - mn);
+    lt = fmaf(mlk.y, c, lt);
+    acc.x = fmaf(ok.x, c, acc.x);
+    acc.y = fmaf(ok.y, c, acc.y);
+    acc.z = fmaf(ok.z, c, acc.z);
+    acc.w = fmaf(ok.w, c, acc.w);
+  }
+  const float inv = 1.f / lt;
+  const size_t oi = ((size_t)token * a.Hq + h) * D + 4 * d4;
+  if constexpr (ET::kBytes == 2) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+}
+
 // Walk of decode worker `wg` of `n_wg` (workgroups of 4 waves) over the
-// chunks of the decode key axis the plan kernel cut (see pa_plan.hip):
-// workgroup wg serves KV head wg % Hkv, its waves take successive chunks, and
-// each wave calls seg(seq, token, wrow, kbeg, kend, part, nparts, kvh) for the
-// part of every row its chunk covers.
+// chunks of the decode key axis the plan kernel cut (see pa_plan.hip). Wave
+// gw = 4 wg + wave serves KV head gw % Hkv: the four waves of a workgroup
+// serve different heads, so every XCD streams several heads' rows at once
+// (one head per workgroup measured slower). The waves of a head take its
+// chunks in turn; for every chunk the wave calls
+// seg(seq, token, wrow, kbeg, kend, part, nparts, kvh) on the part of each row
+// the chunk covers.
 template <typename Seg>
 __device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, int n_wg, Seg&& seg) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const PlanOffsets po = plan_offsets(a.S, a.cap_dec, a.cap_pf);
+  const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
   const int4* rows = reinterpret_cast<const int4*>(a.plan + po.rows);
   const int* first_row = a.plan + po.first_row;
   const int n_rows = a.plan[0], C = a.plan[2], n_chunks = a.plan[3], A = a.plan[4];
-  const int kvh = wg % a.Hkv;
-  const int stride = (n_wg / a.Hkv) * 4;  // waves serving this KV head
-  for (int chunk = (wg / a.Hkv) * 4 + wave; chunk < n_chunks; chunk += stride) {
+  const int Hkv = a.Hkv;
+  const int gw = wg * 4 + wave;
+  const int kvh = gw % Hkv;
+  const int n_head = (n_wg * 4 - kvh + Hkv - 1) / Hkv;  // waves serving this head
+  for (int chunk = gw / Hkv; chunk < n_chunks; chunk += n_head) {
     const int c0 = chunk * C, c1 = c0 + C;
     for (int i = first_row[chunk];; ++i) {
       const int4 r = rows[i];  // (sequence, offset, keys, token)

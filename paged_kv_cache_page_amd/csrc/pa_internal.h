@@ -30,34 +30,53 @@ struct AttnArgs {
   int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / smallest size))
   int32_t dec_grid;     // workgroups of the decode kernel (a multiple of 8)
   float scale_log2e;    // scale * log2(e): weights are exp2(s * scale_log2e - m)
+  // Key-range pieces of long prefill items (automatic partitions only):
+  float* pf_ws;         // partials: o [pf_slots][kPrefillRows][D], then (m, l) [pf_slots][kPrefillRows]
+  int32_t pf_slots;     // partial slots (0 = never split)
+  int32_t pf_workers;   // workgroups of the kernel that runs the prefill items
 };
 
 // Plan layout, in ints from the start of the workspace:
-//   header [kPlanHeaderInts]: [0] decode rows R, [1] prefill items (per KV
-//     head), [2] chunk keys C, [3] chunks, [4] row alignment A, [5..7]
-//     unused, [8 + h] cursor of the tick kernel's prefill queue of KV head h
-//     (zeroed)
+//   header [32]: [0] decode rows R, [1] prefill entries (per KV head), [2]
+//     chunk keys C, [3] chunks, [4] row alignment A, [5] cut prefill items,
+//     [6..31] unused
+//   prefill queue cursors: Hq counters, one per 128-byte line (Hq >= Hkv
+//     bounds the KV heads, which the workspace query does not see): the
+//     queue of KV head h at kPlanLine * (1 + h); zeroed by the plan kernel,
+//     advanced with device-scope atomics
 //   decode rows: S x (sequence, key offset, keys, token); row i's keys occupy
 //     [offset, offset + round_up(keys, A)) of the concatenated key axis
 //   partitions per sequence: S ints (0 = no decode row)
 //   first decode row of each chunk: cap_dec ints
-//   prefill items: cap_pf x (sequence, row tile)
-constexpr int kPlanHeaderInts = 16;
-constexpr int kPlanCursors = 8;
+//   prefill entries (16-byte aligned): cap_pf x (sequence, row tile,
+//     piece j | pieces J << 16, first partial slot), in decreasing cost order;
+//     an item (sequence, row tile) of J > 1 pieces owns the partial slots
+//     [slot, slot + J * Hkv): KV head h, piece j at slot + h * J + j
+//   cut prefill items: cap_pf x (sequence, row tile, J, slot), merged by the
+//     prefill merge kernel after the tick
+constexpr int kPlanLine = 32;  // ints per 128-byte cache line
 struct PlanOffsets {
-  size_t rows, nparts, first_row, pf, total;
+  size_t rows, nparts, first_row, pf, merge, total;
 };
-__host__ __device__ inline PlanOffsets plan_offsets(long S, long cap_dec, long cap_pf) {
+__host__ __device__ inline PlanOffsets plan_offsets(long S, long Hq, long cap_dec, long cap_pf) {
   PlanOffsets o;
-  o.rows = kPlanHeaderInts;
+  o.rows = (size_t)kPlanLine * (1 + (size_t)Hq);
   o.nparts = o.rows + 4 * (size_t)S;
   o.first_row = o.nparts + (size_t)S;
-  o.pf = o.first_row + (size_t)cap_dec;
-  o.total = o.pf + 2 * (size_t)cap_pf;
+  o.pf = (o.first_row + (size_t)cap_dec + 3) / 4 * 4;
+  o.merge = o.pf + 4 * (size_t)cap_pf;
+  o.total = o.merge + 4 * (size_t)cap_pf;
   return o;
 }
+__host__ __device__ inline int plan_pf_cursor(int h) { return kPlanLine * (1 + h); }
 // Query rows per prefill workgroup; a tile holds kPrefillRows / G tokens.
-constexpr int kPrefillRows = 64;
+constexpr int kPrefillRows = 128;
+// Keys per prefill K/V tile (the unit in which prefill items are cut into pieces).
+constexpr int kPrefillTileKeys = 64;
+// Partial slots of prefill pieces (per call; the plan kernel lengthens the
+// pieces until they fit) and the shortest piece, in tiles.
+constexpr int kPrefillSlots = 512;
+constexpr int kMinPieceTiles = 4;
 
 // Workgroups of `func` (launched with `threads` threads) that the current
 // device holds at once: compute units x resident workgroups per unit. Cached
@@ -94,12 +113,13 @@ hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipS
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s);
 
-// Fused tick (pa_tick.hip): decode rows and prefill chunks in one grid.
+// Fused tick (pa_tick.hip): decode rows and prefill chunks (K4 on MFMA) in
+// one persistent grid; tick_grid = its workgroup count.
 bool tick_supported(pa_dtype_t dt, int D);
+int tick_grid(pa_dtype_t dt, int D, int G);
 hipError_t launch_tick(pa_dtype_t dt, const AttnArgs& a, hipStream_t s);
-
-// K4 (pa_prefill.hip): MFMA prefill-chunk attention for sequences with L > 1.
-bool prefill_mfma_supported(pa_dtype_t dt, int D, int G);
-hipError_t launch_prefill_mfma(pa_dtype_t dt, const AttnArgs& a, hipStream_t s);
+// After the tick (pa_tick.hip): merge of the decode rows' split-KV partitions
+// and of the pieces of cut prefill items, in one launch.
+hipError_t launch_tick_reduce(const AttnArgs& a, hipStream_t s);
 
 }  // namespace pa

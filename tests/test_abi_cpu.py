@@ -104,10 +104,12 @@ def test_attention_empty_tick_is_ok_without_touching_memory():
     assert attn(S=0, T=0) == OK
 
 
-def _plan_bytes(S, cap_dec, cap_pf):
-    # header 16, decode rows 4 * S, partitions per sequence S, chunk starts cap_dec,
-    # prefill items 2 * cap_pf (ints), padded to 256 bytes
-    return -(-(16 + 5 * S + cap_dec + 2 * cap_pf) * 4 // 256) * 256
+def _plan_bytes(S, cap_dec, cap_pf, Hq):
+    # header 32, one 32-int line per prefill queue cursor (Hq), decode rows 4 * S,
+    # partitions per sequence S, chunk starts cap_dec, then (16-byte aligned)
+    # prefill entries 4 * cap_pf and cut items 4 * cap_pf (ints), padded to 256 bytes
+    pf = -(-(32 * (1 + Hq) + 5 * S + cap_dec) // 4) * 4
+    return -(-(pf + 8 * cap_pf) * 4 // 256) * 256
 
 
 def test_workspace_size_query():
@@ -116,18 +118,26 @@ def test_workspace_size_query():
     # automatic split: decode rows share one key axis cut into chunks of at least 256
     # keys (P = 256), so a row of n keys has at most ceil(n / 256) + 1 partials
     assert ws(64, 64, 32, 128, 1, 256, 256, 0, BF16) == (
-        _plan_bytes(64, 64 * 2, 0) + 64 * 2 * 32 * 130 * 4)
+        _plan_bytes(64, 64 * 2, 0, 32) + 64 * 2 * 32 * 130 * 4)
     n = ws(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
-    assert n == _plan_bytes(64, 64 * 17, 0) + 64 * 17 * 32 * 130 * 4
+    assert n == _plan_bytes(64, 64 * 17, 0, 32) + 64 * 17 * 32 * 130 * 4
     # an explicit split of 1024 keys: partitions aligned to the row start, 4 partials
     assert ws(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == (
-        _plan_bytes(64, 64 * 4, 0) + 64 * 4 * 32 * 130 * 4)
+        _plan_bytes(64, 64 * 4, 0, 32) + 64 * 4 * 32 * 130 * 4)
     # a partition spans at most 64 pages: with P = 16 an explicit 4096 is capped at 63 * 16
-    assert ws(4, 4, 4, 16, 1, 4096, 16, 4096, F32) == _plan_bytes(4, 4 * 5, 0) + 4 * 5 * 4 * 18 * 4
-    # prefill rows: a row tile holds at least 8 tokens (64 rows, group <= 8), so at most
-    # min(S * ceil(Lmax / 8), T / 8 + S) row tiles are planned
+    assert ws(4, 4, 4, 16, 1, 4096, 16, 4096, F32) == (
+        _plan_bytes(4, 4 * 5, 0, 4) + -(-(4 * 5 * 4 * 18 * 4) // 256) * 256)  # padded to 256
+    # prefill rows: a row tile holds at least 16 tokens (128 rows, group <= 8), so at
+    # most min(S * ceil(Lmax / 16), T / 16 + S) row tiles are planned; with automatic
+    # partitions long items may be cut into pieces: 512 partial slots of 128 rows
+    # (D + 2 floats each), one more entry per slot at most
+    pf_bytes = -(-(512 * 128 * 130 * 4) // 256) * 256
     assert ws(51, 2096, 32, 128, 1024, 4096, 256, 0, BF16) == (
-        _plan_bytes(51, 51 * 17, min(51 * 128, 2096 // 8 + 51)) + 51 * 17 * 32 * 130 * 4)
+        _plan_bytes(51, 51 * 17, min(51 * 64, 2096 // 16 + 51) + 512, 32)
+        + 51 * 17 * 32 * 130 * 4 + pf_bytes)
+    # a fixed split never cuts prefill items
+    assert ws(51, 2096, 32, 128, 1024, 4096, 256, 1024, BF16) == (
+        _plan_bytes(51, 51 * 4, min(51 * 64, 2096 // 16 + 51), 32) + 51 * 4 * 32 * 130 * 4)
     # fp32 with prefill rows takes the per-token path (512-key partitions): one row per
     # token, no plan
     assert ws(4, 40, 4, 16, 20, 1024, 16, 0, F32) == 40 * 2 * 4 * 18 * 4

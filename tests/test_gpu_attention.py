@@ -61,6 +61,8 @@ SMALL_CASES = [
     (W.BF16, 8, 8, 128, 256, (1, 257, 600, 1000), (1, 1, 88, 129)),   # group 1, n = 1
     (W.BF16, 16, 2, 64, 32, (5, 70, 200), (5, 1, 131)),               # group 8
     (W.BF16, 4, 2, 128, 16, (16, 32, 48), (16, 16, 16)),              # page-aligned chunks
+    (W.BF16, 32, 4, 64, 16, (3000, 1, 700), (200, 1, 64)),            # long items cut into pieces
+    (W.BF16, 16, 8, 128, 256, (5000, 2600), (300, 40)),               # pieces, group 2
     (W.F32, 4, 2, 16, 16, (5, 17, 33, 64), (1, 3, 1, 20)),            # fp32 prefill (token path)
     (W.F32, 8, 1, 64, 16, (100, 3, 700), (1, 3, 65)),
     (W.F32, 8, 4, 128, 32, (90, 190), (1, 45)),
