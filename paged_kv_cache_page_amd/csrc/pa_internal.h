@@ -77,6 +77,10 @@ constexpr int kPrefillTileKeys = 64;
 // pieces until they fit) and the shortest piece, in tiles.
 constexpr int kPrefillSlots = 512;
 constexpr int kMinPieceTiles = 4;
+// Decode keys a decode wave streams (one KV head, K and V) in the time a
+// prefill workgroup takes for one K/V tile of its item, both sharing the GPU:
+// about 0.1 us per key against 3 us per tile on MI355X at head_dim 128.
+constexpr int kDecodeKeysPerTile = 32;
 
 // Workgroups of `func` (launched with `threads` threads) that the current
 // device holds at once: compute units x resident workgroups per unit. Cached

@@ -2,9 +2,10 @@
 //
 // The host knows only upper bounds (max_query_len, max_seq_len); the lengths of
 // the tick's sequences live in device memory. Instead of launching a grid over
-// every (sequence, tile) pair and letting most workgroups exit, one small
-// workgroup reads query_start_loc and seq_lens once and writes two compact
-// lists into the workspace:
+// every (sequence, tile) pair and letting most workgroups exit, a single wave
+// reads query_start_loc and seq_lens and writes compact lists into the
+// workspace (one wave: wave-level scans and reductions, no workgroup
+// barriers; a 1024-thread version spent most of its time in them):
 //   decode rows   every row with query length 1, laid end to end on one key
 //                 axis (each row padded to a multiple of A keys), cut into
 //                 equal chunks of C keys, one per decode wave: every wave gets
@@ -31,48 +32,33 @@ namespace pa {
 
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kCostBins = 2048;
-constexpr int kCachedSeqs = 4096;  // sequence shapes kept in LDS between the passes
+constexpr int kPlanThreads = 64;    // one wave
+constexpr int kCostBins = 2048;     // key tiles of a prefill item, capped
+constexpr int kCachedSeqs = 4096;   // sequence shapes kept in LDS between the passes
 
-constexpr int kPlanWaves = kPlanThreads / 64;
-
-// Exclusive scan of one int per thread over the workgroup (a shuffle scan in
-// each wave, then the wave totals through LDS); returns the thread's offset
-// and writes the workgroup total to *total (uniform).
-__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Exclusive prefix sum over the wave; *total = the wave's sum (uniform).
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x & 63;
   int incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int t = __shfl_up(incl, off);
     if (lane >= off) incl += t;
   }
-  if (lane == 63) s_wave[w] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < kPlanWaves; ++i) {
-    const int x = s_wave[i];
-    before += i < w ? x : 0;
-    all += x;
-  }
-  __syncthreads();  // s_wave is free again
-  *total = all;
-  return before + incl - v;
+  *total = __shfl(incl, 63);
+  return incl - v;
 }
 
-// Sum of one 64-bit value per thread over the workgroup (uniform result).
-__device__ long long block_sum(long long v, long long* s_wave) {
+__device__ __forceinline__ long long wave_sum(long long v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
-  __syncthreads();
-  long long all = 0;
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
-  for (int i = 0; i < kPlanWaves; ++i) all += s_wave[i];
-  __syncthreads();
-  return all;
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
+  return v;
 }
 
 struct SeqShape {
@@ -91,6 +77,8 @@ __device__ __forceinline__ SeqShape seq_shape(const AttnArgs& a, int s) {
   return r;
 }
 
+__device__ __forceinline__ bool is_prefill(const SeqShape& sh) { return sh.L > 1 && sh.n >= sh.L; }
+
 // Key tiles of row tile mt (the keys its last row sees, in kPrefillTileKeys
 // units), capped at kCostBins - 1: the plan cuts and orders items by this.
 __device__ __forceinline__ int item_tiles(const SeqShape& sh, int mt, int TM) {
@@ -103,16 +91,33 @@ __device__ __forceinline__ int item_tiles(const SeqShape& sh, int mt, int TM) {
 // Pieces of an item of t tiles for piece length Tp (1 = not cut).
 __device__ __forceinline__ int item_pieces(int t, int Tp) { return t > Tp ? (t + Tp - 1) / Tp : 1; }
 
+// Calls f(s, shape) for every prefill sequence, the whole wave together (its
+// lanes then go over the sequence's row tiles); sequences are found 64 at a
+// time with a ballot, so decode-only stretches cost one test per lane.
+template <typename Shape, typename F>
+__device__ __forceinline__ void for_prefill_seqs(int S, Shape&& shape, F&& f) {
+  const int lane = threadIdx.x & 63;
+  for (int c0 = 0; c0 < S; c0 += 64) {
+    const int s = c0 + lane;
+    SeqShape sh{0, 0, 0};
+    if (s < S) sh = shape(s);
+    unsigned long long m = __ballot(s < S && is_prefill(sh));
+    while (m) {
+      const int i = __builtin_ctzll(m);
+      m &= m - 1;
+      const SeqShape u{__shfl(sh.L, i), __shfl(sh.n, i), __shfl(sh.q0, i)};
+      f(c0 + i, u);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* plan, int cap_dec,
                                                             int cap_pf, int TM) {
-  __shared__ int s_buf[kPlanWaves];
-  __shared__ long long s_keys[kPlanWaves];
   __shared__ int s_hist[kCostBins];
   __shared__ int s_cur[kCostBins];
-  __shared__ int s_tp, s_slot_next, s_merge_next, s_maxt;
-  __shared__ long long s_tiles[kPlanWaves];
   __shared__ int s_L[kCachedSeqs], s_n[kCachedSeqs], s_q0[kCachedSeqs];
-  const int tid = threadIdx.x;
+  __shared__ int s_slot_next, s_merge_next;
+  const int lane = threadIdx.x;
   const PlanOffsets po = plan_offsets(a.S, a.Hq, cap_dec, cap_pf);
   int4* dec_rows = reinterpret_cast<int4*>(plan + po.rows);
   int* nparts_of = plan + po.nparts;
@@ -125,13 +130,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     return s < kCachedSeqs ? SeqShape{s_L[s], s_n[s], s_q0[s]} : seq_shape(a, s);
   };
 
-  for (int i = tid; i < kCostBins; i += kPlanThreads) s_hist[i] = 0;
-  if (tid == 0) s_maxt = 0;
-  __syncthreads();
+  for (int i = lane; i < kCostBins / 4; i += 64)
+    reinterpret_cast<int4*>(s_hist)[i] = make_int4(0, 0, 0, 0);
+  if (lane == 0) {
+    s_slot_next = 0;
+    s_merge_next = 0;
+  }
 
-  // ---- pass 1: shapes, padded decode keys, prefill cost histogram ----
+  // ---- pass 1: shapes, padded decode keys ----
   long long my_keys = 0;
-  for (int s = tid; s < a.S; s += kPlanThreads) {
+  for (int s = lane; s < a.S; s += 64) {
     const SeqShape sh = seq_shape(a, s);
     if (s < kCachedSeqs) {
       s_L[s] = sh.L;
@@ -140,58 +148,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     }
     if (sh.L == 1 && sh.n >= 1) my_keys += (sh.n + A - 1) / A * A;
   }
-  const long long total_keys = block_sum(my_keys, s_keys);  // length of the key axis
-  // prefill items' key tiles: one wave per sequence, lanes over its row tiles
-  const int lane = tid & 63, wid = tid >> 6;
-  long long my_tiles = 0;
-  for (int s = wid; s < a.S; s += kPlanWaves) {
-    const SeqShape sh = shape(s);
-    if (sh.L > 1 && sh.n >= sh.L) {
-      const int ntiles = (sh.L + TM - 1) / TM;
-      for (int mt = lane; mt < ntiles; mt += 64) {
-        const int t = item_tiles(sh, mt, TM);
-        atomicAdd(&s_hist[t], 1);
-        atomicMax(&s_maxt, t);
-        my_tiles += t;
-      }
-    }
-  }
-  const long long item_tiles_all = block_sum(my_tiles, s_tiles);  // per KV head
-
-  // ---- piece length Tp (wave 0): the mean tile count per prefill workgroup,
-  // doubled until the cut items' partials (J slots per item and KV head) fit ----
-  if (wid == 0) {
-    int Tp = 0x3FFFFFFF;  // never cut
-    if (a.pf_slots > 0 && a.part_tokens == 0 && item_tiles_all > 0) {
-      const long long w = a.pf_workers > 0 ? a.pf_workers : 1;
-      long long t0 = (item_tiles_all * a.Hkv + w - 1) / w;
-      Tp = (int)(t0 < kMinPieceTiles ? kMinPieceTiles : (t0 > kCostBins ? kCostBins : t0));
-      for (int tries = 0;; ++tries) {
-        long long need = 0;
-        for (int b = lane; b <= s_maxt; b += 64) {  // bins past the longest item are empty
-          const int J = item_pieces(b, Tp);
-          if (J > 1) need += (long long)s_hist[b] * J;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) need += __shfl_xor(need, off);
-        if (need * a.Hkv <= a.pf_slots) break;
-        if (tries >= 12) {
-          Tp = 0x3FFFFFFF;
-          break;
-        }
-        Tp *= 2;
-      }
-    }
-    if (lane == 0) {
-      s_tp = Tp;
-      s_slot_next = 0;
-      s_merge_next = 0;
-    }
-  }
+  const long long total_keys = wave_sum(my_keys);  // length of the decode key axis
   __syncthreads();
-  const int Tp = s_tp;
 
-  // ---- chunk size ----
+  // ---- prefill items: key tiles (histogram, sum, max) ----
+  long long my_tiles = 0;
+  int my_maxt = 0;
+  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
+    const int ntiles = (sh.L + TM - 1) / TM;
+    for (int mt = lane; mt < ntiles; mt += 64) {
+      const int t = item_tiles(sh, mt, TM);
+      atomicAdd(&s_hist[t], 1);
+      my_tiles += t;
+      my_maxt = max(my_maxt, t);
+    }
+  });
+  const long long item_tiles_all = wave_sum(my_tiles);  // per KV head
+  const int maxt = wave_max(my_maxt);
+  __syncthreads();
+
+  // ---- chunk size of the decode key axis ----
   int C = a.part_tokens;
   if (C <= 0) {
     // one chunk per decode wave of the least-served KV head
@@ -202,10 +178,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   }
   const long long chunks = (total_keys + C - 1) / C;
 
+  // ---- piece length Tp: the mean tile count per prefill workgroup, but no
+  // less than the time a decode wave spends on its chunk (items shorter than
+  // that finish while the decode rows stream anyway, and cutting them only
+  // adds partials), doubled until the cut items' partials (J slots per item
+  // and KV head) fit ----
+  int Tp = 0x3FFFFFFF;  // never cut
+  if (a.pf_slots > 0 && a.part_tokens == 0 && item_tiles_all > 0) {
+    const long long w = a.pf_workers > 0 ? a.pf_workers : 1;
+    long long t0 = (item_tiles_all * a.Hkv + w - 1) / w;
+    if (total_keys > 0) t0 = max(t0, (long long)(C + kDecodeKeysPerTile - 1) / kDecodeKeysPerTile);
+    Tp = (int)(t0 < kMinPieceTiles ? kMinPieceTiles : (t0 > kCostBins ? kCostBins : t0));
+    for (int tries = 0;; ++tries) {
+      long long need = 0;
+      for (int b = lane; b <= maxt; b += 64) {
+        const int J = item_pieces(b, Tp);
+        if (J > 1) need += (long long)s_hist[b] * J;
+      }
+      if (wave_sum(need) * a.Hkv <= a.pf_slots) break;
+      if (tries >= 12) {
+        Tp = 0x3FFFFFFF;
+        break;
+      }
+      Tp *= 2;
+    }
+  }
+
   // ---- pass 2: decode rows, their offsets on the key axis, chunk starts ----
   int row_base = 0, off_base = 0;
-  for (int c0 = 0; c0 < a.S; c0 += kPlanThreads) {
-    const int s = c0 + tid;
+  for (int c0 = 0; c0 < a.S; c0 += 64) {
+    const int s = c0 + lane;
     SeqShape sh{0, 0, 0};
     int is_dec = 0, pad = 0;
     if (s < a.S) {
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
       }
     }
     int nrows, npad;
-    const int ri = row_base + block_exclusive_scan(is_dec, s_buf, &nrows);
-    const int off = off_base + block_exclusive_scan(pad, s_buf, &npad);
+    const int ri = row_base + wave_excl_scan(is_dec, &nrows);
+    const int off = off_base + wave_excl_scan(pad, &npad);
     if (s < a.S) {
       int np = 0;
       if (is_dec) {
@@ -236,68 +238,58 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
 
   // ---- entries per cost bin: piece j of an item of t tiles cut into J has
   // (j + 1) t / J - j t / J tiles ----
-  for (int i = tid; i < kCostBins; i += kPlanThreads) s_hist[i] = 0;
+  for (int b = lane; b <= maxt; b += 64) s_hist[b] = 0;
   __syncthreads();
-  for (int s = wid; s < a.S; s += kPlanWaves) {
-    const SeqShape sh = shape(s);
-    if (sh.L > 1 && sh.n >= sh.L) {
-      const int ntiles = (sh.L + TM - 1) / TM;
-      for (int mt = lane; mt < ntiles; mt += 64) {
-        const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
-        for (int j = 0; j < J; ++j) atomicAdd(&s_hist[(j + 1) * t / J - j * t / J], 1);
-      }
+  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
+    const int ntiles = (sh.L + TM - 1) / TM;
+    for (int mt = lane; mt < ntiles; mt += 64) {
+      const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
+      for (int j = 0; j < J; ++j) atomicAdd(&s_hist[(j + 1) * t / J - j * t / J], 1);
     }
-  }
+  });
   __syncthreads();
 
   // ---- bin offsets in decreasing cost: bin b starts after all bins > b ----
   int pf_total = 0;
-  // (kCostBins = 2 * kPlanThreads: each thread owns bins 2t and 2t+1 of the
-  // reversed order)
-  {
-    const int r0 = 2 * tid, r1 = 2 * tid + 1;  // positions in decreasing-cost order
-    const int b0 = kCostBins - 1 - r0, b1 = kCostBins - 1 - r1;
-    const int h0 = s_hist[b0], h1 = s_hist[b1];
-    const int off = block_exclusive_scan(h0 + h1, s_buf, &pf_total);
-    s_cur[b0] = off;
-    s_cur[b1] = off + h0;
+  for (int r0 = 0; r0 <= maxt; r0 += 64) {
+    const int r = r0 + lane, b = maxt - r;  // r-th bin in decreasing cost order
+    const int h = r <= maxt ? s_hist[b] : 0;
+    int tot;
+    const int off = pf_total + wave_excl_scan(h, &tot);
+    if (r <= maxt) s_cur[b] = off;
+    pf_total += tot;
   }
   __syncthreads();
 
-  // ---- pass 3: scatter the prefill entries into their bins (wave per
-  // sequence); a cut item takes J * Hkv partial slots ----
-  for (int s = wid; s < a.S; s += kPlanWaves) {
-    const SeqShape sh = shape(s);
-    if (sh.L > 1 && sh.n >= sh.L) {
-      const int ntiles = (sh.L + TM - 1) / TM;
-      for (int mt = lane; mt < ntiles; mt += 64) {
-        const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
-        int slot = 0;
-        if (J > 1) {
-          slot = atomicAdd(&s_slot_next, J * a.Hkv);
-          const int m = atomicAdd(&s_merge_next, 1);
-          if (m < cap_pf) merge_items[m] = make_int4(s, mt, J, slot);
-        }
-        for (int j = 0; j < J; ++j) {
-          const int idx = atomicAdd(&s_cur[(j + 1) * t / J - j * t / J], 1);
-          if (idx < cap_pf) pf_items[idx] = make_int4(s, mt, j | (J << 16), slot);
-        }
+  // ---- scatter the prefill entries into their bins; a cut item takes
+  // J * Hkv partial slots ----
+  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
+    const int ntiles = (sh.L + TM - 1) / TM;
+    for (int mt = lane; mt < ntiles; mt += 64) {
+      const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
+      int slot = 0;
+      if (J > 1) {
+        slot = atomicAdd(&s_slot_next, J * a.Hkv);
+        const int m = atomicAdd(&s_merge_next, 1);
+        if (m < cap_pf) merge_items[m] = make_int4(s, mt, J, slot);
+      }
+      for (int j = 0; j < J; ++j) {
+        const int idx = atomicAdd(&s_cur[(j + 1) * t / J - j * t / J], 1);
+        if (idx < cap_pf) pf_items[idx] = make_int4(s, mt, j | (J << 16), slot);
       }
     }
-  }
+  });
   __syncthreads();
-  if (tid == 0) {
+  if (lane == 0) {
     plan[0] = row_base;
     plan[1] = min(pf_total, cap_pf);
     plan[2] = C;
     plan[3] = (int)(chunks < cap_dec ? chunks : cap_dec);
     plan[4] = A;
     plan[5] = min(s_merge_next, cap_pf);
-    for (int i = 6; i < kPlanLine; ++i) plan[i] = 0;
   }
-  for (int h = tid; h < a.Hkv; h += kPlanThreads) {
-    plan[plan_pf_cursor(h)] = 0;
-  }
+  for (int i = 6 + lane; i < kPlanLine; i += 64) plan[i] = 0;
+  for (int h = lane; h < a.Hkv; h += 64) plan[plan_pf_cursor(h)] = 0;
 }
 
 }  // namespace

@@ -55,10 +55,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     // derived from it stay in scalar registers with scalar branches
     int it = __builtin_amdgcn_readfirstlane(pf_take(cursor, &s_next));
     while (it < n_items) {
-      // claim the next item now: the atomic's latency hides behind this one
-      int next = 0;
-      if (threadIdx.x == 0)
-        next = __hip_atomic_fetch_add(cursor, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // (the next entry is claimed only once this one is done: claimed ahead,
+      // the last entries sat with busy workgroups while the decode workers,
+      // done with their rows, found the queues empty)
       // Prefill waves issue ahead of the decode waves sharing their CU: a
       // prefill tile stalls the whole workgroup at its barriers when its
       // loads or MFMAs wait, while the decode waves' deep load queues absorb
@@ -66,10 +65,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       __builtin_amdgcn_s_setprio(2);
       prefill_item<D, G>(a, sm, items[it], kvh);
       __builtin_amdgcn_s_setprio(0);
-      if (threadIdx.x == 0) s_next = next;
-      __syncthreads();
-      it = __builtin_amdgcn_readfirstlane(s_next);
-      __syncthreads();
+      it = __builtin_amdgcn_readfirstlane(pf_take(cursor, &s_next));
     }
   }
 }
