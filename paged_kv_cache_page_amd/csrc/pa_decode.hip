@@ -361,6 +361,8 @@ __device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int t
 
 template <typename ET, int D, int G, bool TOKEN_MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+  // bf16: each wave's K staging region (see mfma_load)
+  __shared__ uint4 s_kreg[ET::kBytes == 2 ? kWaves * kbuf_units<(D >= 64 ? D : 64)>() : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (TOKEN_MODE) {
     const long unit = (long)blockIdx.x * kWaves + wave;
@@ -375,14 +377,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     if (part >= nparts) return;
     const int kbeg = part * PT;
     if constexpr (ET::kBytes == 2)
-      decode_segment_mfma<D, G, kDecodeBufs>(a, ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part,
-                                nparts, kvh, true);
+    {
+      const DecSeg d{ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part, nparts, kvh};
+      decode_segment_mfma<D, G, kDecodeBufs>(a, d, decode_prefetch<D, G>(a, d), true,
+                                             s_kreg + wave * kbuf_units<D>());
+    }
     else
       decode_segment<ET, D, G, true>(a, ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part,
                                      nparts, kvh);
   } else {
     if constexpr (ET::kBytes == 2) {
-      decode_chunks_mfma<D, G>(a, blockIdx.x, gridDim.x);
+      decode_chunks_mfma<D, G>(a, blockIdx.x, gridDim.x, s_kreg);
     } else {
       decode_walk(a, blockIdx.x, gridDim.x,
                   [&](int seq, int token, int wrow, int kbeg, int kend, int part, int nparts,

@@ -115,39 +115,74 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
   }
 }
 
-// Walk of decode worker `wg` of `n_wg` (workgroups of 4 waves) over the
-// chunks of the decode key axis the plan kernel cut (see pa_plan.hip). Wave
-// gw = 4 wg + wave serves KV head gw % Hkv: the four waves of a workgroup
-// serve different heads, so every XCD streams several heads' rows at once
-// (one head per workgroup measured slower). The waves of a head take its
-// chunks in turn; for every chunk the wave calls
-// seg(seq, token, wrow, kbeg, kend, part, nparts, kvh) on the part of each row
-// the chunk covers.
-template <typename Seg>
-__device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, int n_wg, Seg&& seg) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
-  const int4* rows = reinterpret_cast<const int4*>(a.plan + po.rows);
-  const int* first_row = a.plan + po.first_row;
-  const int n_rows = a.plan[0], C = a.plan[2], n_chunks = a.plan[3], A = a.plan[4];
-  const int Hkv = a.Hkv;
-  const int gw = wg * 4 + wave;
-  const int kvh = gw % Hkv;
-  const int n_head = (n_wg * 4 - kvh + Hkv - 1) / Hkv;  // waves serving this head
-  for (int chunk = gw / Hkv; chunk < n_chunks; chunk += n_head) {
-    const int c0 = chunk * C, c1 = c0 + C;
-    for (int i = first_row[chunk];; ++i) {
-      const int4 r = rows[i];  // (sequence, offset, keys, token)
+// One range of a decode row handled by one wave: keys [kbeg, kend) of
+// sequence seq for query row token (row wrow of the split-KV workspace),
+// partition part of the row's nparts, KV head kvh.
+struct DecSeg {
+  int seq, token, wrow, kbeg, kend, part, nparts, kvh;
+};
+
+// Walk of decode wave gw = 4 wg + wave over the chunks of the decode key axis
+// the plan kernel cut (see pa_plan.hip). Wave gw serves KV head gw % Hkv: the
+// four waves of a workgroup serve different heads, so every XCD streams
+// several heads' rows at once (one head per workgroup measured slower). The
+// waves of a head take its chunks in turn; next() yields the part of every row
+// each chunk covers.
+struct DecodeCursor {
+  const int4* rows;  // (sequence, offset, keys, token) per decode row
+  const int* first_row;
+  int n_rows, C, n_chunks, A, n_head, kvh, chunk, i;
+
+  __device__ __forceinline__ DecodeCursor(const AttnArgs& a, int wg, int n_wg) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
+    rows = reinterpret_cast<const int4*>(a.plan + po.rows);
+    first_row = a.plan + po.first_row;
+    n_rows = a.plan[0];
+    C = a.plan[2];
+    n_chunks = a.plan[3];
+    A = a.plan[4];
+    const int gw = wg * 4 + wave;
+    kvh = gw % a.Hkv;
+    n_head = (n_wg * 4 - kvh + a.Hkv - 1) / a.Hkv;  // waves serving this head
+    chunk = gw / a.Hkv;
+    i = chunk < n_chunks ? first_row[chunk] : 0;
+  }
+
+  __device__ __forceinline__ bool next(DecSeg& d) {
+    while (chunk < n_chunks) {
+      const int4 r = rows[i];
       const int off = r.y, n = r.z;
       const int pad = (n + A - 1) / A * A;
-      const int kbeg = max(c0, off) - off;
-      const int kend = min(min(c1, off + pad) - off, n);
+      const int c0 = chunk * C, c1 = c0 + C;
       const int j0 = off / C;
-      const int nparts = (off + pad - 1) / C - j0 + 1;
-      if (kbeg < kend) seg(r.x, r.w, r.x, kbeg, kend, chunk - j0, nparts, kvh);
-      if (off + pad >= c1 || i + 1 >= n_rows) break;
+      d.seq = r.x;
+      d.token = r.w;
+      d.wrow = r.x;
+      d.kbeg = max(c0, off) - off;
+      d.kend = min(min(c1, off + pad) - off, n);
+      d.part = chunk - j0;
+      d.nparts = (off + pad - 1) / C - j0 + 1;
+      d.kvh = kvh;
+      if (off + pad >= c1 || i + 1 >= n_rows) {  // the chunk ends in this row
+        chunk += n_head;
+        if (chunk < n_chunks) i = first_row[chunk];
+      } else {
+        ++i;
+      }
+      if (d.kbeg < d.kend) return true;
     }
+    return false;
   }
+};
+
+// seg(seq, token, wrow, kbeg, kend, part, nparts, kvh) for every range of the
+// wave's chunks, in order.
+template <typename Seg>
+__device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, int n_wg, Seg&& seg) {
+  DecodeCursor cur(a, wg, n_wg);
+  DecSeg d;
+  while (cur.next(d)) seg(d.seq, d.token, d.wrow, d.kbeg, d.kend, d.part, d.nparts, d.kvh);
 }
 
 // ---------------------------------------------------------------------------
@@ -187,6 +222,25 @@ struct MfmaBuf {
   uint4 v[MfmaDecodeShape<D, G>::UNROLL];
 };
 
+// K rows of a 16-key buffer are loaded as whole 128-byte lines (8 lanes per
+// line, 8 keys per load instruction): loads laid out for the MFMA A operand
+// directly (16 keys x 64 bytes per instruction) streamed at ~4.8 TB/s against
+// ~6.3 TB/s for whole lines on MI355X. Load i of a lane holds key
+// 8 (i / (D / 64)) + lane / 8, 16-byte chunk 8 (i % (D / 64)) + lane % 8; the
+// wave passes the buffer through its own 16-key LDS region to put it in the
+// operand layout (mfma_compute). Unit (16 bytes) of key k, chunk c there:
+//   64 ((D / 64) (k / 8) + c / 8) + 8 (k % 8) + ((c % 8) ^ (k / 2) ^ 4 (k % 2)) % 8
+// Writes cover whole 128-byte runs, and the operand reads (lane l: key l % 16,
+// chunk 4 ks + l / 16) hit distinct banks whether 8 or 16 lanes are served a
+// cycle.
+template <int D>
+__device__ __forceinline__ int kbuf_unit(int k, int c) {
+  return 64 * ((D / 64) * (k >> 3) + (c >> 3)) + 8 * (k & 7) + (((c & 7) ^ (k >> 1) ^ ((k & 1) << 2)) & 7);
+}
+// 16-byte units of one wave's K region
+template <int D>
+constexpr int kbuf_units() { return 16 * D * 2 / 16; }
+
 // Issue the loads of the 16 keys starting at kb (as load_buf).
 template <int D, int G>
 __device__ __forceinline__ void mfma_load(MfmaBuf<D, G>& b, const char* kbase, const char* vbase,
@@ -198,7 +252,9 @@ __device__ __forceinline__ void mfma_load(MfmaBuf<D, G>& b, const char* kbase, c
   const size_t step_off = (((size_t)page << p_shift) + row0) * slot_stride;
   const char* kp = kbase + step_off + k_off;
 #pragma unroll
-  for (int ks = 0; ks < SH::KSTEPS; ++ks) b.k[ks] = *reinterpret_cast<const uint4*>(kp + 64 * ks);
+  for (int i = 0; i < SH::KSTEPS; ++i)
+    b.k[i] = *reinterpret_cast<const uint4*>(kp + (size_t)(8 * (i / (D / 64))) * slot_stride +
+                                             128 * (i % (D / 64)));
   const char* vp = vbase + step_off + v_off;
 #pragma unroll
   for (int u = 0; u < SH::UNROLL; ++u)
@@ -213,12 +269,29 @@ template <int D, int G>
 __device__ __forceinline__ void mfma_compute(MfmaBuf<D, G>& b, const uint4 (&qb)[D / 32],
                                              float& m_run, float& l_part, float (&o)[G][8],
                                              int kb, int kend, int rrow, int slot, float sl2e,
-                                             float bias) {
+                                             float bias, uint4* kreg) {
   typedef MfmaDecodeShape<D, G> SH;
+  // K through the wave's LDS region into the A-operand layout (lane l: key
+  // l % 16, dims 8 (l / 16) + 32 ks ..). Only this wave touches the region and
+  // its LDS accesses run in order, so no barrier is needed.
+  // (an explicit LDS pointer: through a generic one the compiler could not
+  // rule out aliasing with the register buffers and kept them in scratch)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  lds_u32x4* kl = (lds_u32x4*)kreg;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < SH::KSTEPS; ++i)
+    kl[kbuf_unit<D>(8 * (i / (D / 64)) + (lane >> 3), 8 * (i % (D / 64)) + (lane & 7))] =
+        __builtin_bit_cast(u32x4_t, b.k[i]);
+  uint4 kop[SH::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < SH::KSTEPS; ++ks)
+    kop[ks] = __builtin_bit_cast(uint4, kl[kbuf_unit<D>(lane & 15, 4 * ks + (lane >> 4))]);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[ks]),
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]),
                                                   __builtin_bit_cast(bf16x8_t, qb[ks]), acc, 0,
                                                   0, 0);
   // log2-domain scores; bias is -inf in the lanes of heads >= G
@@ -337,12 +410,44 @@ __device__ __forceinline__ float lane_sum_xor(float x) {
   }
 }
 
+// The loads a range needs before its first K/V buffer: the page ids of its
+// pages (lane i: the i-th) and the Q^T operand (head col's dims 8 rrow + 32 ks
+// ..). Issued for the next range while the current one streams, so a range
+// start waits only for its first K/V buffer. The values are used (clamped,
+// masked) only in decode_segment_mfma, so issuing them waits for nothing.
+template <int D, int G>
+struct DecPre {
+  int page_raw;
+  uint4 qb[MfmaDecodeShape<D, G>::KSTEPS];
+};
+
+template <int D, int G>
+__device__ __forceinline__ DecPre<D, G> decode_prefetch(const AttnArgs& a, const DecSeg& d) {
+  typedef MfmaDecodeShape<D, G> SH;
+  DecPre<D, G> p;
+  const int lane = threadIdx.x & 63;
+  const int rrow = lane >> 4, col = lane & 15;
+  const int pg0 = d.kbeg >> a.p_shift;
+  const int npg = ((d.kend - 1) >> a.p_shift) - pg0 + 1;
+  const int* bt_row = a.block_tables + (size_t)d.seq * a.max_blocks;
+  p.page_raw = bt_row[pg0 + (lane < npg ? lane : 0)];
+  const size_t row_bytes = (size_t)SH::ROWB;
+  const char* qrow = (const char*)a.q + ((size_t)d.token * a.Hq + (size_t)d.kvh * G) * row_bytes;
+  const int hq = col < G ? col : 0;
+#pragma unroll
+  for (int ks = 0; ks < SH::KSTEPS; ++ks)
+    p.qb[ks] = *reinterpret_cast<const uint4*>(qrow + hq * row_bytes + 16 * rrow + 64 * ks);
+  return p;
+}
+
 template <int D, int G, int NBUF>
-__device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, int seq, int token,
-                                                    int wrow, int kbeg, int kend, int part,
-                                                    int nparts, int kvh, bool token_mode) {
+__device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, const DecSeg& d,
+                                                    const DecPre<D, G>& pre, bool token_mode,
+                                                    uint4* kreg) {
   typedef MfmaDecodeShape<D, G> SH;
   constexpr int LPK = SH::LPK, NSLOT = SH::NSLOT;
+  const int token = d.token, wrow = d.wrow, kbeg = d.kbeg, kend = d.kend, part = d.part;
+  const int nparts = d.nparts, kvh = d.kvh;
   const int lane = threadIdx.x & 63;
   const int rrow = lane >> 4, col = lane & 15;  // score layout: keys 4 rrow.., head col
   const int slot = lane / LPK, sub = lane % LPK;  // V layout
@@ -350,21 +455,14 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, int seq, 
 
   const int pg0 = kbeg >> p_shift;
   const int npg = ((kend - 1) >> p_shift) - pg0 + 1;
-  const int* bt_row = a.block_tables + (size_t)seq * a.max_blocks;
-  const int page_reg = lane < npg ? clampi(bt_row[pg0 + lane], 0, a.num_pages - 1) : 0;
+  const int page_reg = lane < npg ? clampi(pre.page_raw, 0, a.num_pages - 1) : 0;
 
-  // Q^T operand: head col's dims 8 rrow + 32 ks ..
+  // Q^T operand, zero in the lanes of heads >= G
   const size_t row_bytes = (size_t)SH::ROWB;
   uint4 qb[SH::KSTEPS];
-  {
-    const char* qrow = (const char*)a.q + ((size_t)token * a.Hq + (size_t)kvh * G) * row_bytes;
-    const int hq = col < G ? col : 0;
 #pragma unroll
-    for (int ks = 0; ks < SH::KSTEPS; ++ks) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qrow + hq * row_bytes + 16 * rrow + 64 * ks);
-      qb[ks] = col < G ? x : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
+  for (int ks = 0; ks < SH::KSTEPS; ++ks)
+    qb[ks] = col < G ? pre.qb[ks] : make_uint4(0u, 0u, 0u, 0u);
   const float bias = col < G ? 0.f : -INFINITY;
 
   float m_run = kNegBig, l_part = 0.f;
@@ -377,7 +475,7 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, int seq, 
   const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes;
   const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes;
   const size_t slot_stride = (size_t)a.Hkv * row_bytes;
-  const uint32_t k_off = (uint32_t)(col * slot_stride) + 16 * rrow;
+  const uint32_t k_off = (uint32_t)((lane >> 3) * slot_stride) + 16 * (lane & 7);
   const uint32_t v_off = (uint32_t)(slot * SH::UNROLL * slot_stride) + 16 * sub;
   const float sl2e = a.scale_log2e;
 
@@ -402,7 +500,7 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, int seq, 
       __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this compute
       if (j < nbuf)
         mfma_compute<D, G>(buf[p], qb, m_run, l_part, o, kbeg + 16 * j, kend, rrow, slot, sl2e,
-                           bias);
+                           bias, kreg);
     }
   }
 
@@ -460,14 +558,27 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, int seq, 
 }
 
 
+// The decode ranges of wave gw, each range's page ids and Q issued while the
+// previous range streams. lds: kbuf_units<D>() 16-byte units per wave of the
+// workgroup (wave w uses the w-th block).
 template <int D, int G>
-__device__ __forceinline__ void decode_chunks_mfma(const AttnArgs& a, int wg, int n_wg) {
-  decode_walk(a, wg, n_wg,
-              [&](int seq, int token, int wrow, int kbeg, int kend, int part, int nparts,
-                  int kvh) {
-                decode_segment_mfma<D, G, kDecodeBufs>(a, seq, token, wrow, kbeg, kend, part,
-                                                       nparts, kvh, false);
-              });
+__device__ __forceinline__ void decode_chunks_mfma(const AttnArgs& a, int wg, int n_wg,
+                                                   uint4* lds) {
+  uint4* kreg = lds + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kbuf_units<D>();
+  DecodeCursor cur(a, wg, n_wg);
+  DecSeg d;
+  if (!cur.next(d)) return;
+  DecPre<D, G> p = decode_prefetch<D, G>(a, d);
+  for (;;) {
+    DecSeg dn;
+    const bool more = cur.next(dn);
+    DecPre<D, G> pn;
+    if (more) pn = decode_prefetch<D, G>(a, dn);
+    decode_segment_mfma<D, G, kDecodeBufs>(a, d, p, false, kreg);
+    if (!more) break;
+    d = dn;
+    p = pn;
+  }
 }
 
 }  // namespace pa

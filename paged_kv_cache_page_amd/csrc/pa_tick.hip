@@ -42,7 +42,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ PfSmem<D> sm;
   __shared__ int s_next;
   static_assert(kPfThreads == 64 * 4, "decode workers are workgroups of four waves");
-  if ((int)blockIdx.x < a.dec_grid) decode_chunks_mfma<D, G>(a, blockIdx.x, a.dec_grid);
+  // decode workers stage K in the (not yet used) prefill tile buffers
+  static_assert(sizeof(sm.k) >= 4 * kbuf_units<D>() * sizeof(uint4), "decode K staging fits");
+  if ((int)blockIdx.x < a.dec_grid)
+    decode_chunks_mfma<D, G>(a, blockIdx.x, a.dec_grid, reinterpret_cast<uint4*>(sm.k));
 
   const int4* items = reinterpret_cast<const int4*>(a.plan + plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf).pf);
   const int n_items = a.plan[1];
