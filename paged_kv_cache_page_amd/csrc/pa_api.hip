@@ -143,6 +143,7 @@ bool use_mfma_prefill(pa_dtype_t dt, int D, int max_query_len) {
 struct WsLayout {
   long cap_dec, cap_pf;
   size_t plan_bytes, partial_bytes, pf_bytes;
+  long part_slots;
   int max_parts, pf_slots;
   bool token_mode;
 };
@@ -168,6 +169,9 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
   w.plan_bytes = 0;
   w.pf_slots = 0;
   w.pf_bytes = 0;
+  // partial slots: at most max_parts per row (packed by the plan kernel in
+  // seq mode: a row has one partition per chunk it overlaps)
+  w.part_slots = (long)(w.token_mode ? T : S) * w.max_parts;
   if (!w.token_mode) {
     w.cap_dec = (long)S * w.max_parts;
     if (max_query_len > 1) {
@@ -187,8 +191,7 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
     }
     w.plan_bytes = (plan_offsets(S, Hq, w.cap_dec, w.cap_pf).total * sizeof(int) + 255) / 256 * 256;
   }
-  const long rows = w.token_mode ? T : S;
-  w.partial_bytes = w.max_parts > 1 ? ((size_t)rows * (size_t)w.max_parts * (size_t)Hq *
+  w.partial_bytes = w.max_parts > 1 ? ((size_t)w.part_slots * (size_t)Hq *
                                            ((size_t)D + 2) * sizeof(float) + 255) / 256 * 256
                                     : 0;
   return w;
@@ -315,7 +318,8 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   const size_t need = wl.plan_bytes + wl.partial_bytes + wl.pf_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && ((uintptr_t)workspace & 255u)) return PA_ERR_INVALID_ARG;
-  if (wl.cap_dec > INT32_MAX / 2 || wl.cap_pf > INT32_MAX / 2) return PA_ERR_INVALID_ARG;
+  if (wl.cap_dec > INT32_MAX / 2 || wl.cap_pf > INT32_MAX / 2 || wl.part_slots > INT32_MAX / 2)
+    return PA_ERR_INVALID_ARG;
   // decode rows are laid end to end on one int32 key axis (rows padded to at
   // most one partition)
   if (!wl.token_mode &&
@@ -351,6 +355,7 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.part_min = split_min(page_size);
   a.part_max = split_max(page_size);
   a.max_parts = wl.max_parts;
+  a.part_slots = (int32_t)wl.part_slots;
   a.dec_grid = wl.token_mode ? 0 : decode_grid(dtype, head_dim, G);
   a.scale_log2e = scale * kLog2e;
   a.pf_slots = wl.pf_slots;

@@ -233,9 +233,9 @@ __device__ __forceinline__ void merge_slots(float (&m)[G], float (&lsum)[G],
 
 // One work item, run by one wave: keys [kbeg, kend) (kbeg a multiple of 16,
 // kend > kbeg) of sequence `seq` for query row `token`, one KV head. Range
-// `part` of the row's `nparts`; partials go to workspace row `wrow`.
+// `part` of the row's `nparts`; its partials go to slot pslot + part.
 template <typename ET, int D, int G, bool TOKEN_MODE>
-__device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int token, int wrow,
+__device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int token, int pslot,
                                                int kbeg, int kend, int part, int nparts,
                                                int kvh) {
   typedef DecodeShape<ET, D> SH;
@@ -345,14 +345,14 @@ __device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int t
                           o[g][4 * l + 3] * inv);
       }
     } else {
-      const size_t pi = ((size_t)wrow * a.max_parts + part) * a.Hq + h;
+      const size_t pi = ((size_t)pslot + part) * a.Hq + h;
       float* po = a.ws + pi * D;
 #pragma unroll
       for (int i = 0; i < DPL; i += 4)
         *reinterpret_cast<float4*>(po + SH::dim_of(sub, i)) =
             make_float4(o[g][i], o[g][i + 1], o[g][i + 2], o[g][i + 3]);
       if (sub == 0) {
-        float* ml = a.ws + (size_t)(TOKEN_MODE ? a.T : a.S) * a.max_parts * a.Hq * D;
+        float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
         *reinterpret_cast<float2*>(ml + 2 * pi) = make_float2(m[g], lsum[g]);
       }
     }
@@ -378,21 +378,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     const int kbeg = part * PT;
     if constexpr (ET::kBytes == 2)
     {
-      const DecSeg d{ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part, nparts, kvh};
-      decode_segment_mfma<D, G, kDecodeBufs>(a, d, decode_prefetch<D, G>(a, d), true,
-                                             s_kreg + wave * kbuf_units<D>());
+      const DecSeg d{ri.seq, row, row * a.max_parts, kbeg, min(ri.n_eff, kbeg + PT), part,
+                     nparts, kvh};
+      decode_range_alone<D, G>(a, d, s_kreg + wave * kbuf_units<D>());
     }
     else
-      decode_segment<ET, D, G, true>(a, ri.seq, row, row, kbeg, min(ri.n_eff, kbeg + PT), part,
-                                     nparts, kvh);
+      decode_segment<ET, D, G, true>(a, ri.seq, row, row * a.max_parts, kbeg,
+                                     min(ri.n_eff, kbeg + PT), part, nparts, kvh);
   } else {
     if constexpr (ET::kBytes == 2) {
       decode_chunks_mfma<D, G>(a, blockIdx.x, gridDim.x, s_kreg);
     } else {
       decode_walk(a, blockIdx.x, gridDim.x,
-                  [&](int seq, int token, int wrow, int kbeg, int kend, int part, int nparts,
+                  [&](int seq, int token, int pslot, int kbeg, int kend, int part, int nparts,
                       int kvh) {
-                    decode_segment<ET, D, G, false>(a, seq, token, wrow, kbeg, kend, part, nparts,
+                    decode_segment<ET, D, G, false>(a, seq, token, pslot, kbeg, kend, part, nparts,
                                                     kvh);
                   });
     }

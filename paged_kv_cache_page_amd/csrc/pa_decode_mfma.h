@@ -8,12 +8,10 @@
 
 namespace pa {
 
-// bf16 decode: register buffers per wave (16 keys each) and resident
-// workgroups per CU. One workgroup per CU keeps the waves of a CU the same
-// age: the wave arbiter favours older waves, and with several workgroups per
-// CU the younger ones' loads queue behind the older ones' and the kernel ends
-// on a tail of late waves. The deeper ring keeps enough bytes in flight.
-constexpr int kDecodeBufs = 2;
+// bf16 decode: resident workgroups per CU. One workgroup per CU keeps the
+// waves of a CU the same age: the wave arbiter favours older waves, and with
+// several workgroups per CU the younger ones' loads queue behind the older
+// ones' and the kernel ends on a tail of late waves.
 constexpr int kDecodeWgPerCu = 1;
 
 // Which row a work item serves, and that row's key limit.
@@ -73,21 +71,26 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
   const long row = rh / a.Hq;
   if (row >= (TOKEN_MODE ? a.T : a.S)) return;
   int nparts, token;
+  size_t slot0;  // partial slot of part 0
   if constexpr (TOKEN_MODE) {
     const RowInfo ri = row_info<true>(a, (int)row);
     if (!ri.active) return;
     nparts = (ri.n_eff + a.part_tokens - 1) / a.part_tokens;
+    nparts = min(nparts, a.max_parts);
     token = (int)row;
+    slot0 = (size_t)row * a.max_parts;
   } else {
-    nparts = a.plan[plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf).nparts + row];
+    // row = decode row of the plan
+    if (row >= a.plan[0]) return;
+    const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
+    nparts = a.plan[po.nparts + row];
     if (nparts <= 1) return;
-    token = a.qsl[row];
+    token = reinterpret_cast<const int4*>(a.plan + po.rows)[row].w;
+    slot0 = (size_t)a.plan[po.pbase + row];
   }
   if (nparts <= 1) return;
-  nparts = min(nparts, a.max_parts);
-  const long rows = TOKEN_MODE ? a.T : a.S;
-  const float* ml = a.ws + (size_t)rows * a.max_parts * a.Hq * D;
-  const size_t p0 = (size_t)row * a.max_parts * a.Hq + h;  // partial index of part 0
+  const float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
+  const size_t p0 = slot0 * a.Hq + h;  // partial index of part 0
   float mn = kNegBig;
   for (int k = 0; k < nparts; ++k) mn = fmaxf(mn, ml[2 * (p0 + (size_t)k * a.Hq)]);
   float lt = 0.f;
@@ -116,73 +119,114 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
 }
 
 // One range of a decode row handled by one wave: keys [kbeg, kend) of
-// sequence seq for query row token (row wrow of the split-KV workspace),
-// partition part of the row's nparts, KV head kvh.
+// sequence seq for query row token, partition part of the row's nparts (its
+// partials at slot pslot + part of the split-KV workspace), KV head kvh.
 struct DecSeg {
-  int seq, token, wrow, kbeg, kend, part, nparts, kvh;
+  int seq, token, pslot, kbeg, kend, part, nparts, kvh;
 };
 
 // Walk of decode wave gw = 4 wg + wave over the chunks of the decode key axis
-// the plan kernel cut (see pa_plan.hip). Wave gw serves KV head gw % Hkv: the
-// four waves of a workgroup serve different heads, so every XCD streams
-// several heads' rows at once (one head per workgroup measured slower). The
-// waves of a head take its chunks in turn; next() yields the part of every row
-// each chunk covers.
+// the plan kernel cut (see pa_plan.hip). Wave gw first takes chunk gw / Hkv
+// of KV head gw % Hkv (the four waves of a workgroup serve different heads, so
+// every XCD streams several heads' rows at once); chunks past one per wave
+// are items t = (chunk, KV head) claimed from one shared counter, t -> head
+// t % Hkv, chunk n_static + t / Hkv, until they run out. Each claim is issued one
+// chunk ahead, so its atomic returns while the wave streams. next() yields the
+// part of every row each chunk covers.
 struct DecodeCursor {
-  const int4* rows;  // (sequence, offset, keys, token) per decode row
-  const int* first_row;
-  int n_rows, C, n_chunks, A, n_head, kvh, chunk, i;
+  const int4* rows;       // (sequence, offset, keys, token) per decode row
+  const int* first_row;   // first row of each chunk
+  const int* nparts_of;   // partitions per row
+  const int* pbase_of;    // first partial slot per row
+  int* counter;           // claimed items
+  int n_rows, C, n_chunks, n_static, n_items, A, Hkv, kvh, chunk, i;
+  int claim;   // item claimed ahead (lane 0)
+  bool ended;  // the last range yielded ended its chunk
+
+  __device__ __forceinline__ void claim_next() {
+    claim = n_items;
+    if (n_items > 0 && (threadIdx.x & 63) == 0)
+      claim = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Move to the claimed item (or past the last chunk when none is left).
+  __device__ __forceinline__ void take_claim() {
+    const int t = __builtin_amdgcn_readfirstlane(claim);
+    if (t < n_items) {
+      kvh = t % Hkv;
+      chunk = n_static + t / Hkv;
+      i = first_row[chunk];
+      claim_next();
+    } else {
+      chunk = n_chunks;
+    }
+  }
 
   __device__ __forceinline__ DecodeCursor(const AttnArgs& a, int wg, int n_wg) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
     rows = reinterpret_cast<const int4*>(a.plan + po.rows);
     first_row = a.plan + po.first_row;
+    nparts_of = a.plan + po.nparts;
+    pbase_of = a.plan + po.pbase;
+    counter = a.plan + plan_dec_cursor(a.Hq);
     n_rows = a.plan[0];
     C = a.plan[2];
     n_chunks = a.plan[3];
     A = a.plan[4];
+    n_static = a.plan[6];
+    n_items = a.plan[7];
+    Hkv = a.Hkv;
+    (void)n_wg;
     const int gw = wg * 4 + wave;
-    kvh = gw % a.Hkv;
-    n_head = (n_wg * 4 - kvh + a.Hkv - 1) / a.Hkv;  // waves serving this head
-    chunk = gw / a.Hkv;
-    i = chunk < n_chunks ? first_row[chunk] : 0;
+    kvh = gw % Hkv;
+    chunk = gw / Hkv;
+    i = 0;
+    ended = false;
+    claim_next();
+    if (chunk < n_static)
+      i = first_row[chunk];
+    else
+      take_claim();
   }
 
+  // (A chunk's end is acted on at the following call, so the claim taken
+  // there has had a whole range's time to return.)
   __device__ __forceinline__ bool next(DecSeg& d) {
-    while (chunk < n_chunks) {
+    for (;;) {
+      if (ended) {
+        take_claim();
+        ended = false;
+      }
+      if (chunk >= n_chunks) return false;
       const int4 r = rows[i];
+      const int np = nparts_of[i], pb = pbase_of[i];
       const int off = r.y, n = r.z;
       const int pad = (n + A - 1) / A * A;
       const int c0 = chunk * C, c1 = c0 + C;
-      const int j0 = off / C;
       d.seq = r.x;
       d.token = r.w;
-      d.wrow = r.x;
+      d.pslot = pb;
       d.kbeg = max(c0, off) - off;
       d.kend = min(min(c1, off + pad) - off, n);
-      d.part = chunk - j0;
-      d.nparts = (off + pad - 1) / C - j0 + 1;
+      d.part = chunk - off / C;
+      d.nparts = np;
       d.kvh = kvh;
-      if (off + pad >= c1 || i + 1 >= n_rows) {  // the chunk ends in this row
-        chunk += n_head;
-        if (chunk < n_chunks) i = first_row[chunk];
-      } else {
+      if (off + pad >= c1 || i + 1 >= n_rows)  // the chunk ends in this row
+        ended = true;
+      else
         ++i;
-      }
       if (d.kbeg < d.kend) return true;
     }
-    return false;
   }
 };
 
-// seg(seq, token, wrow, kbeg, kend, part, nparts, kvh) for every range of the
+// seg(seq, token, pslot, kbeg, kend, part, nparts, kvh) for every range of the
 // wave's chunks, in order.
 template <typename Seg>
 __device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, int n_wg, Seg&& seg) {
   DecodeCursor cur(a, wg, n_wg);
   DecSeg d;
-  while (cur.next(d)) seg(d.seq, d.token, d.wrow, d.kbeg, d.kend, d.part, d.nparts, d.kvh);
+  while (cur.next(d)) seg(d.seq, d.token, d.pslot, d.kbeg, d.kend, d.part, d.nparts, d.kvh);
 }
 
 // ---------------------------------------------------------------------------
@@ -241,24 +285,67 @@ __device__ __forceinline__ int kbuf_unit(int k, int c) {
 template <int D>
 constexpr int kbuf_units() { return 16 * D * 2 / 16; }
 
-// Issue the loads of the 16 keys starting at kb (as load_buf).
+// Where a range's 16-key buffers come from.
+struct DecSrc {
+  const char* kbase;  // K pool + the KV head's offset within a slot
+  const char* vbase;
+  int page_raw;       // lane i: block-table entry of the range's i-th page (unchecked)
+  int pg0;            // the range's first page
+  int kbeg;           // first key (a multiple of 16)
+  int nbuf;           // 16-key buffers (>= 1)
+};
+
+// Per-lane offsets of the K and V loads within a 16-key buffer.
+struct DecLane {
+  size_t slot_stride;  // bytes between consecutive slots of a page
+  uint32_t k_off, v_off;
+};
+
 template <int D, int G>
-__device__ __forceinline__ void mfma_load(MfmaBuf<D, G>& b, const char* kbase, const char* vbase,
-                                          int page_reg, int pg0, int p_shift, size_t slot_stride,
-                                          int kb, uint32_t k_off, uint32_t v_off) {
+__device__ __forceinline__ DecLane dec_lane(const AttnArgs& a) {
   typedef MfmaDecodeShape<D, G> SH;
-  const int page = __builtin_amdgcn_readlane(page_reg, (kb >> p_shift) - pg0);
-  const int row0 = kb & ((1 << p_shift) - 1);
-  const size_t step_off = (((size_t)page << p_shift) + row0) * slot_stride;
-  const char* kp = kbase + step_off + k_off;
+  const int lane = threadIdx.x & 63;
+  const int slot = lane / SH::LPK, sub = lane % SH::LPK;
+  DecLane l;
+  l.slot_stride = (size_t)a.Hkv * SH::ROWB;
+  l.k_off = (uint32_t)((lane >> 3) * l.slot_stride) + 16 * (lane & 7);
+  l.v_off = (uint32_t)(slot * SH::UNROLL * l.slot_stride) + 16 * sub;
+  return l;
+}
+
+template <int D, int G>
+__device__ __forceinline__ DecSrc dec_src(const AttnArgs& a, const DecSeg& d, int page_raw) {
+  typedef MfmaDecodeShape<D, G> SH;
+  DecSrc s;
+  s.kbase = (const char*)a.k_pool + (size_t)d.kvh * SH::ROWB;
+  s.vbase = (const char*)a.v_pool + (size_t)d.kvh * SH::ROWB;
+  s.page_raw = page_raw;
+  s.pg0 = d.kbeg >> a.p_shift;
+  s.kbeg = d.kbeg;
+  s.nbuf = (d.kend - d.kbeg + 15) / 16;
+  return s;
+}
+
+// Issue the loads of buffer x of range s (past its end: its last buffer). A
+// 16-key buffer never crosses a page (kbeg is a multiple of 16, P >= 16).
+template <int D, int G>
+__device__ __forceinline__ void mfma_load(MfmaBuf<D, G>& b, const AttnArgs& a, const DecSrc& s,
+                                          int x, const DecLane& ln) {
+  typedef MfmaDecodeShape<D, G> SH;
+  const int kb = s.kbeg + 16 * min(x, s.nbuf - 1);
+  int page = __builtin_amdgcn_readlane(s.page_raw, (kb >> a.p_shift) - s.pg0);
+  page = min(max(page, 0), a.num_pages - 1);
+  const int row0 = kb & ((1 << a.p_shift) - 1);
+  const size_t step_off = (((size_t)page << a.p_shift) + row0) * ln.slot_stride;
+  const char* kp = s.kbase + step_off + ln.k_off;
 #pragma unroll
   for (int i = 0; i < SH::KSTEPS; ++i)
-    b.k[i] = *reinterpret_cast<const uint4*>(kp + (size_t)(8 * (i / (D / 64))) * slot_stride +
+    b.k[i] = *reinterpret_cast<const uint4*>(kp + (size_t)(8 * (i / (D / 64))) * ln.slot_stride +
                                              128 * (i % (D / 64)));
-  const char* vp = vbase + step_off + v_off;
+  const char* vp = s.vbase + step_off + ln.v_off;
 #pragma unroll
   for (int u = 0; u < SH::UNROLL; ++u)
-    b.v[u] = *reinterpret_cast<const uint4*>(vp + (size_t)u * slot_stride);
+    b.v[u] = *reinterpret_cast<const uint4*>(vp + (size_t)u * ln.slot_stride);
 }
 
 __device__ __forceinline__ uint32_t word_of4(const uint4& v, int w) {
@@ -414,7 +501,7 @@ __device__ __forceinline__ float lane_sum_xor(float x) {
 // pages (lane i: the i-th) and the Q^T operand (head col's dims 8 rrow + 32 ks
 // ..). Issued for the next range while the current one streams, so a range
 // start waits only for its first K/V buffer. The values are used (clamped,
-// masked) only in decode_segment_mfma, so issuing them waits for nothing.
+// masked) only in decode_range, so issuing them waits for nothing.
 template <int D, int G>
 struct DecPre {
   int page_raw;
@@ -440,25 +527,25 @@ __device__ __forceinline__ DecPre<D, G> decode_prefetch(const AttnArgs& a, const
   return p;
 }
 
-template <int D, int G, int NBUF>
-__device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, const DecSeg& d,
-                                                    const DecPre<D, G>& pre, bool token_mode,
-                                                    uint4* kreg) {
+// One decode range on a wave. b0 holds (its loads issued) buffer 0 of the
+// range; the two register buffers alternate, the loads of the next buffer in
+// flight while one computes. The range's last step loads buffer 0 of the next
+// range sn into the other buffer, so the stream does not drain between
+// ranges (after the last range, sn is the range itself: a re-read of one
+// buffer). That is b1 when the range has an odd number of buffers: the
+// caller then passes the buffers swapped for the next range.
+template <int D, int G>
+__device__ __forceinline__ void decode_range(const AttnArgs& a, MfmaBuf<D, G>& b0,
+                                             MfmaBuf<D, G>& b1, const DecSeg& d,
+                                             const DecPre<D, G>& pre, const DecSrc& s,
+                                             const DecSrc& sn, const DecLane& ln, uint4* kreg) {
   typedef MfmaDecodeShape<D, G> SH;
   constexpr int LPK = SH::LPK, NSLOT = SH::NSLOT;
-  const int token = d.token, wrow = d.wrow, kbeg = d.kbeg, kend = d.kend, part = d.part;
-  const int nparts = d.nparts, kvh = d.kvh;
   const int lane = threadIdx.x & 63;
   const int rrow = lane >> 4, col = lane & 15;  // score layout: keys 4 rrow.., head col
   const int slot = lane / LPK, sub = lane % LPK;  // V layout
-  const int p_shift = a.p_shift;
-
-  const int pg0 = kbeg >> p_shift;
-  const int npg = ((kend - 1) >> p_shift) - pg0 + 1;
-  const int page_reg = lane < npg ? clampi(pre.page_raw, 0, a.num_pages - 1) : 0;
 
   // Q^T operand, zero in the lanes of heads >= G
-  const size_t row_bytes = (size_t)SH::ROWB;
   uint4 qb[SH::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)
@@ -472,36 +559,25 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, const Dec
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
 
-  const char* kbase = (const char*)a.k_pool + (size_t)kvh * row_bytes;
-  const char* vbase = (const char*)a.v_pool + (size_t)kvh * row_bytes;
-  const size_t slot_stride = (size_t)a.Hkv * row_bytes;
-  const uint32_t k_off = (uint32_t)((lane >> 3) * slot_stride) + 16 * (lane & 7);
-  const uint32_t v_off = (uint32_t)(slot * SH::UNROLL * slot_stride) + 16 * sub;
   const float sl2e = a.scale_log2e;
-
-  // A ring of NBUF register buffers: the loads of the next NBUF - 1 buffers
-  // are in flight while one computes. Every step issues one buffer's loads
-  // unconditionally, so the compiler waits only for the buffer it consumes;
-  // steps past the range re-read its last buffer (just fetched: an L2 hit)
-  // and skip the compute.
-  MfmaBuf<D, G> buf[NBUF];
-  const int nbuf = (kend - kbeg + 15) / 16;
-  const int kb_last = kbeg + 16 * (nbuf - 1);
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    mfma_load<D, G>(buf[p], kbase, vbase, page_reg, pg0, p_shift, slot_stride,
-                    min(kbeg + 16 * p, kb_last), k_off, v_off);
-  for (int j0 = 0; j0 < nbuf; j0 += NBUF) {
-#pragma unroll
-    for (int p = 0; p < NBUF; ++p) {
-      const int j = j0 + p;
-      mfma_load<D, G>(buf[(p + NBUF - 1) % NBUF], kbase, vbase, page_reg, pg0, p_shift,
-                      slot_stride, min(kbeg + 16 * (j + NBUF - 1), kb_last), k_off, v_off);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this compute
-      if (j < nbuf)
-        mfma_compute<D, G>(buf[p], qb, m_run, l_part, o, kbeg + 16 * j, kend, rrow, slot, sl2e,
-                           bias, kreg);
-    }
+  const int nb = s.nbuf, kend = d.kend;
+  auto load = [&](MfmaBuf<D, G>& b, int x) {
+    if (x < nb)
+      mfma_load<D, G>(b, a, s, x, ln);
+    else
+      mfma_load<D, G>(b, a, sn, x - nb, ln);
+  };
+  for (int j = 0;; j += 2) {
+    load(b1, j + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this compute
+    mfma_compute<D, G>(b0, qb, m_run, l_part, o, s.kbeg + 16 * j, kend, rrow, slot, sl2e, bias,
+                       kreg);
+    if (j + 1 >= nb) break;
+    load(b0, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_compute<D, G>(b1, qb, m_run, l_part, o, s.kbeg + 16 * (j + 1), kend, rrow, slot, sl2e,
+                       bias, kreg);
+    if (j + 2 >= nb) break;
   }
 
   // Sums over the lanes of a head (l) and over the V slots (o): one max for
@@ -520,6 +596,7 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, const Dec
 
   // Slot s writes the heads h with h % NSLOT == s; the head's l and m come
   // from lane col = h of the row.
+  const size_t row_bytes = (size_t)SH::ROWB;
   const uint32_t lu = __float_as_uint(l), mu = __float_as_uint(m_run);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -535,21 +612,21 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, const Dec
       default: lh = row_bcast<7>(lu); mh = row_bcast<7>(mu); break;
     }
     if (h % NSLOT != slot) continue;
-    const int hq = kvh * G + h;
-    if (nparts == 1) {
+    const int hq = d.kvh * G + h;
+    if (d.nparts == 1) {
       const float inv = 1.f / __uint_as_float(lh);
       uint32_t wv[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) wv[w] = pack_bf16x2(o[h][2 * w] * inv, o[h][2 * w + 1] * inv);
-      char* orow = (char*)a.out + ((size_t)token * a.Hq + hq) * row_bytes;
+      char* orow = (char*)a.out + ((size_t)d.token * a.Hq + hq) * row_bytes;
       *reinterpret_cast<uint4*>(orow + 16 * sub) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     } else {
-      const size_t pi = ((size_t)wrow * a.max_parts + part) * a.Hq + hq;
+      const size_t pi = ((size_t)d.pslot + d.part) * a.Hq + hq;
       float* po = a.ws + pi * D + 8 * sub;
       *reinterpret_cast<float4*>(po) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
       *reinterpret_cast<float4*>(po + 4) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
       if (sub == 0) {
-        float* ml = a.ws + (size_t)(token_mode ? a.T : a.S) * a.max_parts * a.Hq * D;
+        float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
         *reinterpret_cast<float2*>(ml + 2 * pi) =
             make_float2(__uint_as_float(mh), __uint_as_float(lh));
       }
@@ -557,27 +634,50 @@ __device__ __forceinline__ void decode_segment_mfma(const AttnArgs& a, const Dec
   }
 }
 
+// A single range (one wave, one work item).
+template <int D, int G>
+__device__ __forceinline__ void decode_range_alone(const AttnArgs& a, const DecSeg& d,
+                                                   uint4* kreg) {
+  const DecLane ln = dec_lane<D, G>(a);
+  const DecPre<D, G> p = decode_prefetch<D, G>(a, d);
+  const DecSrc s = dec_src<D, G>(a, d, p.page_raw);
+  MfmaBuf<D, G> b0, b1;
+  mfma_load<D, G>(b0, a, s, 0, ln);
+  decode_range<D, G>(a, b0, b1, d, p, s, s, ln, kreg);
+}
 
-// The decode ranges of wave gw, each range's page ids and Q issued while the
-// previous range streams. lds: kbuf_units<D>() 16-byte units per wave of the
-// workgroup (wave w uses the w-th block).
+// The decode ranges of wave gw, streamed back to back: each range's page ids
+// and Q are issued while the previous range streams, and its first buffer is
+// loaded during the previous range's last step. lds: kbuf_units<D>() 16-byte
+// units per wave of the workgroup (wave w uses the w-th block).
 template <int D, int G>
 __device__ __forceinline__ void decode_chunks_mfma(const AttnArgs& a, int wg, int n_wg,
                                                    uint4* lds) {
   uint4* kreg = lds + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kbuf_units<D>();
+  const DecLane ln = dec_lane<D, G>(a);
   DecodeCursor cur(a, wg, n_wg);
   DecSeg d;
   if (!cur.next(d)) return;
   DecPre<D, G> p = decode_prefetch<D, G>(a, d);
+  DecSrc s = dec_src<D, G>(a, d, p.page_raw);
+  MfmaBuf<D, G> b0, b1;
+  mfma_load<D, G>(b0, a, s, 0, ln);
+  bool flip = false;  // the current range's buffer 0 is in b1
   for (;;) {
     DecSeg dn;
     const bool more = cur.next(dn);
-    DecPre<D, G> pn;
-    if (more) pn = decode_prefetch<D, G>(a, dn);
-    decode_segment_mfma<D, G, kDecodeBufs>(a, d, p, false, kreg);
+    if (!more) dn = d;
+    const DecPre<D, G> pn = decode_prefetch<D, G>(a, dn);
+    const DecSrc sn = dec_src<D, G>(a, dn, pn.page_raw);
+    if (!flip)
+      decode_range<D, G>(a, b0, b1, d, p, s, sn, ln, kreg);
+    else
+      decode_range<D, G>(a, b1, b0, d, p, s, sn, ln, kreg);
     if (!more) break;
+    flip ^= (s.nbuf & 1) != 0;
     d = dn;
     p = pn;
+    s = sn;
   }
 }
 

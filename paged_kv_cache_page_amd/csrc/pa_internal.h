@@ -19,7 +19,7 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* qsl;
   void* out;
-  float* ws;           // split-KV partials: o [rows*max_parts*Hq*D], then (m, l) pairs
+  float* ws;           // split-KV partials: o [part_slots*Hq*D], then (m, l) pairs
   int* plan;           // work lists written by the plan kernel (see pa_plan.hip)
   int32_t cap_dec, cap_pf;  // capacities of the decode chunk and prefill item lists
   int32_t S, T, Hq, Hkv, D, P, num_pages, max_blocks;
@@ -28,6 +28,7 @@ struct AttnArgs {
   int32_t part_tokens;  // keys per split-KV partition (at most); 0 = chosen by the plan kernel
   int32_t part_min, part_max;  // bounds of a chosen partition size (multiples of 16)
   int32_t max_parts;    // partitions a row may need (ceil(max_seq_len / smallest size))
+  int32_t part_slots;   // split-KV partial slots (each holds all Hq heads of one partition)
   int32_t dec_grid;     // workgroups of the decode kernel (a multiple of 8)
   float scale_log2e;    // scale * log2(e): weights are exp2(s * scale_log2e - m)
   // Key-range pieces of long prefill items (automatic partitions only):
@@ -39,14 +40,17 @@ struct AttnArgs {
 // Plan layout, in ints from the start of the workspace:
 //   header [32]: [0] decode rows R, [1] prefill entries (per KV head), [2]
 //     chunk keys C, [3] chunks, [4] row alignment A, [5] cut prefill items,
-//     [6..31] unused
+//     [6] chunks taken one per decode wave n_s, [7] claimed items (chunks
+//     past n_s x Hkv), [8..31] unused
 //   prefill queue cursors: Hq counters, one per 128-byte line (Hq >= Hkv
 //     bounds the KV heads, which the workspace query does not see): the
-//     queue of KV head h at kPlanLine * (1 + h); zeroed by the plan kernel,
+//     queue of KV head h at kPlanLine * (1 + h); then the counter of the
+//     claimed decode chunks on line 1 + Hq. All zeroed by the plan kernel,
 //     advanced with device-scope atomics
 //   decode rows: S x (sequence, key offset, keys, token); row i's keys occupy
 //     [offset, offset + round_up(keys, A)) of the concatenated key axis
-//   partitions per sequence: S ints (0 = no decode row)
+//   partitions per decode row: S ints
+//   first partial slot per decode row: S ints (rows of one partition own none)
 //   first decode row of each chunk: cap_dec ints
 //   prefill entries (16-byte aligned): cap_pf x (sequence, row tile,
 //     piece j | pieces J << 16, first partial slot), in decreasing cost order;
@@ -56,19 +60,22 @@ struct AttnArgs {
 //     prefill merge kernel after the tick
 constexpr int kPlanLine = 32;  // ints per 128-byte cache line
 struct PlanOffsets {
-  size_t rows, nparts, first_row, pf, merge, total;
+  size_t rows, nparts, pbase, first_row, pf, merge, total;
 };
 __host__ __device__ inline PlanOffsets plan_offsets(long S, long Hq, long cap_dec, long cap_pf) {
   PlanOffsets o;
-  o.rows = (size_t)kPlanLine * (1 + (size_t)Hq);
+  o.rows = (size_t)kPlanLine * (2 + (size_t)Hq);
   o.nparts = o.rows + 4 * (size_t)S;
-  o.first_row = o.nparts + (size_t)S;
+  o.pbase = o.nparts + (size_t)S;
+  o.first_row = o.pbase + (size_t)S;
   o.pf = (o.first_row + (size_t)cap_dec + 3) / 4 * 4;
   o.merge = o.pf + 4 * (size_t)cap_pf;
   o.total = o.merge + 4 * (size_t)cap_pf;
   return o;
 }
 __host__ __device__ inline int plan_pf_cursor(int h) { return kPlanLine * (1 + h); }
+__host__ __device__ inline int plan_dec_cursor(int Hq) { return kPlanLine * (1 + Hq); }
+
 // Query rows per prefill workgroup; a tile holds kPrefillRows / G tokens.
 constexpr int kPrefillRows = 128;
 // Keys per prefill K/V tile (the unit in which prefill items are cut into pieces).

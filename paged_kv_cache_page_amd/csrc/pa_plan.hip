@@ -12,7 +12,9 @@
 //                 the same work however the lengths are spread (split-KV for
 //                 long rows, several short rows per chunk); with a fixed
 //                 partition size A = C = that size, so a chunk never spans
-//                 two rows and a row's partitions depend on the row alone;
+//                 two rows and a row's partitions depend on the row alone.
+//                 A row of several partitions owns that many consecutive
+//                 split-KV partial slots;
 //   prefill entries (sequence, row tile, piece) for every sequence with query
 //                 length > 1, ordered by decreasing number of key tiles, so that
 //                 the longest start first (longest-processing-time-first
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   const PlanOffsets po = plan_offsets(a.S, a.Hq, cap_dec, cap_pf);
   int4* dec_rows = reinterpret_cast<int4*>(plan + po.rows);
   int* nparts_of = plan + po.nparts;
+  int* pbase_of = plan + po.pbase;
   int* first_row = plan + po.first_row;
   int4* pf_items = reinterpret_cast<int4*>(plan + po.pf);
   int4* merge_items = reinterpret_cast<int4*>(plan + po.merge);
@@ -167,16 +170,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   const int maxt = wave_max(my_maxt);
   __syncthreads();
 
-  // ---- chunk size of the decode key axis ----
+  // ---- chunk size of the decode key axis: one chunk per decode wave of the
+  // least-served KV head; chunks past that count (from a fixed partition size,
+  // or chunks capped at the largest partition) are claimed from a counter ----
+  const long long waves = max(1, a.dec_grid * 4 / a.Hkv);
+  const long long dec_share = (total_keys + waves - 1) / waves;  // keys per decode wave
   int C = a.part_tokens;
   if (C <= 0) {
-    // one chunk per decode wave of the least-served KV head
-    const long long waves = (long long)a.dec_grid * 4 / a.Hkv;
-    long long c = (total_keys + waves - 1) / waves;
-    c = (c + 15) / 16 * 16;
+    const long long c = (dec_share + 15) / 16 * 16;
     C = (int)(c < a.part_min ? a.part_min : (c > a.part_max ? a.part_max : c));
   }
-  const long long chunks = (total_keys + C - 1) / C;
+  long long chunks = (total_keys + C - 1) / C;
+  if (chunks > cap_dec) chunks = cap_dec;  // (never: the workspace query bounds the chunks)
+  const int n_static = (int)(chunks < waves ? chunks : waves);
 
   // ---- piece length Tp: the mean tile count per prefill workgroup, but no
   // less than the time a decode wave spends on its chunk (items shorter than
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   if (a.pf_slots > 0 && a.part_tokens == 0 && item_tiles_all > 0) {
     const long long w = a.pf_workers > 0 ? a.pf_workers : 1;
     long long t0 = (item_tiles_all * a.Hkv + w - 1) / w;
-    if (total_keys > 0) t0 = max(t0, (long long)(C + kDecodeKeysPerTile - 1) / kDecodeKeysPerTile);
+    if (total_keys > 0) t0 = max(t0, (dec_share + kDecodeKeysPerTile - 1) / kDecodeKeysPerTile);
     Tp = (int)(t0 < kMinPieceTiles ? kMinPieceTiles : (t0 > kCostBins ? kCostBins : t0));
     for (int tries = 0;; ++tries) {
       long long need = 0;
@@ -204,8 +210,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     }
   }
 
-  // ---- pass 2: decode rows, their offsets on the key axis, chunk starts ----
-  int row_base = 0, off_base = 0;
+  // ---- pass 2: decode rows, their offsets on the key axis, chunk starts,
+  // partial slots (rows of more than one partition) ----
+  int row_base = 0, off_base = 0, slot_base = 0;
   for (int c0 = 0; c0 < a.S; c0 += 64) {
     const int s = c0 + lane;
     SeqShape sh{0, 0, 0};
@@ -220,20 +227,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     int nrows, npad;
     const int ri = row_base + wave_excl_scan(is_dec, &nrows);
     const int off = off_base + wave_excl_scan(pad, &npad);
-    if (s < a.S) {
-      int np = 0;
-      if (is_dec) {
-        const int j0 = off / C, j1 = (off + pad - 1) / C;
-        np = j1 - j0 + 1;
-        dec_rows[ri] = make_int4(s, off, sh.n, sh.q0);
-        // chunks whose first key falls in this row start here
-        for (int j = (off + C - 1) / C; j <= j1; ++j)
-          if (j < cap_dec) first_row[j] = ri;
-      }
-      nparts_of[s] = np;
+    int np = 0, j0 = 0, j1 = -1;
+    if (is_dec) {
+      j0 = off / C;
+      j1 = (off + pad - 1) / C;
+      np = j1 - j0 + 1;
+    }
+    int nslots;
+    const int pb = slot_base + wave_excl_scan(np > 1 ? np : 0, &nslots);
+    if (is_dec) {
+      dec_rows[ri] = make_int4(s, off, sh.n, sh.q0);
+      nparts_of[ri] = np;
+      pbase_of[ri] = pb;
+      // chunks whose first key falls in this row start here
+      for (int j = (off + C - 1) / C; j <= j1; ++j)
+        if (j < cap_dec) first_row[j] = ri;
     }
     row_base += nrows;
     off_base += npad;
+    slot_base += nslots;
   }
 
   // ---- entries per cost bin: piece j of an item of t tiles cut into J has
@@ -284,11 +296,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     plan[0] = row_base;
     plan[1] = min(pf_total, cap_pf);
     plan[2] = C;
-    plan[3] = (int)(chunks < cap_dec ? chunks : cap_dec);
+    plan[3] = (int)chunks;
     plan[4] = A;
     plan[5] = min(s_merge_next, cap_pf);
+    plan[6] = n_static;
+    plan[7] = ((int)chunks - n_static) * a.Hkv;
+    plan[plan_dec_cursor(a.Hq)] = 0;
   }
-  for (int i = 6 + lane; i < kPlanLine; i += 64) plan[i] = 0;
+  for (int i = 8 + lane; i < kPlanLine; i += 64) plan[i] = 0;
   for (int h = lane; h < a.Hkv; h += 64) plan[plan_pf_cursor(h)] = 0;
 }
 
