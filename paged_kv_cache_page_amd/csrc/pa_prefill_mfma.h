@@ -102,7 +102,7 @@ struct PfShape {
   static constexpr int DMA_PER_TILE = 2 * DMA_PER_WAVE;  // K and V, per wave
   static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * kPfWaves * 1024 == TILE_BYTES,
                 "a tile is whole DMA instructions per wave");
-  static_assert(DMA_PER_TILE * (kPfStages - 1) <= 63, "vmcnt immediate");
+  static_assert(DMA_PER_TILE * (kPfStages - 2) <= 63, "vmcnt immediate");
 };
 
 // LDS of one prefill workgroup: two stages of K and V tiles and the
@@ -123,8 +123,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// wait_vmcnt<tiles * per_tile> for a run-time tiles in [0, kPfStages - 1].
-template <int PER_TILE, int T = kPfStages - 1>
+// wait_vmcnt<tiles * per_tile> for a run-time tiles in [0, kPfStages - 2]
+// (the tiles whose loads may stay in flight while one is computed).
+template <int PER_TILE, int T = kPfStages - 2>
 __device__ __forceinline__ void wait_tiles(int tiles) {
   if constexpr (T == 0) {
     wait_vmcnt<0>();
@@ -207,7 +208,7 @@ __device__ __forceinline__ uint32_t dma_lane_v(int j, size_t slot_stride) {
 }
 
 template <int D>
-__device__ __forceinline__ void tile_dma_full(uint16_t* sk, uint16_t* sv, const char* kpool,
+__device__ __forceinline__ void tile_dma_full(uint32_t sk, uint32_t sv, const char* kpool,
                                               const char* vpool, const int* s_pt,
                                               const int* bt_row, int num_pages, int p_shift,
                                               size_t slot_stride, int kb0, int kmax, int wave,
@@ -226,13 +227,12 @@ __device__ __forceinline__ void tile_dma_full(uint16_t* sk, uint16_t* sv, const 
   for (int i = 0; i < SH::DMA_PER_WAVE; ++i) {
     const int q = wave * SH::DMA_PER_WAVE + i;
     // K: chunks 4 (q % (CPR / 4)) .. + 3 of the block's 16 keys
-    lds_dma16_s(kblk + 64 * (i % (CPR / 4)), lk, lds_addr(sk + 512 * q));
+    lds_dma16_s(kblk + 64 * (i % (CPR / 4)), lk, sk + 1024 * q);
     // V: 8-key group q % 2 of the block, chunk pairs 4 (q % (CPR / 8)) .. + 3
     //    (D = 128: CPR / 8 = 2 instructions per 8-key group; D = 64: one)
     const int g8 = (64 * q) / (8 * CPR);
     const int cp = ((64 * q) % (8 * CPR)) / 16;
-    lds_dma16_s(vblk + (size_t)(8 * (g8 & 1)) * slot_stride + 32 * cp, lv,
-                lds_addr(sv + 512 * q));
+    lds_dma16_s(vblk + (size_t)(8 * (g8 & 1)) * slot_stride + 32 * cp, lv, sv + 1024 * q);
   }
 }
 
@@ -241,7 +241,7 @@ __device__ __forceinline__ void tile_dma_full(uint16_t* sk, uint16_t* sv, const 
 // hold anything; their scores are masked and their V rows repeat key kmax - 1
 // under a zero weight).
 template <int D>
-__device__ __forceinline__ void tile_dma_partial(uint16_t* sk, uint16_t* sv, const char* kpool,
+__device__ __forceinline__ void tile_dma_partial(uint32_t sk, uint32_t sv, const char* kpool,
                                                  const char* vpool, const int* s_pt,
                                                  const int* bt_row, int num_pages, int p_shift,
                                                  size_t slot_stride, int kb0, int kmax, int wave,
@@ -258,7 +258,7 @@ __device__ __forceinline__ void tile_dma_partial(uint16_t* sk, uint16_t* sv, con
       const int key = min(kb0 + row, kmax - 1);
       const uint32_t pg = block_page(s_pt, bt_row, num_pages, p_shift, kb0 + (row & ~15), kmax);
       const size_t off = (((size_t)pg << p_shift) + (size_t)(key & rmask)) * slot_stride + 16 * c;
-      lds_dma16(kpool + off, lds_addr(sk + 512 * q));
+      lds_dma16(kpool + off, sk + 1024 * q);
     }
     {
       const int row = (u / (8 * CPR)) * 8 + (u % 16) / 2;
@@ -266,7 +266,7 @@ __device__ __forceinline__ void tile_dma_partial(uint16_t* sk, uint16_t* sv, con
       const int key = min(kb0 + row, kmax - 1);
       const uint32_t pg = block_page(s_pt, bt_row, num_pages, p_shift, kb0 + (row & ~15), kmax);
       const size_t off = (((size_t)pg << p_shift) + (size_t)(key & rmask)) * slot_stride + 16 * c;
-      lds_dma16(vpool + off, lds_addr(sv + 512 * q));
+      lds_dma16(vpool + off, sv + 1024 * q);
     }
   }
 }
@@ -463,38 +463,43 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
 
   // A ring of kPfStages LDS stages: the loads of the next kPfStages - 1 tiles
   // are in flight while tile t computes. Every wave waits for its own loads of
-  // tile t (vmcnt: the later tiles' loads are the most recent ones), then the
-  // barrier makes all waves' loads visible.
+  // tile t (vmcnt: the later tiles' loads are the most recent ones); then one
+  // barrier per tile both makes all waves' loads of tile t visible and tells
+  // that every wave is done with tile t - 1, whose stage the loads issued
+  // right after it refill.
   const uint32_t lk = dma_lane_k(lane, slot_stride), lv = dma_lane_v(lane, slot_stride);
+  // LDS byte addresses of the stages (wave-uniform: scalar registers)
+  const uint32_t lds_k0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(sm.k[0]));
+  const uint32_t lds_v0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(sm.v[0]));
+  constexpr uint32_t kStageBytes = sizeof(sm.k[0]);
   auto issue = [&](int tile, int stage) {
     const int kb0 = tile * kBN;
+    const uint32_t sk = lds_k0 + kStageBytes * stage, sv = lds_v0 + kStageBytes * stage;
     if (kb0 + kBN <= kmax)
-      tile_dma_full<D>(sm.k[stage], sm.v[stage], kpool, vpool, sm.pt, bt_row, a.num_pages,
-                       p_shift, slot_stride, kb0, kmax, wave, lk, lv);
+      tile_dma_full<D>(sk, sv, kpool, vpool, sm.pt, bt_row, a.num_pages, p_shift, slot_stride,
+                       kb0, kmax, wave, lk, lv);
     else
-      tile_dma_partial<D>(sm.k[stage], sm.v[stage], kpool, vpool, sm.pt, bt_row, a.num_pages,
-                          p_shift, slot_stride, kb0, kmax, wave, lane);
+      tile_dma_partial<D>(sk, sv, kpool, vpool, sm.pt, bt_row, a.num_pages, p_shift,
+                          slot_stride, kb0, kmax, wave, lane);
   };
 #pragma unroll
   for (int t = 0; t < kPfStages - 1; ++t)
     if (tb + t < te) issue(tb + t, t);
   int st = 0;  // stage of tile t
   for (int t = tb; t < te; ++t) {
-    const int tn = t + kPfStages - 1;  // tile whose loads start now
-    if (tn < te) {
-      issue(tn, st == 0 ? kPfStages - 1 : st - 1);  // stage (t - tb + kPfStages - 1) % kPfStages
-    }
-    wait_tiles<SH::DMA_PER_TILE>(min(te - 1 - t, kPfStages - 1));
+    wait_tiles<SH::DMA_PER_TILE>(min(te - 1 - t, kPfStages - 2));
     lds_barrier();
+    const int tn = t + kPfStages - 1;  // tile whose loads start now
+    if (tn < te) issue(tn, st == 0 ? kPfStages - 1 : st - 1);  // the stage of tile t - 1
     const int kb0 = t * kBN;
     const bool masked[2] = {kb0 + kBN - 1 > min_limit[0], kb0 + kBN - 1 > min_limit[1]};
     tile_compute<D>(sm.k[st], sm.v[st], kb0, qop, limit, masked, sl2e, col, grp, m_run, l_run,
                     acc_o);
-    // stage st is free for tile t + kPfStages once every wave's reads of it
-    // have returned (their results fed the MFMAs above)
-    lds_barrier();
     st = st + 1 == kPfStages ? 0 : st + 1;
   }
+  // every wave is done with the stages (and the page ids) before the next
+  // item's loads refill them
+  lds_barrier();
 
   if (pJ > 1) {
     // ---- piece of a cut item: partial (m, l, o) of the 128 rows ----
