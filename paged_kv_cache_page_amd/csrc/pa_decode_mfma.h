@@ -60,7 +60,8 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
 
 // K3 task idx = (row, query head, 4 consecutive dims): merge the row's
 // split-KV partitions, m* = max_k m_k,
-// o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k.
+// o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k (m* taken as a running
+// maximum, the sums rescaled when it grows).
 template <typename ET, bool TOKEN_MODE>
 __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
   const int D = a.D;
@@ -80,26 +81,36 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
     token = (int)row;
     slot0 = (size_t)row * a.max_parts;
   } else {
-    // row = decode row of the plan
-    if (row >= a.plan[0]) return;
+    // row = decode row of the plan. The four loads are independent (entries
+    // past the plan's rows hold stale values and are used only once row is
+    // known to be a decode row), so they overlap.
     const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
+    const int n_rows = a.plan[0];
     nparts = a.plan[po.nparts + row];
-    if (nparts <= 1) return;
     token = reinterpret_cast<const int4*>(a.plan + po.rows)[row].w;
     slot0 = (size_t)a.plan[po.pbase + row];
+    if (row >= n_rows) return;
   }
   if (nparts <= 1) return;
   const float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
   const size_t p0 = slot0 * a.Hq + h;  // partial index of part 0
-  float mn = kNegBig;
-  for (int k = 0; k < nparts; ++k) mn = fmaxf(mn, ml[2 * (p0 + (size_t)k * a.Hq)]);
-  float lt = 0.f;
+  // one pass with a running max: all partitions' loads are independent
+  float mn = kNegBig, lt = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int k = 0; k < nparts; ++k) {
     const size_t pi = p0 + (size_t)k * a.Hq;
     const float2 mlk = *reinterpret_cast<const float2*>(ml + 2 * pi);
     const float4 ok = *reinterpret_cast<const float4*>(a.ws + pi * D + 4 * d4);
+    if (mlk.x > mn) {
+      const float c = fast_exp2(mn - mlk.x);
+      mn = mlk.x;
+      lt *= c;
+      acc.x *= c;
+      acc.y *= c;
+      acc.z *= c;
+      acc.w *= c;
+    }
     const float c = fast_exp2(mlk.x - mn);
     lt = fmaf(mlk.y, c, lt);
     acc.x = fmaf(ok.x, c, acc.x);
