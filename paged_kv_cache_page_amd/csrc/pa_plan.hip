@@ -38,16 +38,28 @@ constexpr int kPlanThreads = 64;    // one wave
 constexpr int kCostBins = 2048;     // key tiles of a prefill item, capped
 constexpr int kCachedSeqs = 4096;   // sequence shapes kept in LDS between the passes
 
+// Inclusive prefix sum over the wave with DPP lane moves (no LDS round
+// trips): shifts by 1, 2, 4, 8 within each 16-lane row, then lane 15 of a row
+// added to the next row (row_bcast:15, rows 1 and 3) and lane 31 to the upper
+// half (row_bcast:31, rows 2 and 3). Lanes a move does not reach read 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp0<0x111, 0xF>(v);  // row_shr:1
+  v += dpp0<0x112, 0xF>(v);  // row_shr:2
+  v += dpp0<0x114, 0xF>(v);  // row_shr:4
+  v += dpp0<0x118, 0xF>(v);  // row_shr:8
+  v += dpp0<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp0<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum over the wave; *total = the wave's sum (uniform).
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
-  const int lane = threadIdx.x & 63;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  *total = __shfl(incl, 63);
+  const int incl = wave_incl_scan(v);
+  *total = __builtin_amdgcn_readlane(incl, 63);
   return incl - v;
 }
 
@@ -55,6 +67,10 @@ __device__ __forceinline__ long long wave_sum(long long v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   return v;
+}
+
+__device__ __forceinline__ int wave_sum32(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
 
 __device__ __forceinline__ int wave_max(int v) {
@@ -107,7 +123,8 @@ __device__ __forceinline__ void for_prefill_seqs(int S, Shape&& shape, F&& f) {
     while (m) {
       const int i = __builtin_ctzll(m);
       m &= m - 1;
-      const SeqShape u{__shfl(sh.L, i), __shfl(sh.n, i), __shfl(sh.q0, i)};
+      const SeqShape u{__builtin_amdgcn_readlane(sh.L, i), __builtin_amdgcn_readlane(sh.n, i),
+                       __builtin_amdgcn_readlane(sh.q0, i)};
       f(c0 + i, u);
     }
   }
@@ -140,8 +157,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     s_merge_next = 0;
   }
 
-  // ---- pass 1: shapes, padded decode keys ----
-  long long my_keys = 0;
+  // ---- pass 1: shapes, padded decode keys (the key axis fits an int: the
+  // caller's bounds are checked on the host) ----
+  int my_keys = 0;
   for (int s = lane; s < a.S; s += 64) {
     const SeqShape sh = seq_shape(a, s);
     if (s < kCachedSeqs) {
@@ -151,7 +169,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
     }
     if (sh.L == 1 && sh.n >= 1) my_keys += (sh.n + A - 1) / A * A;
   }
-  const long long total_keys = wave_sum(my_keys);  // length of the decode key axis
+  const int total_keys = wave_sum32(my_keys);  // length of the decode key axis
   __syncthreads();
 
   // ---- prefill items: key tiles (histogram, sum, max) ----
@@ -173,16 +191,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   // ---- chunk size of the decode key axis: one chunk per decode wave of the
   // least-served KV head; chunks past that count (from a fixed partition size,
   // or chunks capped at the largest partition) are claimed from a counter ----
-  const long long waves = max(1, a.dec_grid * 4 / a.Hkv);
-  const long long dec_share = (total_keys + waves - 1) / waves;  // keys per decode wave
+  // (32-bit unsigned divisions: the 64-bit ones are long software routines)
+  const unsigned waves = (unsigned)max(1, a.dec_grid * 4 / a.Hkv);
+  const unsigned tk = (unsigned)total_keys;
+  const unsigned dec_share = (tk + waves - 1u) / waves;  // keys per decode wave (no overflow)
   int C = a.part_tokens;
   if (C <= 0) {
-    const long long c = (dec_share + 15) / 16 * 16;
-    C = (int)(c < a.part_min ? a.part_min : (c > a.part_max ? a.part_max : c));
+    const unsigned c = (dec_share + 15u) / 16u * 16u;
+    C = (int)(c < (unsigned)a.part_min ? (unsigned)a.part_min
+                                       : (c > (unsigned)a.part_max ? (unsigned)a.part_max : c));
   }
-  long long chunks = (total_keys + C - 1) / C;
+  int chunks = (int)((tk + (unsigned)C - 1u) / (unsigned)C);
   if (chunks > cap_dec) chunks = cap_dec;  // (never: the workspace query bounds the chunks)
-  const int n_static = (int)(chunks < waves ? chunks : waves);
+  const int n_static = chunks < (int)waves ? chunks : (int)waves;
 
   // ---- piece length Tp: the mean tile count per prefill workgroup, but no
   // less than the time a decode wave spends on its chunk (items shorter than
@@ -192,8 +213,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   int Tp = 0x3FFFFFFF;  // never cut
   if (a.pf_slots > 0 && a.part_tokens == 0 && item_tiles_all > 0) {
     const long long w = a.pf_workers > 0 ? a.pf_workers : 1;
-    long long t0 = (item_tiles_all * a.Hkv + w - 1) / w;
-    if (total_keys > 0) t0 = max(t0, (dec_share + kDecodeKeysPerTile - 1) / kDecodeKeysPerTile);
+    long long t0 = (long long)(((double)item_tiles_all * a.Hkv + (double)(w - 1)) / (double)w);
+    if (total_keys > 0)
+      t0 = max(t0, (long long)((dec_share + kDecodeKeysPerTile - 1) / kDecodeKeysPerTile));
     Tp = (int)(t0 < kMinPieceTiles ? kMinPieceTiles : (t0 > kCostBins ? kCostBins : t0));
     for (int tries = 0;; ++tries) {
       long long need = 0;
@@ -249,17 +271,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnArgs a, int* pla
   }
 
   // ---- entries per cost bin: piece j of an item of t tiles cut into J has
-  // (j + 1) t / J - j t / J tiles ----
-  for (int b = lane; b <= maxt; b += 64) s_hist[b] = 0;
-  __syncthreads();
-  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
-    const int ntiles = (sh.L + TM - 1) / TM;
-    for (int mt = lane; mt < ntiles; mt += 64) {
-      const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
-      for (int j = 0; j < J; ++j) atomicAdd(&s_hist[(j + 1) * t / J - j * t / J], 1);
-    }
-  });
-  __syncthreads();
+  // (j + 1) t / J - j t / J tiles (when nothing is cut, the item histogram
+  // already is that) ----
+  if (Tp < maxt) {
+    for (int b = lane; b <= maxt; b += 64) s_hist[b] = 0;
+    __syncthreads();
+    for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
+      const int ntiles = (sh.L + TM - 1) / TM;
+      for (int mt = lane; mt < ntiles; mt += 64) {
+        const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
+        for (int j = 0; j < J; ++j) atomicAdd(&s_hist[(j + 1) * t / J - j * t / J], 1);
+      }
+    });
+    __syncthreads();
+  }
 
   // ---- bin offsets in decreasing cost: bin b starts after all bins > b ----
   int pf_total = 0;
