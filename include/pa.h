@@ -113,6 +113,7 @@ pa_status_t pa_compute_slot_mapping(const int32_t* block_tables, const int32_t* 
  *             no RoPE (then q and k are left unchanged and k is stored as is)
  *   k_pool, v_pool [num_pages, P, Hkv, D], written at the mapped slots only
  *
+ * head_dim: a multiple of 16, at most 2048 (else PA_ERR_UNSUPPORTED).
  * Rotation: for pair (i, i + D/2), x1' = x1*c - x2*s and x2' = x2*c + x1*s in
  * float32 with each product and sum rounded separately (no fused
  * multiply-add), then rounded to nearest-even into the storage dtype. A

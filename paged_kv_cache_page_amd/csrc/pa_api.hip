@@ -260,7 +260,8 @@ pa_status_t pa_rope_and_cache_write(void* q, void* k, const void* v, const int32
   if ((long)num_pages * page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
   if (q && Hq < 1) return PA_ERR_INVALID_ARG;
   if (cos_sin && max_pos < 1) return PA_ERR_INVALID_ARG;
-  if (head_dim % 16) return PA_ERR_UNSUPPORTED;  // 16-byte vectors on each half row
+  // 16-byte vectors on each half row, at most one workgroup's worth per half row
+  if (head_dim % 16 || head_dim > kRopeMaxHeadDim) return PA_ERR_UNSUPPORTED;
   if (T == 0) return PA_OK;
   if (!k || !v || !positions || !slot_mapping || !k_pool || !v_pool) return PA_ERR_INVALID_ARG;
   if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(k_pool) ||

@@ -100,7 +100,9 @@ int cu_count();
 void profile_before(const char* name, hipStream_t stream);
 void profile_after(hipStream_t stream);
 
-// K0 / a1 / K1 (pa_rope_cache.hip)
+// K0 / a1 / K1 (pa_rope_cache.hip). K1 takes head dims up to kRopeMaxHeadDim
+// (the vectors of a half row fit one workgroup).
+constexpr int kRopeMaxHeadDim = 2048;
 hipError_t launch_rope_table(float* out, int max_pos, int D, double theta, hipStream_t s);
 hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* qsl, const int32_t* pos,
                                int32_t* slots, int S, int T, int max_blocks, int P,

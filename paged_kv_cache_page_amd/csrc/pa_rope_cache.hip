@@ -42,19 +42,29 @@ hipError_t launch_rope_table(float* out, int max_pos, int D, double theta, hipSt
 
 // ---------------------------------------------------------------- a1 -------
 // Token t belongs to the last sequence s with qsl[s] <= t (empty sequences
-// have qsl[s] == qsl[s+1] and are passed over by the search).
-__global__ __launch_bounds__(256) void slot_mapping_kernel(
+// have qsl[s] == qsl[s+1] and are passed over by the search). The workgroup
+// first copies query_start_loc into LDS (one round of loads) and searches
+// there, instead of a chain of dependent global loads per token.
+constexpr int kSlotThreads = 256;
+constexpr int kSlotQslLds = 4096;  // sequences searched in LDS; longer lists are read from memory
+
+__global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
     const int32_t* __restrict__ bt, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ pos, int32_t* __restrict__ slots, int S, int T, int max_blocks,
     int P, int num_pages) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ int s_qsl[kSlotQslLds + 1];
+  const bool in_lds = S <= kSlotQslLds;
+  if (in_lds)
+    for (int i = threadIdx.x; i <= S; i += kSlotThreads) s_qsl[i] = qsl[i];
+  const int t = blockIdx.x * kSlotThreads + threadIdx.x;
+  const int p = t < T ? pos[t] : -1;  // issued before the barrier: overlaps the copy
+  __syncthreads();
   if (t >= T) return;
   int lo = 0, hi = S;  // qsl[lo] <= t < qsl[hi] when the metadata is well formed
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid;
+    if ((in_lds ? s_qsl[mid] : qsl[mid]) <= t) lo = mid; else hi = mid;
   }
-  const int p = pos[t];
   int slot = -1;
   if (p >= 0) {
     const int blk = p / P;
@@ -71,8 +81,9 @@ hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* qsl, const int3
                                int num_pages, hipStream_t s) {
   if (T == 0) return hipSuccess;
   profile_before("slot_mapping", s);
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3((T + 255) / 256), dim3(256), 0, s, bt, qsl, pos,
-                     slots, S, T, max_blocks, P, num_pages);
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((T + kSlotThreads - 1) / kSlotThreads),
+                     dim3(kSlotThreads), 0, s, bt, qsl, pos, slots, S, T, max_blocks, P,
+                     num_pages);
   profile_after(s);
   return hipGetLastError();
 }
@@ -120,8 +131,10 @@ struct RotPair<F32> {
   }
 };
 
+constexpr int kRopeThreads = 256;
+
 template <typename ET>
-__global__ __launch_bounds__(256) void rope_cache_write_kernel(
+__global__ __launch_bounds__(kRopeThreads) void rope_cache_write_kernel(
     char* __restrict__ q, char* __restrict__ k, const char* __restrict__ v,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ slots,
     const float* __restrict__ cs, char* __restrict__ k_pool, char* __restrict__ v_pool, int Hq,
@@ -140,10 +153,24 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(
   const int nq = q ? Hq : 0;
   const int rot_tasks = (nq + Hkv) * vec_half;
   const int tasks = rot_tasks + Hkv * vec_row;
+  // The block size is a multiple of vec_half (see the launch), so a
+  // thread's rotation tasks all take the same vector c of the half row: its
+  // cos/sin values are loaded once.
+  const int c = (int)threadIdx.x % vec_half;
+  float cv[VP], sv[VP];
+  if (rotate) {
+    const float4* cp = reinterpret_cast<const float4*>(cs + (size_t)p * D + c * VP);
+    const float4* sp = reinterpret_cast<const float4*>(cs + (size_t)p * D + half + c * VP);
+#pragma unroll
+    for (int i = 0; i < VP / 4; ++i) {
+      const float4 cc = cp[i], ss = sp[i];
+      cv[4 * i] = cc.x; cv[4 * i + 1] = cc.y; cv[4 * i + 2] = cc.z; cv[4 * i + 3] = cc.w;
+      sv[4 * i] = ss.x; sv[4 * i + 1] = ss.y; sv[4 * i + 2] = ss.z; sv[4 * i + 3] = ss.w;
+    }
+  }
   for (int task = threadIdx.x; task < tasks; task += blockDim.x) {
     if (task < rot_tasks) {
       const int h = task / vec_half;
-      const int c = task % vec_half;
       const bool is_k = h >= nq;
       const int kh = h - nq;
       char* row = is_k ? k + ((size_t)t * Hkv + kh) * row_bytes
@@ -152,15 +179,6 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(
       uint4* p2 = reinterpret_cast<uint4*>(row + (size_t)half * EB + (size_t)c * 16);
       uint4 a = *p1, b = *p2;
       if (rotate) {
-        float cv[VP], sv[VP];
-        const float4* cp = reinterpret_cast<const float4*>(cs + (size_t)p * D + c * VP);
-        const float4* sp = reinterpret_cast<const float4*>(cs + (size_t)p * D + half + c * VP);
-#pragma unroll
-        for (int i = 0; i < VP / 4; ++i) {
-          const float4 cc = cp[i], ss = sp[i];
-          cv[4 * i] = cc.x; cv[4 * i + 1] = cc.y; cv[4 * i + 2] = cc.z; cv[4 * i + 3] = cc.w;
-          sv[4 * i] = ss.x; sv[4 * i + 1] = ss.y; sv[4 * i + 2] = ss.z; sv[4 * i + 3] = ss.w;
-        }
         RotPair<ET>::rotate(a, b, cv, sv);
         *p1 = a;
         *p2 = b;
@@ -187,12 +205,16 @@ hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* 
                                    int P, int num_pages, int max_pos, hipStream_t s) {
   if (T == 0) return hipSuccess;
   profile_before("rope_cache_write", s);
+  // threads: the largest multiple of the vectors per half row (D / 16 for
+  // bf16, D / 8 for fp32) that fits the block
+  const int vec_half = D / 2 / (dt == PA_BF16 ? 8 : 4);
+  const int threads = kRopeThreads / vec_half * vec_half;
   if (dt == PA_BF16) {
-    hipLaunchKernelGGL(rope_cache_write_kernel<BF16>, dim3(T), dim3(256), 0, s, (char*)q,
+    hipLaunchKernelGGL(rope_cache_write_kernel<BF16>, dim3(T), dim3(threads), 0, s, (char*)q,
                        (char*)k, (const char*)v, pos, slots, cs, (char*)k_pool, (char*)v_pool,
                        Hq, Hkv, D, P, num_pages, max_pos);
   } else {
-    hipLaunchKernelGGL(rope_cache_write_kernel<F32>, dim3(T), dim3(256), 0, s, (char*)q,
+    hipLaunchKernelGGL(rope_cache_write_kernel<F32>, dim3(T), dim3(threads), 0, s, (char*)q,
                        (char*)k, (const char*)v, pos, slots, cs, (char*)k_pool, (char*)v_pool,
                        Hq, Hkv, D, P, num_pages, max_pos);
   }

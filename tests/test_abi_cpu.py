@@ -167,6 +167,7 @@ def cache_write(**kw):
     (dict(max_pos=0), INVALID),
     (dict(Hq=0), INVALID),                       # q given but no query heads
     (dict(D=40), UNSUPPORTED),
+    (dict(D=2064), UNSUPPORTED),                 # past 2048
     (dict(k=ctypes.c_void_p(0x10004)), INVALID),
 ])
 def test_cache_write_rejects_bad_host_arguments(kw, code):

@@ -100,7 +100,10 @@ def test_rope_and_cache_write_bit_exact(cfg):
     _check_write(t, d, d.table.cpu().numpy())
 
 
-@pytest.mark.parametrize("dtype,D", [(W.F32, 16), (W.F32, 128), (W.BF16, 64)])
+# (D = 48 bf16 and 80 fp32: 3 and 10 vectors per half row, so the workgroup is
+# 255 and 250 threads)
+@pytest.mark.parametrize("dtype,D", [(W.F32, 16), (W.F32, 128), (W.BF16, 64), (W.BF16, 48),
+                                     (W.F32, 80)])
 def test_rope_and_cache_write_small_shapes(dtype, D):
     rng = np.random.default_rng(50 + D)
     t = W.build_tick(rng, name="small", dtype=dtype, Hq=8, Hkv=2, D=D, P=16,
