@@ -63,6 +63,9 @@ SMALL_CASES = [
     (W.BF16, 4, 2, 128, 16, (16, 32, 48), (16, 16, 16)),              # page-aligned chunks
     (W.BF16, 32, 4, 64, 16, (3000, 1, 700), (200, 1, 64)),            # long items cut into pieces
     (W.BF16, 16, 8, 128, 256, (5000, 2600), (300, 40)),               # pieces, group 2
+    # 16-token pages cap a chunk at 63 pages (1008 keys): 160 k decode keys per KV head
+    # make more chunks than the 128 decode waves of a head, claimed from the counter
+    (W.BF16, 16, 8, 64, 16, (40000, 40000, 40000, 40000), (1, 1, 1, 1)),
     (W.F32, 4, 2, 16, 16, (5, 17, 33, 64), (1, 3, 1, 20)),            # fp32 prefill (token path)
     (W.F32, 8, 1, 64, 16, (100, 3, 700), (1, 3, 65)),
     (W.F32, 8, 4, 128, 32, (90, 190), (1, 45)),
