@@ -20,8 +20,9 @@
 // Computing the transposed products keeps a query row's scores, running max,
 // running sum and output column in the same lanes: a lane's S^T accumulator
 // (4 keys of each 16-key block, one query row) is its P^T operand once the
-// contraction's key order is defined to match, and the row max and sum
-// combine the four lanes of a row with v_permlane16_swap / v_permlane32_swap.
+// contraction's key order is defined to match, and the row max combines the
+// four lanes of a row with v_permlane16_swap / v_permlane32_swap. The row sum
+// is one more product per k-step, of the weights with a block of ones.
 //
 // K and V tiles go from global memory straight into LDS (global_load_lds,
 // 16 bytes per lane, no registers), two stages deep: tile t + 1 is in flight
@@ -277,7 +278,7 @@ template <int D>
 __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t* sv, int kb0,
                                              const uint4 (&qop)[2][D / 32], const int (&limit)[2],
                                              const bool (&masked)[2], float sl2e, int col,
-                                             int grp, float (&m_run)[2], float (&l_run)[2],
+                                             int grp, float (&m_run)[2], f32x4_t (&l_acc)[2],
                                              f32x4_t (&acc_o)[2][D / 16]) {
   constexpr int DSTEPS = D / 32;
   constexpr int DBLK = D / 16;
@@ -332,7 +333,10 @@ __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t*
       const float mn = fmaxf(m_run[b], tmax);
       const float corr = fast_exp2(m_run[b] - mn);
       m_run[b] = mn;
-      l_run[b] *= corr;
+      l_acc[b][0] *= corr;
+      l_acc[b][1] *= corr;
+      l_acc[b][2] *= corr;
+      l_acc[b][3] *= corr;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         acc_o[b][db][0] *= corr;
@@ -346,7 +350,6 @@ __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t*
     for (int k = 0; k < 2 * kKB; ++k) {
       const float p0 = fast_exp2(fmaf(sv[2 * k], sl2e, neg_m));
       const float p1 = fast_exp2(fmaf(sv[2 * k + 1], sl2e, neg_m));
-      l_run[b] += p0 + p1;
       const f32x2_t pf = {p0, p1};  // rounded once to bf16 (round to nearest even)
       pw[b][k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2e_t));
     }
@@ -360,10 +363,16 @@ __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t*
   // this lane's byte offset in the V tile (the rest is known per (ks, r, db))
   const int vlane = 16 * ((grp >> 1) * 8 * CPR + (4 * (grp & 1) + s / 4) * 2 + (s % 4) / 2) +
                     8 * (s % 2);
+  // Row sums: the same P^T operands times a 16 x 32 block of ones give, in
+  // every output element, the sum of the row's bf16 weights (the values the
+  // P.V products use), on the matrix cores instead of 32 VALU adds.
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 #pragma unroll
   for (int ks = 0; ks < kKB / 2; ++ks) {
     const uint4 pop0 = make_uint4(pw[0][4 * ks], pw[0][4 * ks + 1], pw[0][4 * ks + 2], pw[0][4 * ks + 3]);
     const uint4 pop1 = make_uint4(pw[1][4 * ks], pw[1][4 * ks + 1], pw[1][4 * ks + 2], pw[1][4 * ks + 3]);
+    l_acc[0] = mfma16x16x32(ones, pop0, l_acc[0]);
+    l_acc[1] = mfma16x16x32(ones, pop1, l_acc[1]);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       uint32_t w[4];
@@ -447,7 +456,10 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
   }
 
   f32x4_t acc_o[2][DBLK];
-  float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {kNegBig, kNegBig};
+  // row sums on the matrix cores (see tile_compute): every element of a
+  // lane's accumulator holds the sum of its query row
+  f32x4_t l_acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -493,7 +505,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
     if (tn < te) issue(tn, st == 0 ? kPfStages - 1 : st - 1);  // the stage of tile t - 1
     const int kb0 = t * kBN;
     const bool masked[2] = {kb0 + kBN - 1 > min_limit[0], kb0 + kBN - 1 > min_limit[1]};
-    tile_compute<D>(sm.k[st], sm.v[st], kb0, qop, limit, masked, sl2e, col, grp, m_run, l_run,
+    tile_compute<D>(sm.k[st], sm.v[st], kb0, qop, limit, masked, sl2e, col, grp, m_run, l_acc,
                     acc_o);
     st = st + 1 == kPfStages ? 0 : st + 1;
   }
@@ -509,7 +521,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int r = wave * kRowsPerWave + 16 * b + col;
-      const float lt = sum4rows(l_run[b]);
+      const float lt = l_acc[b][0];
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
         *reinterpret_cast<float4*>(po + (size_t)r * D + db * 16 + grp * 4) =
@@ -522,7 +534,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
   // ---- normalise and store ----
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const float lt = sum4rows(l_run[b]);
+    const float lt = l_acc[b][0];
     if (row_ok[b]) {
       const float inv = 1.f / lt;
       uint16_t* orow =
