@@ -3,9 +3,10 @@
 // Decode is HBM-bound: every key row of a (sequence, KV head) is read once and
 // used by all G query heads of its group (grouped-query attention: Helios blog,
 // "torch.sdpa and Flash Attention"), about 2*G flops per byte. The kernel is
-// written for that bound: VALU dot products (no matrix cores), 16-byte row
-// loads through the page table, the next buffer's loads in flight while the
-// current one computes, and the softmax kept online in registers.
+// written for that bound: 16-byte row loads through the page table, the next
+// buffer's loads in flight while the current one computes, and the softmax
+// kept online in registers. The float32 path below takes its dot products on
+// VALU; the bf16 path (pa_decode_mfma.h) puts the scores on matrix cores.
 //
 // Work decomposition. A work item is a key range of one row for one KV head
 // and is owned by ONE wave: no LDS, no workgroup barrier, so a wave never
@@ -387,9 +388,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
                                      min(ri.n_eff, kbeg + PT), part, nparts, kvh);
   } else {
     if constexpr (ET::kBytes == 2) {
-      decode_chunks_mfma<D, G>(a, blockIdx.x, gridDim.x, s_kreg);
+      decode_chunks_mfma<D, G>(a, blockIdx.x, s_kreg);
     } else {
-      decode_walk(a, blockIdx.x, gridDim.x,
+      decode_walk(a, blockIdx.x,
                   [&](int seq, int token, int pslot, int kbeg, int kend, int part, int nparts,
                       int kvh) {
                     decode_segment<ET, D, G, false>(a, seq, token, pslot, kbeg, kend, part, nparts,

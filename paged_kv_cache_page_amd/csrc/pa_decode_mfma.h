@@ -172,7 +172,7 @@ struct DecodeCursor {
     }
   }
 
-  __device__ __forceinline__ DecodeCursor(const AttnArgs& a, int wg, int n_wg) {
+  __device__ __forceinline__ DecodeCursor(const AttnArgs& a, int wg) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
     rows = reinterpret_cast<const int4*>(a.plan + po.rows);
@@ -187,7 +187,6 @@ struct DecodeCursor {
     n_static = a.plan[6];
     n_items = a.plan[7];
     Hkv = a.Hkv;
-    (void)n_wg;
     const int gw = wg * 4 + wave;
     kvh = gw % Hkv;
     chunk = gw / Hkv;
@@ -234,8 +233,8 @@ struct DecodeCursor {
 // seg(seq, token, pslot, kbeg, kend, part, nparts, kvh) for every range of the
 // wave's chunks, in order.
 template <typename Seg>
-__device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, int n_wg, Seg&& seg) {
-  DecodeCursor cur(a, wg, n_wg);
+__device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, Seg&& seg) {
+  DecodeCursor cur(a, wg);
   DecSeg d;
   while (cur.next(d)) seg(d.seq, d.token, d.pslot, d.kbeg, d.kend, d.part, d.nparts, d.kvh);
 }
@@ -243,8 +242,9 @@ __device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, int n_wg,
 // ---------------------------------------------------------------------------
 // bf16 work item with the scores on matrix cores. Per 16-key buffer:
 //   S^T[key, head] = K[key, :] . Q[head, :]   v_mfma_f32_16x16x32_bf16, A = K
-//   rows loaded straight into the A layout (lane l: key l % 16, dims 8(l/16) +
-//   32 ks ..), B = Q^T (lane l: head l % 16, zero for heads >= G). Lane (r, c)
+//   rows in the A layout (lane l: key l % 16, dims 8(l/16) + 32 ks ..; loaded
+//   as whole lines and rearranged through LDS, see kbuf_unit), B = Q^T (lane
+//   l: head l % 16, zero for heads >= G). Lane (r, c)
 //   (r = l / 16, c = l % 16) then holds the scores of keys 4r .. 4r + 3 for
 //   head c. One running max per head for the whole wave (combined over the
 //   four lanes of a head with permlane swaps), so the per-lane sums and output
@@ -662,11 +662,10 @@ __device__ __forceinline__ void decode_range_alone(const AttnArgs& a, const DecS
 // loaded during the previous range's last step. lds: kbuf_units<D>() 16-byte
 // units per wave of the workgroup (wave w uses the w-th block).
 template <int D, int G>
-__device__ __forceinline__ void decode_chunks_mfma(const AttnArgs& a, int wg, int n_wg,
-                                                   uint4* lds) {
+__device__ __forceinline__ void decode_chunks_mfma(const AttnArgs& a, int wg, uint4* lds) {
   uint4* kreg = lds + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kbuf_units<D>();
   const DecLane ln = dec_lane<D, G>(a);
-  DecodeCursor cur(a, wg, n_wg);
+  DecodeCursor cur(a, wg);
   DecSeg d;
   if (!cur.next(d)) return;
   DecPre<D, G> p = decode_prefetch<D, G>(a, d);

@@ -10,7 +10,9 @@
 //                 axis (each row padded to a multiple of A keys), cut into
 //                 equal chunks of C keys, one per decode wave: every wave gets
 //                 the same work however the lengths are spread (split-KV for
-//                 long rows, several short rows per chunk); with a fixed
+//                 long rows, several short rows per chunk); chunks past one
+//                 per wave (a fixed partition size, or chunks capped at the
+//                 largest partition) are claimed from a counter. With a fixed
 //                 partition size A = C = that size, so a chunk never spans
 //                 two rows and a row's partitions depend on the row alone.
 //                 A row of several partitions owns that many consecutive

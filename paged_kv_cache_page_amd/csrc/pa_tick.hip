@@ -16,8 +16,8 @@
 //     head's queue is empty it takes the other heads' items in turn. There is
 //     one queue per KV head; its cursor is a counter in the plan workspace,
 //     zeroed by the plan kernel and advanced with a device-scope atomic.
-// Split-KV partials of decode rows are merged afterwards by K3, as with the
-// decode kernel.
+// Split-KV partials of decode rows (K3's merge) and the pieces of cut prefill
+// items are merged afterwards by one reduce launch.
 #include "pa_decode_mfma.h"
 #include "pa_prefill_mfma.h"
 
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // decode workers stage K in the (not yet used) prefill tile buffers
   static_assert(sizeof(sm.k) >= 4 * kbuf_units<D>() * sizeof(uint4), "decode K staging fits");
   if ((int)blockIdx.x < a.dec_grid)
-    decode_chunks_mfma<D, G>(a, blockIdx.x, a.dec_grid, reinterpret_cast<uint4*>(sm.k));
+    decode_chunks_mfma<D, G>(a, blockIdx.x, reinterpret_cast<uint4*>(sm.k));
 
   const int4* items = reinterpret_cast<const int4*>(a.plan + plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf).pf);
   const int n_items = a.plan[1];
