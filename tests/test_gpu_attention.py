@@ -63,6 +63,8 @@ SMALL_CASES = [
     (W.BF16, 4, 2, 128, 16, (16, 32, 48), (16, 16, 16)),              # page-aligned chunks
     (W.BF16, 32, 4, 64, 16, (3000, 1, 700), (200, 1, 64)),            # long items cut into pieces
     (W.BF16, 16, 8, 128, 256, (5000, 2600), (300, 40)),               # pieces, group 2
+    (W.BF16, 8, 1, 128, 16, (500, 1, 300), (1, 1, 70)),               # one KV head, group 8
+    (W.BF16, 4, 4, 64, 32, (70, 900, 45), (1, 100, 45)),              # head_dim 64, group 1
     # 16-token pages cap a chunk at 63 pages (1008 keys): 160 k decode keys per KV head
     # make more chunks than the 128 decode waves of a head, claimed from the counter
     (W.BF16, 16, 8, 64, 16, (40000, 40000, 40000, 40000), (1, 1, 1, 1)),
