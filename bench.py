@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--kv-split", type=int, default=0)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="enqueue the step as three calls (slot mapping, RoPE + write, attention) "
+                         "instead of pa_tick_forward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM traffic counters)")
     args = ap.parse_args()
@@ -218,6 +221,12 @@ def main():
 
     def step(i):
         c = copies[i % ROTATE]
+        if not args.separate:
+            pa.pa_tick_forward(c["q"], c["k"], c["v"], c["pos"], c["bt"], c["sl"], c["qsl"], table,
+                               c["kp"], c["vp"], t.max_query_len, t.max_seq_len, scale=t.scale,
+                               kv_split_tokens=args.kv_split, out=c["out"],
+                               slot_mapping=c["slots"], workspace=ws, stream=stream)
+            return
         pa.pa_compute_slot_mapping(c["bt"], c["qsl"], c["pos"], t.P, t.num_pages, out=c["slots"],
                                    stream=stream)
         pa.pa_rope_and_cache_write(c["q"], c["k"], c["v"], c["pos"], c["slots"], table, c["kp"],
@@ -356,7 +365,8 @@ def main():
                    "decode_rows": int((t.query_lens == 1).sum()),
                    "chunks": [int(x) for x in t.query_lens[t.query_lens > 1]],
                    "heads_q_kv": [t.Hq, t.Hkv], "head_dim": t.D, "page_size": t.P,
-                   "pool_pages": t.num_pages, "seed": t.seed, "parallelism": "none (1 GPU)"},
+                   "pool_pages": t.num_pages, "seed": t.seed, "parallelism": "none (1 GPU)",
+                   "entry": "three calls" if args.separate else "pa_tick_forward"},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
         "kernel_sources_sha256": kernel_sources_digest(),
         "wall_s_timed_region": round(wall, 4), **extra,

@@ -11,8 +11,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer argument is DEVICE memory owned by the caller, unless the
- *   comment says otherwise. The library allocates nothing, frees nothing and
- *   never synchronises: it checks its host scalars, enqueues kernels on
+ *   comment says otherwise. The library allocates no memory, frees nothing
+ *   and never synchronises: it checks its host scalars, enqueues kernels on
  *   `stream` (a hipStream_t; NULL = the default stream) and returns.
  * - Return value: PA_OK, or an error code. A PA_ERR_INVALID_ARG or
  *   PA_ERR_UNSUPPORTED return enqueues nothing. Nothing aborts, throws or
@@ -178,6 +178,34 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
                                       int32_t max_seq_len, float scale, int32_t kv_split_tokens,
                                       pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/*
+ * pa_tick_forward -- one layer's whole tick in one call: exactly
+ *   pa_compute_slot_mapping(block_tables, query_start_loc, positions,
+ *                           slot_mapping, ...),
+ *   pa_rope_and_cache_write(q, k, v, positions, slot_mapping, cos_sin,
+ *                           k_pool, v_pool, ...),
+ *   pa_paged_attention_varlen(q, k_pool, v_pool, block_tables, seq_lens,
+ *                             query_start_loc, out, ...)
+ * in that order, with the same arguments, layouts, preconditions and results
+ * (q must not be NULL; slot_mapping [T] int32 is written), bit for bit. The
+ * tick's new K/V are stored before any attention read (Helios blog,
+ * "Continuous batching": all the tick's rows, prefill and decode, go through
+ * one forward). Enqueued as two launches fewer: the slot mapping, the page
+ * write and the attention call's planning (which reads only
+ * query_start_loc and seq_lens) share one launch, then the attention
+ * kernels follow on `stream`. Every check of the three calls is made before
+ * anything is enqueued.
+ */
+pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* positions,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, const float* cos_sin, void* k_pool,
+                            void* v_pool, void* out, int32_t* slot_mapping, int32_t S, int32_t T,
+                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_blocks_per_seq,
+                            int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
+                            float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing for benchmarks (not part of the tick). While on, every kernel

@@ -19,7 +19,7 @@ __all__ = [
     "PA_F32", "PA_BF16", "lib", "lib_path", "PaError",
     "pa_abi_version", "pa_status_string", "pa_rope_cos_sin_table", "pa_compute_slot_mapping",
     "pa_rope_and_cache_write", "pa_paged_attention_workspace_size", "pa_paged_attention_varlen",
-    "pa_profile_start", "pa_profile_stop", "pa_profile_reset",
+    "pa_tick_forward", "pa_profile_start", "pa_profile_stop", "pa_profile_reset",
 ]
 
 PA_F32 = 0
@@ -43,6 +43,9 @@ SIGNATURES = {
     "pa_paged_attention_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                          _i32, _vp, _sz, _vp]),
+    "pa_tick_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_profile_start": (_i32, [_i32]),
     "pa_profile_stop": (_i32, [ctypes.POINTER(_i32)]),
     "pa_profile_get": (_i32, [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(_f32)]),
@@ -241,6 +244,71 @@ def pa_paged_attention_varlen(q, k_pool, v_pool, block_tables, seq_lens, query_s
         _ptr(query_start_loc), _ptr(out), S, T, Hq, Hkv, D, P, num_pages, max_blocks,
         int(max_query_len), int(max_seq_len), float(scale), int(kv_split_tokens), dt,
         _ptr(workspace), ws_bytes, _stream(stream)), "pa_paged_attention_varlen")
+    return out
+
+
+def pa_tick_forward(q, k, v, positions, block_tables, seq_lens, query_start_loc, cos_sin,
+                    k_pool, v_pool, max_query_len, max_seq_len, scale=None, kv_split_tokens=0,
+                    out=None, slot_mapping=None, workspace=None, stream=None):
+    """One layer's tick in one call: slot mapping, RoPE + page write, attention.
+
+    Same as ``pa_compute_slot_mapping`` + ``pa_rope_and_cache_write`` +
+    ``pa_paged_attention_varlen`` with these arguments (q and k are rotated in
+    place); the attention's planning kernel overlaps the first two. Returns
+    ``out``; ``slot_mapping`` ``[T]`` int32 is written (allocated if None).
+    """
+    torch = _torch()
+    _dev(q, "q", ndim=3)
+    dt = _dtype_code(q)
+    _dev(k, "k", q.dtype, 3)
+    _dev(v, "v", q.dtype, 3)
+    _dev(positions, "positions", torch.int32, 1)
+    _dev(k_pool, "k_pool", q.dtype, 4)
+    _dev(v_pool, "v_pool", q.dtype, 4)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(query_start_loc, "query_start_loc", torch.int32, 1)
+    if cos_sin is not None:
+        _dev(cos_sin, "cos_sin", torch.float32, 2)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    S, max_blocks = block_tables.shape
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D):
+        raise ValueError("q/k/v shapes disagree")
+    if tuple(k_pool.shape) != (num_pages, P, Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("pool shape must be [num_pages, P, Hkv, D]")
+    if positions.shape[0] != T:
+        raise ValueError("positions needs one entry per token")
+    if seq_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("seq_lens needs S entries and query_start_loc S + 1")
+    max_pos = cos_sin.shape[0] if cos_sin is not None else 0
+    if cos_sin is not None and cos_sin.shape[1] != D:
+        raise ValueError("cos_sin must be [max_pos, head_dim]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, 3)
+    if slot_mapping is None:
+        slot_mapping = torch.empty(T, dtype=torch.int32, device=q.device)
+    _dev(slot_mapping, "slot_mapping", torch.int32, 1)
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping needs one entry per token")
+    need = pa_paged_attention_workspace_size(S, T, Hq, D, int(max_query_len), int(max_seq_len),
+                                             P, int(kv_split_tokens), dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_tick_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(block_tables), _ptr(seq_lens),
+        _ptr(query_start_loc), _ptr(cos_sin), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+        _ptr(slot_mapping), S, T, Hq, Hkv, D, P, num_pages, max_blocks, int(max_query_len),
+        int(max_seq_len), max_pos, float(scale), int(kv_split_tokens), dt, _ptr(workspace),
+        ws_bytes, _stream(stream)), "pa_tick_forward")
     return out
 
 

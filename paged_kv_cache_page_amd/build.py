@@ -18,8 +18,10 @@ LIB = os.path.join(HERE, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 # Per-file extra flags. The RoPE/cache-write unit rounds every product and sum
-# separately, so contraction into fused multiply-adds is off there.
-EXTRA = {"pa_rope_cache.hip": ["-ffp-contract=off"]}
+# separately, so contraction into fused multiply-adds is off there; it also
+# compiles the plan (pa_plan.h), which the plan kernel's unit then compiles
+# with the same flag.
+EXTRA = {"pa_rope_cache.hip": ["-ffp-contract=off"], "pa_plan.hip": ["-ffp-contract=off"]}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",

@@ -213,7 +213,7 @@ using namespace pa;
 #pragma GCC visibility push(default)
 extern "C" {
 
-int32_t pa_abi_version(void) { return 1; }
+int32_t pa_abi_version(void) { return 2; }
 
 const char* pa_status_string(pa_status_t status) {
   switch (status) {
@@ -234,26 +234,23 @@ pa_status_t pa_rope_cos_sin_table(float* cos_sin, int32_t max_pos, int32_t head_
   return from_hip(launch_rope_table(cos_sin, max_pos, head_dim, theta, (hipStream_t)stream));
 }
 
-pa_status_t pa_compute_slot_mapping(const int32_t* block_tables, const int32_t* query_start_loc,
-                                    const int32_t* positions, int32_t* slot_mapping, int32_t S,
-                                    int32_t T, int32_t max_blocks_per_seq, int32_t page_size,
-                                    int32_t num_pages, void* stream) {
+namespace {
+pa_status_t slot_mapping_check(const int32_t* block_tables, const int32_t* query_start_loc,
+                               const int32_t* positions, const int32_t* slot_mapping, int32_t S,
+                               int32_t T, int32_t max_blocks_per_seq, int32_t page_size,
+                               int32_t num_pages) {
   if (S < 0 || T < 0 || max_blocks_per_seq < 1 || page_size < 1 || num_pages < 1)
     return PA_ERR_INVALID_ARG;
   if ((long)num_pages * page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
   if (T > 0 && (S < 1 || !block_tables || !query_start_loc || !positions || !slot_mapping))
     return PA_ERR_INVALID_ARG;
-  return from_hip(launch_slot_mapping(block_tables, query_start_loc, positions, slot_mapping, S,
-                                      T, max_blocks_per_seq, page_size, num_pages,
-                                      (hipStream_t)stream));
+  return PA_OK;
 }
 
-pa_status_t pa_rope_and_cache_write(void* q, void* k, const void* v, const int32_t* positions,
-                                    const int32_t* slot_mapping, const float* cos_sin,
-                                    void* k_pool, void* v_pool, int32_t T, int32_t Hq,
-                                    int32_t Hkv, int32_t head_dim, int32_t page_size,
-                                    int32_t num_pages, int32_t max_pos, pa_dtype_t dtype,
-                                    void* stream) {
+pa_status_t rope_check(const void* q, const void* k, const void* v, const int32_t* positions,
+                       const int32_t* slot_mapping, const float* cos_sin, const void* k_pool,
+                       const void* v_pool, int32_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                       int32_t page_size, int32_t num_pages, int32_t max_pos, pa_dtype_t dtype) {
   if (!dtype_ok(dtype) || T < 0 || Hq < 0 || Hkv < 1 || head_dim < 1 || page_size < 1 ||
       num_pages < 1)
     return PA_ERR_INVALID_ARG;
@@ -267,6 +264,32 @@ pa_status_t pa_rope_and_cache_write(void* q, void* k, const void* v, const int32
   if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(k_pool) ||
       !aligned16(v_pool) || (cos_sin && !aligned16(cos_sin)))
     return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+}  // namespace
+
+pa_status_t pa_compute_slot_mapping(const int32_t* block_tables, const int32_t* query_start_loc,
+                                    const int32_t* positions, int32_t* slot_mapping, int32_t S,
+                                    int32_t T, int32_t max_blocks_per_seq, int32_t page_size,
+                                    int32_t num_pages, void* stream) {
+  const pa_status_t st = slot_mapping_check(block_tables, query_start_loc, positions,
+                                            slot_mapping, S, T, max_blocks_per_seq, page_size,
+                                            num_pages);
+  if (st != PA_OK) return st;
+  return from_hip(launch_slot_mapping(block_tables, query_start_loc, positions, slot_mapping, S,
+                                      T, max_blocks_per_seq, page_size, num_pages,
+                                      (hipStream_t)stream));
+}
+
+pa_status_t pa_rope_and_cache_write(void* q, void* k, const void* v, const int32_t* positions,
+                                    const int32_t* slot_mapping, const float* cos_sin,
+                                    void* k_pool, void* v_pool, int32_t T, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, int32_t page_size,
+                                    int32_t num_pages, int32_t max_pos, pa_dtype_t dtype,
+                                    void* stream) {
+  const pa_status_t st = rope_check(q, k, v, positions, slot_mapping, cos_sin, k_pool, v_pool, T,
+                                    Hq, Hkv, head_dim, page_size, num_pages, max_pos, dtype);
+  if (st != PA_OK || T == 0) return st;
   return from_hip(launch_rope_cache_write(dtype, q, k, v, positions, slot_mapping, cos_sin,
                                           k_pool, v_pool, T, Hq, Hkv, head_dim, page_size,
                                           num_pages, max_pos, (hipStream_t)stream));
@@ -283,15 +306,29 @@ size_t pa_paged_attention_workspace_size(int32_t S, int32_t T, int32_t Hq, int32
                              kv_split_tokens, dtype);
 }
 
-pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const void* v_pool,
-                                      const int32_t* block_tables, const int32_t* seq_lens,
-                                      const int32_t* query_start_loc, void* out, int32_t S,
-                                      int32_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                                      int32_t page_size, int32_t num_pages,
-                                      int32_t max_blocks_per_seq, int32_t max_query_len,
-                                      int32_t max_seq_len, float scale, int32_t kv_split_tokens,
-                                      pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+namespace {
+
+// One attention call prepared: its checked arguments and workspace layout.
+struct AttnCall {
+  AttnArgs a;
+  WsLayout wl;
+  pa_dtype_t dtype;
+  int G;
+  bool empty;  // nothing to enqueue (no rows)
+};
+
+// Every host-side check of pa_paged_attention_varlen, then the kernel
+// arguments. Enqueues nothing.
+pa_status_t attention_setup(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, void* out, int32_t S, int32_t T,
+                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_blocks_per_seq,
+                            int32_t max_query_len, int32_t max_seq_len, float scale,
+                            int32_t kv_split_tokens, pa_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes, AttnCall& c) {
+  c.empty = false;
+  c.dtype = dtype;
   if (!dtype_ok(dtype) || S < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || head_dim < 1 ||
       page_size < 1 || num_pages < 1 || max_blocks_per_seq < 1 || max_query_len < 0 ||
       max_seq_len < 0 || !isfinite(scale))
@@ -303,7 +340,11 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   const int G = Hq / Hkv;
   if (page_size < 16 || (page_size & (page_size - 1)) || !decode_supported(dtype, head_dim, G))
     return PA_ERR_UNSUPPORTED;  // pages: a power of two of at least 16 tokens
-  if (T == 0 || S == 0) return PA_OK;
+  c.G = G;
+  if (T == 0 || S == 0) {
+    c.empty = true;
+    return PA_OK;
+  }
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc || !out)
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
@@ -314,21 +355,23 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_pool, pool_bytes) ||
       overlap(out, qbytes, v_pool, pool_bytes))
     return PA_ERR_INVALID_ARG;
-  const WsLayout wl = workspace_layout(S, T, Hq, head_dim, max_query_len, max_seq_len,
-                                       page_size, kv_split_tokens, dtype);
-  const size_t need = wl.plan_bytes + wl.partial_bytes + wl.pf_bytes;
+  c.wl = workspace_layout(S, T, Hq, head_dim, max_query_len, max_seq_len, page_size,
+                          kv_split_tokens, dtype);
+  const size_t need = c.wl.plan_bytes + c.wl.partial_bytes + c.wl.pf_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && ((uintptr_t)workspace & 255u)) return PA_ERR_INVALID_ARG;
-  if (wl.cap_dec > INT32_MAX / 2 || wl.cap_pf > INT32_MAX / 2 || wl.part_slots > INT32_MAX / 2)
+  if (c.wl.cap_dec > INT32_MAX / 2 || c.wl.cap_pf > INT32_MAX / 2 ||
+      c.wl.part_slots > INT32_MAX / 2)
     return PA_ERR_INVALID_ARG;
   // decode rows are laid end to end on one int32 key axis (rows padded to at
   // most one partition)
-  if (!wl.token_mode &&
+  if (!c.wl.token_mode &&
       (long)S * ((long)max_seq_len + split_tokens(kv_split_tokens, page_size, false) + 16) >
           INT32_MAX)
     return PA_ERR_UNSUPPORTED;
 
-  AttnArgs a;
+  AttnArgs& a = c.a;
+  const WsLayout& wl = c.wl;
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -363,25 +406,91 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   a.pf_ws = (float*)((char*)workspace + wl.plan_bytes + wl.partial_bytes);
   a.pf_workers = (!wl.token_mode && wl.cap_pf > 0) ? tick_grid(dtype, head_dim, G) : 1;
 
-  hipStream_t s = (hipStream_t)stream;
+  return PA_OK;
+}
+
+// The plan kernel of a prepared call (seq mode only), on stream s.
+pa_status_t attention_plan(const AttnCall& c, hipStream_t s) {
+  if (c.empty || c.wl.token_mode) return PA_OK;
+  return launch_plan(c.a, c.a.plan, c.a.cap_dec, c.a.cap_pf, kPrefillRows / c.G, s) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+// The attention kernels of a prepared call after its plan, on stream s.
+pa_status_t attention_run(const AttnCall& c, hipStream_t s) {
+  if (c.empty) return PA_OK;
+  const AttnArgs& a = c.a;
   hipError_t e;
-  if (!wl.token_mode) {
-    e = launch_plan(a, a.plan, a.cap_dec, a.cap_pf, kPrefillRows / G, s);
-    if (e != hipSuccess) return PA_ERR_HIP;
-  }
-  if (!wl.token_mode && a.cap_pf > 0 && tick_supported(dtype, head_dim)) {
+  if (!c.wl.token_mode && a.cap_pf > 0 && tick_supported(c.dtype, a.D)) {
     // a tick that may hold prefill chunks: decode and prefill share one grid
-    e = launch_tick(dtype, a, s);
+    e = launch_tick(c.dtype, a, s);
     if (e != hipSuccess) return PA_ERR_HIP;
     return launch_tick_reduce(a, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
-  e = launch_decode(dtype, a, wl.token_mode, s);
+  e = launch_decode(c.dtype, a, c.wl.token_mode, s);
   if (e != hipSuccess) return PA_ERR_HIP;
   if (a.max_parts > 1) {
-    e = launch_split_reduce(dtype, a, wl.token_mode, s);
+    e = launch_split_reduce(c.dtype, a, c.wl.token_mode, s);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;
+}
+
+}  // namespace
+
+pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      const int32_t* query_start_loc, void* out, int32_t S,
+                                      int32_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t max_blocks_per_seq, int32_t max_query_len,
+                                      int32_t max_seq_len, float scale, int32_t kv_split_tokens,
+                                      pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  AttnCall c;
+  pa_status_t st = attention_setup(q, k_pool, v_pool, block_tables, seq_lens, query_start_loc,
+                                   out, S, T, Hq, Hkv, head_dim, page_size, num_pages,
+                                   max_blocks_per_seq, max_query_len, max_seq_len, scale,
+                                   kv_split_tokens, dtype, workspace, workspace_bytes, c);
+  if (st != PA_OK || c.empty) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  st = attention_plan(c, s);
+  return st != PA_OK ? st : attention_run(c, s);
+}
+
+pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* positions,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, const float* cos_sin, void* k_pool,
+                            void* v_pool, void* out, int32_t* slot_mapping, int32_t S, int32_t T,
+                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_blocks_per_seq,
+                            int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
+                            float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  // every check of the three calls before anything is enqueued
+  if (T > 0 && !q) return PA_ERR_INVALID_ARG;
+  pa_status_t st = slot_mapping_check(block_tables, query_start_loc, positions, slot_mapping, S,
+                                      T, max_blocks_per_seq, page_size, num_pages);
+  if (st != PA_OK) return st;
+  st = rope_check(q, k, v, positions, slot_mapping, cos_sin, k_pool, v_pool, T, Hq, Hkv,
+                  head_dim, page_size, num_pages, max_pos, dtype);
+  if (st != PA_OK) return st;
+  AttnCall c{};
+  st = attention_setup(q, k_pool, v_pool, block_tables, seq_lens, query_start_loc, out, S, T, Hq,
+                       Hkv, head_dim, page_size, num_pages, max_blocks_per_seq, max_query_len,
+                       max_seq_len, scale, kv_split_tokens, dtype, workspace, workspace_bytes, c);
+  if (st != PA_OK || T == 0) return st;
+
+  // One launch for the slot mapping, the page write and (seq mode) the plan,
+  // which reads only query_start_loc and seq_lens; then the attention kernels.
+  const bool plan = !c.empty && !c.wl.token_mode;
+  if (launch_tick_prep(dtype, q, k, v, positions, block_tables, query_start_loc, slot_mapping,
+                       cos_sin, k_pool, v_pool, S, T, Hq, Hkv, head_dim, page_size, num_pages,
+                       max_blocks_per_seq, max_pos, plan ? &c.a : nullptr, c.a.cap_dec,
+                       c.a.cap_pf, kPrefillRows / c.G, (hipStream_t)stream) != hipSuccess)
+    return PA_ERR_HIP;
+  return attention_run(c, (hipStream_t)stream);
 }
 
 pa_status_t pa_profile_start(int32_t capacity) {

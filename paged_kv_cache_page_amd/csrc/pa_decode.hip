@@ -16,7 +16,7 @@
 //
 // For the decode rows of a tick the plan kernel lays all rows end to end on
 // one key axis and cuts it into equal chunks, one per wave (see
-// pa_plan.hip): a wave walks the rows its chunk covers, one range per row, so
+// pa_plan.h): a wave walks the rows its chunk covers, one range per row, so
 // every wave gets the same number of keys whatever the spread of lengths
 // (decode_walk in pa_decode_mfma.h). The per-token mode (prefill rows without
 // a matrix-core kernel, i.e. float32) maps waves to (token, fixed partition,

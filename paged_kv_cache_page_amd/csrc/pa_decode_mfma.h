@@ -137,7 +137,7 @@ struct DecSeg {
 };
 
 // Walk of decode wave gw = 4 wg + wave over the chunks of the decode key axis
-// the plan kernel cut (see pa_plan.hip). Wave gw first takes chunk gw / Hkv
+// the plan kernel cut (see pa_plan.h). Wave gw first takes chunk gw / Hkv
 // of KV head gw % Hkv (the four waves of a workgroup serve different heads, so
 // every XCD streams several heads' rows at once); chunks past one per wave
 // are items t = (chunk, KV head) claimed from one shared counter, t -> head

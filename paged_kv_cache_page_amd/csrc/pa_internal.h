@@ -20,7 +20,7 @@ struct AttnArgs {
   const int32_t* qsl;
   void* out;
   float* ws;           // split-KV partials: o [part_slots*Hq*D], then (m, l) pairs
-  int* plan;           // work lists written by the plan kernel (see pa_plan.hip)
+  int* plan;           // work lists written by the plan (see pa_plan.h)
   int32_t cap_dec, cap_pf;  // capacities of the decode chunk and prefill item lists
   int32_t S, T, Hq, Hkv, D, P, num_pages, max_blocks;
   int32_t p_shift;      // log2(P); P is a power of two
@@ -115,6 +115,16 @@ hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* 
 // Work lists (pa_plan.hip). TM = tokens per prefill tile.
 hipError_t launch_plan(const AttnArgs& a, int* plan, int cap_dec, int cap_pf, int TM,
                        hipStream_t s);
+
+// a1 + K1 for every token of the tick and, when plan_args is given, the plan
+// of that attention call, in one launch (pa_rope_cache.hip). Same results as
+// launch_slot_mapping, launch_rope_cache_write and launch_plan.
+hipError_t launch_tick_prep(pa_dtype_t dt, void* q, void* k, const void* v, const int32_t* pos,
+                            const int32_t* bt, const int32_t* qsl, int32_t* slots,
+                            const float* cs, void* k_pool, void* v_pool, int S, int T, int Hq,
+                            int Hkv, int D, int P, int num_pages, int max_blocks, int max_pos,
+                            const AttnArgs* plan_args, int cap_dec, int cap_pf, int TM,
+                            hipStream_t s);
 
 // K2 + K3 (pa_decode.hip). token_mode = false: one row per decode sequence
 // (query length 1; other sequences skipped). token_mode = true: one row per

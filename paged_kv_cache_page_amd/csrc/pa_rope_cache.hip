@@ -9,6 +9,7 @@
 // sum on its own, so the stored K is a fixed function of its inputs.
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_plan.h"
 
 namespace pa {
 
@@ -133,24 +134,31 @@ struct RotPair<F32> {
 
 constexpr int kRopeThreads = 256;
 
+struct RopeArgs {
+  char* q;
+  char* k;
+  const char* v;
+  const int32_t* pos;
+  const float* cs;
+  char* k_pool;
+  char* v_pool;
+  int Hq, Hkv, D, P, num_pages, max_pos;
+};
+
+// K1 for token t, whose page slot is `slot` (stored only when in the pool).
 template <typename ET>
-__global__ __launch_bounds__(kRopeThreads) void rope_cache_write_kernel(
-    char* __restrict__ q, char* __restrict__ k, const char* __restrict__ v,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ slots,
-    const float* __restrict__ cs, char* __restrict__ k_pool, char* __restrict__ v_pool, int Hq,
-    int Hkv, int D, int P, int num_pages, int max_pos) {
+__device__ __forceinline__ void rope_token(const RopeArgs& r, int t, long slot) {
   constexpr int EB = ET::kBytes;
   constexpr int VP = RotPair<ET>::VP;       // elements per 16-byte vector
-  const int t = blockIdx.x;
+  const int D = r.D, Hkv = r.Hkv;
   const int half = D / 2;
   const int vec_half = half / VP;           // vectors per half row
   const int vec_row = D / VP;               // vectors per row
   const size_t row_bytes = (size_t)D * EB;
-  const int p = pos[t];
-  const bool rotate = cs != nullptr && p >= 0 && p < max_pos;
-  const long slot = slots[t];
-  const bool store = slot >= 0 && slot < (long)num_pages * P;
-  const int nq = q ? Hq : 0;
+  const int p = r.pos[t];
+  const bool rotate = r.cs != nullptr && p >= 0 && p < r.max_pos;
+  const bool store = slot >= 0 && slot < (long)r.num_pages * r.P;
+  const int nq = r.q ? r.Hq : 0;
   const int rot_tasks = (nq + Hkv) * vec_half;
   const int tasks = rot_tasks + Hkv * vec_row;
   // The block size is a multiple of vec_half (see the launch), so a
@@ -159,8 +167,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_cache_write_kernel(
   const int c = (int)threadIdx.x % vec_half;
   float cv[VP], sv[VP];
   if (rotate) {
-    const float4* cp = reinterpret_cast<const float4*>(cs + (size_t)p * D + c * VP);
-    const float4* sp = reinterpret_cast<const float4*>(cs + (size_t)p * D + half + c * VP);
+    const float4* cp = reinterpret_cast<const float4*>(r.cs + (size_t)p * D + c * VP);
+    const float4* sp = reinterpret_cast<const float4*>(r.cs + (size_t)p * D + half + c * VP);
 #pragma unroll
     for (int i = 0; i < VP / 4; ++i) {
       const float4 cc = cp[i], ss = sp[i];
@@ -173,8 +181,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_cache_write_kernel(
       const int h = task / vec_half;
       const bool is_k = h >= nq;
       const int kh = h - nq;
-      char* row = is_k ? k + ((size_t)t * Hkv + kh) * row_bytes
-                       : q + ((size_t)t * Hq + h) * row_bytes;
+      char* row = is_k ? r.k + ((size_t)t * Hkv + kh) * row_bytes
+                       : r.q + ((size_t)t * r.Hq + h) * row_bytes;
       uint4* p1 = reinterpret_cast<uint4*>(row + (size_t)c * 16);
       uint4* p2 = reinterpret_cast<uint4*>(row + (size_t)half * EB + (size_t)c * 16);
       uint4 a = *p1, b = *p2;
@@ -184,19 +192,33 @@ __global__ __launch_bounds__(kRopeThreads) void rope_cache_write_kernel(
         *p2 = b;
       }
       if (is_k && store) {
-        char* dst = k_pool + ((size_t)slot * Hkv + kh) * row_bytes;
+        char* dst = r.k_pool + ((size_t)slot * Hkv + kh) * row_bytes;
         *reinterpret_cast<uint4*>(dst + (size_t)c * 16) = a;
         *reinterpret_cast<uint4*>(dst + (size_t)half * EB + (size_t)c * 16) = b;
       }
     } else if (store) {
       const int j = task - rot_tasks;
       const int h = j / vec_row;
-      const int c = j % vec_row;
-      const uint4 x =
-          *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + h) * row_bytes + (size_t)c * 16);
-      *reinterpret_cast<uint4*>(v_pool + ((size_t)slot * Hkv + h) * row_bytes + (size_t)c * 16) = x;
+      const int cj = j % vec_row;
+      const uint4 x = *reinterpret_cast<const uint4*>(r.v + ((size_t)t * Hkv + h) * row_bytes +
+                                                      (size_t)cj * 16);
+      *reinterpret_cast<uint4*>(r.v_pool + ((size_t)slot * Hkv + h) * row_bytes +
+                                (size_t)cj * 16) = x;
     }
   }
+}
+
+template <typename ET>
+__global__ __launch_bounds__(kRopeThreads) void rope_cache_write_kernel(
+    RopeArgs r, const int32_t* __restrict__ slots) {
+  rope_token<ET>(r, blockIdx.x, slots[blockIdx.x]);
+}
+
+// Threads of a K1 workgroup: the largest multiple of the vectors per half row
+// (D / 16 for bf16, D / 8 for fp32) that fits the block.
+int rope_threads(pa_dtype_t dt, int D) {
+  const int vec_half = D / 2 / (dt == PA_BF16 ? 8 : 4);
+  return kRopeThreads / vec_half * vec_half;
 }
 
 hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* v,
@@ -204,20 +226,97 @@ hipError_t launch_rope_cache_write(pa_dtype_t dt, void* q, void* k, const void* 
                                    void* k_pool, void* v_pool, int T, int Hq, int Hkv, int D,
                                    int P, int num_pages, int max_pos, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  const RopeArgs r{(char*)q, (char*)k, (const char*)v, pos, cs, (char*)k_pool, (char*)v_pool,
+                   Hq, Hkv, D, P, num_pages, max_pos};
+  const int threads = rope_threads(dt, D);
   profile_before("rope_cache_write", s);
-  // threads: the largest multiple of the vectors per half row (D / 16 for
-  // bf16, D / 8 for fp32) that fits the block
-  const int vec_half = D / 2 / (dt == PA_BF16 ? 8 : 4);
-  const int threads = kRopeThreads / vec_half * vec_half;
-  if (dt == PA_BF16) {
-    hipLaunchKernelGGL(rope_cache_write_kernel<BF16>, dim3(T), dim3(threads), 0, s, (char*)q,
-                       (char*)k, (const char*)v, pos, slots, cs, (char*)k_pool, (char*)v_pool,
-                       Hq, Hkv, D, P, num_pages, max_pos);
-  } else {
-    hipLaunchKernelGGL(rope_cache_write_kernel<F32>, dim3(T), dim3(threads), 0, s, (char*)q,
-                       (char*)k, (const char*)v, pos, slots, cs, (char*)k_pool, (char*)v_pool,
-                       Hq, Hkv, D, P, num_pages, max_pos);
+  if (dt == PA_BF16)
+    hipLaunchKernelGGL(rope_cache_write_kernel<BF16>, dim3(T), dim3(threads), 0, s, r, slots);
+  else
+    hipLaunchKernelGGL(rope_cache_write_kernel<F32>, dim3(T), dim3(threads), 0, s, r, slots);
+  profile_after(s);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- a1 + K1 + plan -----
+// The tick's forward before attention, in one launch: workgroup 0's first
+// wave computes the attention plan (it reads only query_start_loc and
+// seq_lens), every other workgroup takes one token: finds its sequence and
+// page slot (a1; the slot is also stored), then rotates and writes it (K1).
+// The launch ends when the longer of the two is done, instead of running
+// slot mapping, page write and plan one after the other.
+
+// Last sequence s in [0, S) with qsl[s] <= t (0 if none): the same sequence
+// as a1's search when query_start_loc is non-decreasing. One wave, all lanes
+// together: each round tests 64 evenly spaced entries of the remaining range
+// and keeps the stretch between the last entry <= t and the next.
+__device__ __forceinline__ int wave_find_seq(const int32_t* __restrict__ qsl, int S, int t) {
+  const int lane = (int)threadIdx.x & 63;
+  int lo = 0, len = S;
+  while (len > 64) {
+    const int stride = (len + 63) / 64;
+    const bool le = lane * stride < len && qsl[lo + lane * stride] <= t;
+    const int c = __popcll(__ballot(le));
+    if (c == 0) return lo;
+    lo += (c - 1) * stride;
+    len = min(stride, len - (c - 1) * stride);
   }
+  const bool le = lane < len && qsl[lo + lane] <= t;
+  const int c = __popcll(__ballot(le));
+  return c == 0 ? lo : lo + c - 1;
+}
+
+// Fewer cached sequence shapes than the plan kernel: this LDS is reserved by
+// every workgroup of the launch, and the page-write workgroups need all their
+// compute unit's slots (8 KiB of cost bins + 12 B per cached sequence).
+constexpr int kPrepCachedSeqs = 960;
+
+template <typename ET>
+__global__ __launch_bounds__(kRopeThreads) void tick_prep_kernel(
+    RopeArgs r, const int32_t* __restrict__ bt, const int32_t* __restrict__ qsl,
+    int32_t* __restrict__ slots, int S, int max_blocks, AttnArgs a, int cap_dec, int cap_pf,
+    int TM, int plan_blocks) {
+  __shared__ PlanLds<kPrepCachedSeqs> sm;
+  if ((int)blockIdx.x < plan_blocks) {
+    if (threadIdx.x < 64) plan_wave(a, a.plan, cap_dec, cap_pf, TM, sm);
+    return;
+  }
+  const int t = (int)blockIdx.x - plan_blocks;
+  const int p = r.pos[t];
+  const int seq = wave_find_seq(qsl, S, t);
+  int slot = -1;
+  if (p >= 0) {
+    const int blk = p / r.P;
+    if (blk < max_blocks) {
+      const int page = bt[(size_t)seq * max_blocks + blk];
+      if (page >= 0 && page < r.num_pages) slot = page * r.P + p % r.P;
+    }
+  }
+  if (threadIdx.x == 0) slots[t] = slot;
+  rope_token<ET>(r, t, slot);
+}
+
+hipError_t launch_tick_prep(pa_dtype_t dt, void* q, void* k, const void* v, const int32_t* pos,
+                            const int32_t* bt, const int32_t* qsl, int32_t* slots,
+                            const float* cs, void* k_pool, void* v_pool, int S, int T, int Hq,
+                            int Hkv, int D, int P, int num_pages, int max_blocks, int max_pos,
+                            const AttnArgs* plan_args, int cap_dec, int cap_pf, int TM,
+                            hipStream_t s) {
+  const int plan_blocks = plan_args ? 1 : 0;
+  if (T + plan_blocks == 0) return hipSuccess;
+  const RopeArgs r{(char*)q, (char*)k, (const char*)v, pos, cs, (char*)k_pool, (char*)v_pool,
+                   Hq, Hkv, D, P, num_pages, max_pos};
+  AttnArgs a{};
+  if (plan_args) a = *plan_args;
+  const int threads = rope_threads(dt, D);
+  const dim3 grid((unsigned)(T + plan_blocks));
+  profile_before("tick_prep", s);
+  if (dt == PA_BF16)
+    hipLaunchKernelGGL(tick_prep_kernel<BF16>, grid, dim3(threads), 0, s, r, bt, qsl, slots, S,
+                       max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
+  else
+    hipLaunchKernelGGL(tick_prep_kernel<F32>, grid, dim3(threads), 0, s, r, bt, qsl, slots, S,
+                       max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
   profile_after(s);
   return hipGetLastError();
 }

@@ -46,7 +46,7 @@ def test_library_exports_nothing_else():
 
 
 def test_status_strings_and_version():
-    assert pa.pa_abi_version() == 1
+    assert pa.pa_abi_version() == 2
     for code in range(5):
         assert pa.pa_status_string(code).startswith("PA_")
     assert "UNKNOWN" in pa.pa_status_string(99)
@@ -190,3 +190,40 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.pa_profile_start(0) == INVALID
     assert lib.pa_profile_get(0, None, 0, None) == INVALID
     assert lib.pa_profile_reset() == OK
+
+
+def tick(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, bt=FAKE, seq_lens=FAKE, qsl=FAKE, cs=FAKE,
+                kp=FAKE, vp=FAKE, out=ctypes.c_void_p(0x900000000), slots=FAKE, S=4, T=4, Hq=8,
+                Hkv=2, D=128, P=256, num_pages=64, max_blocks=16, max_query_len=1,
+                max_seq_len=256, max_pos=4096, scale=0.1, split=0, dtype=BF16, ws=None,
+                ws_bytes=0, stream=None)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_tick_forward(
+        a["q"], a["k"], a["v"], a["pos"], a["bt"], a["seq_lens"], a["qsl"], a["cs"], a["kp"],
+        a["vp"], a["out"], a["slots"], a["S"], a["T"], a["Hq"], a["Hkv"], a["D"], a["P"],
+        a["num_pages"], a["max_blocks"], a["max_query_len"], a["max_seq_len"], a["max_pos"],
+        a["scale"], a["split"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),                     # the tick needs query rows
+    (dict(slots=None), INVALID),                 # slot mapping's checks
+    (dict(max_blocks=0), INVALID),
+    (dict(D=40), UNSUPPORTED),                   # the cache write's checks
+    (dict(max_pos=0), INVALID),
+    (dict(k=ctypes.c_void_p(0x10004)), INVALID),
+    (dict(Hq=7), INVALID),                       # the attention call's checks
+    (dict(P=24), UNSUPPORTED),
+    (dict(split=20), INVALID),
+    (dict(max_query_len=64, max_seq_len=4096), WS_SMALL),
+])
+def test_tick_forward_rejects_bad_host_arguments(kw, code):
+    # every check of the three calls runs before anything is enqueued, so no
+    # pointer here is dereferenced and no GPU is needed
+    assert tick(**kw) == code
+
+
+def test_tick_forward_empty_tick_is_ok_without_touching_memory():
+    assert tick(T=0) == OK

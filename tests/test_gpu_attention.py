@@ -211,3 +211,54 @@ def test_profile_hook_records_kernels():
     assert "plan" in names and "tick_attention" in names
     assert all(ms > 0 for _, ms in rec)
     pa.pa_profile_reset()
+
+
+def _bits(x):
+    return x.view(torch.int16 if x.element_size() == 2 else torch.int32).cpu().numpy()
+
+
+def _many_seqs_tick(seed, S):
+    """S short sequences, mostly decode rows, some chunks of up to 7 tokens and
+    some with no rows this tick (runs of equal query_start_loc entries)."""
+    rng = np.random.default_rng(seed)
+    sl = rng.integers(1, 200, size=S)
+    ql = np.ones(S, np.int64)
+    ql[::50] = np.minimum(sl[::50], 7)
+    ql[3::17] = 0
+    return W.build_tick(rng, name=f"many{S}", dtype=W.BF16, Hq=4, Hkv=2, D=64, P=16,
+                        seq_lens=list(sl), query_lens=list(ql), theta=1e4, poison=True)
+
+
+@pytest.mark.parametrize("which", ["cfg4", "cfg3", "cfg5", "small0", "small_f32", "split512",
+                                   "many100", "many1100", "many4500"])
+def test_tick_forward_equals_the_three_calls_bitwise(which):
+    """pa_tick_forward (slot mapping, page write and plan in one launch) ==
+    the three calls in order; the many-sequence ticks take the token search
+    over more than 64 and more than 4096 sequences and the plan past its
+    cached sequence shapes."""
+    if which.startswith("cfg"):
+        t = W.make_config(int(which[3:]), poison=True)
+    elif which == "small_f32":   # the per-token path: no plan
+        t = _small(120, *SMALL_CASES[10])
+    elif which.startswith("many"):
+        t = _many_seqs_tick(122, int(which[4:]))
+    else:
+        t = _small(121, *SMALL_CASES[0])
+    assert not t.new_in_pool
+    split = 512 if which == "split512" else 0
+    say("tick forward", which)
+    a = DevTick(t).write()
+    ref = a.attend(split)
+    b = DevTick(t)
+    table = pa.pa_rope_cos_sin_table(t.max_pos, t.D, t.theta, device=DEV) if t.theta else None
+    slots = torch.full((t.T,), -7, dtype=torch.int32, device=DEV)
+    out = pa.pa_tick_forward(b.q, b.k, b.v, b.positions, b.block_tables, b.seq_lens, b.qsl,
+                             table, b.k_pool, b.v_pool, t.max_query_len, t.max_seq_len,
+                             scale=t.scale, kv_split_tokens=split, slot_mapping=slots)
+    torch.cuda.synchronize()
+    for name, x, y in (("out", ref, out), ("slots", a.slots, slots), ("q", a.q, b.q),
+                       ("k", a.k, b.k), ("k_pool", a.k_pool, b.k_pool),
+                       ("v_pool", a.v_pool, b.v_pool)):
+        assert np.array_equal(_bits(x), _bits(y)), f"{which}: {name} differs"
+    if which.startswith("many"):  # these sizes are not among the parity cases above
+        check_attention(out, oracle_tick(t), t.dtype, which)
