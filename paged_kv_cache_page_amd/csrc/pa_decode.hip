@@ -362,8 +362,8 @@ __device__ __forceinline__ void decode_segment(const AttnArgs& a, int seq, int t
 
 template <typename ET, int D, int G, bool TOKEN_MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
-  // bf16: each wave's K staging region (see mfma_load)
-  __shared__ uint4 s_kreg[ET::kBytes == 2 ? kWaves * kbuf_units<(D >= 64 ? D : 64)>() : 1];
+  // bf16: each wave's K/V buffers in LDS (see dec_issue)
+  __shared__ uint4 s_kreg[ET::kBytes == 2 ? kWaves * dec_region_units<(D >= 64 ? D : 64)>() : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (TOKEN_MODE) {
     const long unit = (long)blockIdx.x * kWaves + wave;
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     {
       const DecSeg d{ri.seq, row, row * a.max_parts, kbeg, min(ri.n_eff, kbeg + PT), part,
                      nparts, kvh};
-      decode_range_alone<D, G>(a, d, s_kreg + wave * kbuf_units<D>());
+      decode_range_alone<D, G>(a, d, s_kreg + wave * dec_region_units<D>());
     }
     else
       decode_segment<ET, D, G, true>(a, ri.seq, row, row * a.max_parts, kbeg,

@@ -240,61 +240,55 @@ __device__ __forceinline__ void decode_walk(const AttnArgs& a, int wg, Seg&& seg
 }
 
 // ---------------------------------------------------------------------------
-// bf16 work item with the scores on matrix cores. Per 16-key buffer:
+// bf16 work item on matrix cores. Per 16-key buffer:
 //   S^T[key, head] = K[key, :] . Q[head, :]   v_mfma_f32_16x16x32_bf16, A = K
-//   rows in the A layout (lane l: key l % 16, dims 8(l/16) + 32 ks ..; loaded
-//   as whole lines and rearranged through LDS, see kbuf_unit), B = Q^T (lane
-//   l: head l % 16, zero for heads >= G). Lane (r, c)
-//   (r = l / 16, c = l % 16) then holds the scores of keys 4r .. 4r + 3 for
-//   head c. One running max per head for the whole wave (combined over the
-//   four lanes of a head with permlane swaps), so the per-lane sums and output
-//   accumulators of different lanes can be added without rescaling.
-//   P.V stays on v_dot2: V row (key) slot * UNROLL + u of the buffer sits in
-//   the LPK lanes of `slot`; its weights are the (bf16-packed) scores of lane
-//   (slot * UNROLL / 4, head), broadcast along the 16-lane row with DPP
-//   row_newbcast.
+//   rows in the A layout (lane l: key l % 16, dims 8 (l / 16) + 32 ks ..), B =
+//   Q^T (lane l: head l % 16, zero for heads >= G). Lane (r, c) (r = l / 16,
+//   c = l % 16) then holds the scores of keys 4r .. 4r + 3 for head c. One
+//   running max per head for the whole wave (combined over the four lanes of a
+//   head with permlane swaps), so the per-lane sums can be added without
+//   rescaling.
+//   O^T[dim, head] += V^T[dim, key] . P^T[key, head]   v_mfma_f32_16x16x16_bf16
+//   per 16 dims: B = the lane's own bf16 weights (keys 4r .. 4r + 3 of head c:
+//   the score layout as it stands), A = V^T, read transposed from LDS with
+//   ds_read_b64_tr_b16 (lane (r, c) reads key 4r + c / 4, dims 16 db +
+//   4 (c % 4) .. + 3; the instruction exchanges 16-bit elements within each
+//   16-lane group so that lane (r, c) receives dim 16 db + c of keys 4r ..
+//   4r + 3). The accumulators keep that layout: lane (r, c) holds dims
+//   16 db + 4r .. + 3 of head c, final after the last key.
+// K and V of a buffer go from HBM straight into the wave's own LDS region
+// with global_load_lds_dwordx4 (no registers), two buffers deep: the next
+// buffer's loads are in flight while one is computed.
 template <int D, int G>
 struct MfmaDecodeShape {
   static constexpr int ROWB = D * 2;
-  static constexpr int KSTEPS = D / 32;      // k-steps of the score MFMA
-  static constexpr int LPK = ROWB / 16;      // lanes per V row (16 bytes each)
-  static constexpr int NSLOT = 64 / LPK;     // V rows per step
-  static constexpr int UNROLL = 16 / NSLOT;  // steps per 16-key buffer
-  static constexpr int NPAIR = UNROLL / 2;
+  static constexpr int KSTEPS = D / 32;       // k-steps of the score MFMA
+  static constexpr int BUF = 16 * ROWB;       // bytes of one 16-key buffer of K (or V)
+  static constexpr int NQ = BUF / 1024;       // load instructions per matrix per buffer
+  static constexpr int NDMA = 2 * NQ;         // load instructions per buffer (K and V)
   static_assert(D == 64 || D == 128, "bf16 head dims 64 and 128");
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per KV head");
 };
 
+// One wave's LDS region: buffers 0 and 1, each K then V.
+template <int D>
+constexpr int dec_region_bytes() { return 4 * 16 * D * 2; }
+template <int D>
+constexpr int dec_region_units() { return dec_region_bytes<D>() / 16; }
 
-template <int N>
-__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
-}
-
-template <int D, int G>
-struct MfmaBuf {
-  uint4 k[MfmaDecodeShape<D, G>::KSTEPS];
-  uint4 v[MfmaDecodeShape<D, G>::UNROLL];
-};
-
-// K rows of a 16-key buffer are loaded as whole 128-byte lines (8 lanes per
-// line, 8 keys per load instruction): loads laid out for the MFMA A operand
-// directly (16 keys x 64 bytes per instruction) streamed at ~4.8 TB/s against
-// ~6.3 TB/s for whole lines on MI355X. Load i of a lane holds key
-// 8 (i / (D / 64)) + lane / 8, 16-byte chunk 8 (i % (D / 64)) + lane % 8; the
-// wave passes the buffer through its own 16-key LDS region to put it in the
-// operand layout (mfma_compute). Unit (16 bytes) of key k, chunk c there:
+// K buffer layout, in 16-byte units, of key k, chunk c (8 dims):
 //   64 ((D / 64) (k / 8) + c / 8) + 8 (k % 8) + ((c % 8) ^ (k / 2) ^ 4 (k % 2)) % 8
-// Writes cover whole 128-byte runs, and the operand reads (lane l: key l % 16,
-// chunk 4 ks + l / 16) hit distinct banks whether 8 or 16 lanes are served a
-// cycle.
+// The operand reads (lane l: key l % 16, chunk 4 ks + l / 16) hit distinct
+// banks whether 8 or 16 lanes are served a cycle. A load instruction q fills
+// units 64 q .. 64 q + 63 (lane j: unit 64 q + j), so lane j of load q fetches
+// the key and chunk that unit holds.
 template <int D>
 __device__ __forceinline__ int kbuf_unit(int k, int c) {
   return 64 * ((D / 64) * (k >> 3) + (c >> 3)) + 8 * (k & 7) + (((c & 7) ^ (k >> 1) ^ ((k & 1) << 2)) & 7);
 }
-// 16-byte units of one wave's K region
-template <int D>
-constexpr int kbuf_units() { return 16 * D * 2 / 16; }
+// V buffer layout: rows of 2 D bytes, the 32-byte blocks of key k's row
+// permuted by k % 4 (XOR), so that the transposed reads of four keys' same dims
+// hit different banks: unit of key k, chunk c at k (D / 8) + 2 ((c / 2) ^ (k % 4)) + c % 2.
 
 // Where a range's 16-key buffers come from.
 struct DecSrc {
@@ -306,21 +300,37 @@ struct DecSrc {
   int nbuf;           // 16-key buffers (>= 1)
 };
 
-// Per-lane offsets of the K and V loads within a 16-key buffer.
+// Per-lane source offsets of the K and V loads within a 16-key buffer (one
+// per load instruction), and the wave's LDS region.
+template <int D, int G>
 struct DecLane {
   size_t slot_stride;  // bytes between consecutive slots of a page
-  uint32_t k_off, v_off;
+  uint32_t k_off[MfmaDecodeShape<D, G>::NQ], v_off[MfmaDecodeShape<D, G>::NQ];
+  uint32_t lds;        // LDS byte address of the wave's region (wave-uniform)
+  char* region;        // the same region as a pointer
 };
 
 template <int D, int G>
-__device__ __forceinline__ DecLane dec_lane(const AttnArgs& a) {
+__device__ __forceinline__ DecLane<D, G> dec_lane(const AttnArgs& a, uint4* region) {
   typedef MfmaDecodeShape<D, G> SH;
-  const int lane = threadIdx.x & 63;
-  const int slot = lane / SH::LPK, sub = lane % SH::LPK;
-  DecLane l;
+  const int j = threadIdx.x & 63;
+  DecLane<D, G> l;
   l.slot_stride = (size_t)a.Hkv * SH::ROWB;
-  l.k_off = (uint32_t)((lane >> 3) * l.slot_stride) + 16 * (lane & 7);
-  l.v_off = (uint32_t)(slot * SH::UNROLL * l.slot_stride) + 16 * sub;
+#pragma unroll
+  for (int q = 0; q < SH::NQ; ++q) {
+    // K: the inverse of kbuf_unit for unit 64 q + j
+    const int kq = q / (D / 64), cq = q % (D / 64);
+    const int k = 8 * kq + (j >> 3);
+    const int c = 8 * cq + (((j & 7) ^ (k >> 1) ^ ((k & 1) << 2)) & 7);
+    l.k_off[q] = (uint32_t)(k * l.slot_stride) + 16 * c;
+    // V: unit 64 q + j of the row-major, block-permuted layout
+    const int u = 64 * q + j, key = u / (D / 8), w = u % (D / 8);
+    const int cv = 2 * ((w >> 1) ^ (key & 3)) + (w & 1);
+    l.v_off[q] = (uint32_t)(key * l.slot_stride) + 16 * cv;
+  }
+  l.region = reinterpret_cast<char*>(region);
+  l.lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)l.region);
   return l;
 }
 
@@ -337,52 +347,79 @@ __device__ __forceinline__ DecSrc dec_src(const AttnArgs& a, const DecSeg& d, in
   return s;
 }
 
-// Issue the loads of buffer x of range s (past its end: its last buffer). A
-// 16-key buffer never crosses a page (kbeg is a multiple of 16, P >= 16).
+// One 16-byte-per-lane load from global memory (wave-uniform base + per-lane
+// 32-bit offset) into LDS (lane j's 16 bytes at byte lds + 16 j; lds in M0).
+// Inline assembly, so the compiler's wait insertion does not make later LDS
+// reads wait for it: the walk waits for these loads itself (dec_wait). The
+// "memory" clobber keeps other memory accesses on their side of it; M0 is
+// set right before each compiler use of it and holds nothing across code.
+__device__ __forceinline__ void dec_dma16(const char* base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(bs),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (gfx9 s_waitcnt: vmcnt[3:0] and [15:14]; lgkm and export
+// counters left at their maxima), then keep the compiler from moving memory
+// accesses across.
+template <int N>
+__device__ __forceinline__ void dec_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Issue the loads of buffer x of range s (past its end: its last buffer) into
+// LDS buffer `buf` of the wave's region. A 16-key buffer never crosses a page
+// (kbeg is a multiple of 16, P >= 16).
 template <int D, int G>
-__device__ __forceinline__ void mfma_load(MfmaBuf<D, G>& b, const AttnArgs& a, const DecSrc& s,
-                                          int x, const DecLane& ln) {
+__device__ __forceinline__ void dec_issue(const AttnArgs& a, const DecSrc& s, int x, int buf,
+                                          const DecLane<D, G>& ln) {
   typedef MfmaDecodeShape<D, G> SH;
   const int kb = s.kbeg + 16 * min(x, s.nbuf - 1);
   int page = __builtin_amdgcn_readlane(s.page_raw, (kb >> a.p_shift) - s.pg0);
   page = min(max(page, 0), a.num_pages - 1);
   const int row0 = kb & ((1 << a.p_shift) - 1);
   const size_t step_off = (((size_t)page << a.p_shift) + row0) * ln.slot_stride;
-  const char* kp = s.kbase + step_off + ln.k_off;
+  const uint32_t lk = ln.lds + (uint32_t)(2 * SH::BUF * buf), lv = lk + SH::BUF;
 #pragma unroll
-  for (int i = 0; i < SH::KSTEPS; ++i)
-    b.k[i] = *reinterpret_cast<const uint4*>(kp + (size_t)(8 * (i / (D / 64))) * ln.slot_stride +
-                                             128 * (i % (D / 64)));
-  const char* vp = s.vbase + step_off + ln.v_off;
-#pragma unroll
-  for (int u = 0; u < SH::UNROLL; ++u)
-    b.v[u] = *reinterpret_cast<const uint4*>(vp + (size_t)u * ln.slot_stride);
-}
-
-__device__ __forceinline__ uint32_t word_of4(const uint4& v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+  for (int q = 0; q < SH::NQ; ++q) {
+    dec_dma16(s.kbase + step_off, ln.k_off[q], lk + 1024 * q);
+    dec_dma16(s.vbase + step_off, ln.v_off[q], lv + 1024 * q);
+  }
 }
 
 template <int D, int G>
-__device__ __forceinline__ void mfma_compute(MfmaBuf<D, G>& b, const uint4 (&qb)[D / 32],
-                                             float& m_run, float& l_part, float (&o)[G][8],
-                                             int kb, int kend, int rrow, int slot, float sl2e,
-                                             float bias, uint4* kreg) {
+__device__ __forceinline__ void mfma_compute(const DecLane<D, G>& ln, int buf,
+                                             const uint4 (&qb)[D / 32], float& m_run,
+                                             float& l_part, f32x4_t (&oacc)[D / 16], int kb,
+                                             int kend, int rrow, float sl2e, float bias) {
   typedef MfmaDecodeShape<D, G> SH;
-  // K through the wave's LDS region into the A-operand layout (lane l: key
-  // l % 16, dims 8 (l / 16) + 32 ks ..). Only this wave touches the region and
-  // its LDS accesses run in order, so no barrier is needed.
-  // (an explicit LDS pointer: through a generic one the compiler could not
-  // rule out aliasing with the register buffers and kept them in scratch)
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  lds_u32x4* kl = (lds_u32x4*)kreg;
+  typedef short v4i16_dec __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
+  char* kbuf = ln.region + 2 * SH::BUF * buf;
+  char* vbuf = kbuf + SH::BUF;
+  // Keys past the range end (only in the last buffer; wave-uniform test):
+  // their V rows (which may hold anything) are zeroed before the products,
+  // and their scores get no weight below.
+  if (kb + 16 > kend) {
 #pragma unroll
-  for (int i = 0; i < SH::KSTEPS; ++i)
-    kl[kbuf_unit<D>(8 * (i / (D / 64)) + (lane >> 3), 8 * (i % (D / 64)) + (lane & 7))] =
-        __builtin_bit_cast(u32x4_t, b.k[i]);
+    for (int q = 0; q < SH::NQ; ++q) {
+      const int u = 64 * q + lane;
+      if (kb + u / (D / 8) >= kend)
+        *(lds_u32x4*)(vbuf + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
   uint4 kop[SH::KSTEPS];
+  const lds_u32x4* kl = (const lds_u32x4*)kbuf;
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)
     kop[ks] = __builtin_bit_cast(uint4, kl[kbuf_unit<D>(lane & 15, 4 * ks + (lane >> 4))]);
@@ -396,17 +433,9 @@ __device__ __forceinline__ void mfma_compute(MfmaBuf<D, G>& b, const uint4 (&qb)
   float s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = fmaf(acc[i], sl2e, bias);
-  // Keys past the range end (only in the last buffer; wave-uniform test):
-  // no weight, and their V rows (which may hold anything) zeroed.
   if (kb + 16 > kend) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = kb + 4 * rrow + i < kend ? s[i] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < SH::UNROLL; ++u) {
-      const bool ok = kb + slot * SH::UNROLL + u < kend;
-      b.v[u] = make_uint4(ok ? b.v[u].x : 0u, ok ? b.v[u].y : 0u, ok ? b.v[u].z : 0u,
-                          ok ? b.v[u].w : 0u);
-    }
   }
   float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   {
@@ -417,30 +446,19 @@ __device__ __forceinline__ void mfma_compute(MfmaBuf<D, G>& b, const uint4 (&qb)
                                               false);
     mb = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
   }
-  // Rescale only when some head's running max grows (rare after the first keys).
+  // Rescale only when some head's running max grows (rare after the first
+  // keys). Lane (r, c) holds head c's accumulators and running max.
   if (__any(mb > m_run)) {
     const float mn = fmaxf(m_run, mb);
     const float corr = fast_exp2(m_run - mn);
     m_run = mn;
     l_part *= corr;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float ch;
-      if constexpr (true) {
-        const uint32_t cu = __float_as_uint(corr);
-        switch (h) {
-          case 0: ch = __uint_as_float(row_bcast<0>(cu)); break;
-          case 1: ch = __uint_as_float(row_bcast<1>(cu)); break;
-          case 2: ch = __uint_as_float(row_bcast<2>(cu)); break;
-          case 3: ch = __uint_as_float(row_bcast<3>(cu)); break;
-          case 4: ch = __uint_as_float(row_bcast<4>(cu)); break;
-          case 5: ch = __uint_as_float(row_bcast<5>(cu)); break;
-          case 6: ch = __uint_as_float(row_bcast<6>(cu)); break;
-          default: ch = __uint_as_float(row_bcast<7>(cu)); break;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[h][i] *= ch;
+    for (int db = 0; db < D / 16; ++db) {
+      oacc[db][0] *= corr;
+      oacc[db][1] *= corr;
+      oacc[db][2] *= corr;
+      oacc[db][3] *= corr;
     }
   }
   // weights rounded to bf16 once; the sum uses the same rounded values
@@ -450,62 +468,25 @@ __device__ __forceinline__ void mfma_compute(MfmaBuf<D, G>& b, const uint4 (&qb)
   const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2e_t));
   l_part += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
 
-  // V rows of steps (2j, 2j+1) interleaved per dim for v_dot2
-  uint32_t vlo[SH::NPAIR][4], vhi[SH::NPAIR][4];
+  const v4i16_dec pop = __builtin_bit_cast(v4i16_dec, make_uint2(w01, w23));
+  const int rk = 4 * rrow + ((lane & 15) >> 2);  // key this lane's reads start from
 #pragma unroll
-  for (int j = 0; j < SH::NPAIR; ++j)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      vlo[j][w] = __builtin_amdgcn_perm(word_of4(b.v[2 * j + 1], w), word_of4(b.v[2 * j], w),
-                                        0x05040100u);
-      vhi[j][w] = __builtin_amdgcn_perm(word_of4(b.v[2 * j + 1], w), word_of4(b.v[2 * j], w),
-                                        0x07060302u);
-    }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    uint32_t b01, b23;
-    switch (h) {
-      case 0: b01 = row_bcast<0>(w01); b23 = row_bcast<0>(w23); break;
-      case 1: b01 = row_bcast<1>(w01); b23 = row_bcast<1>(w23); break;
-      case 2: b01 = row_bcast<2>(w01); b23 = row_bcast<2>(w23); break;
-      case 3: b01 = row_bcast<3>(w01); b23 = row_bcast<3>(w23); break;
-      case 4: b01 = row_bcast<4>(w01); b23 = row_bcast<4>(w23); break;
-      case 5: b01 = row_bcast<5>(w01); b23 = row_bcast<5>(w23); break;
-      case 6: b01 = row_bcast<6>(w01); b23 = row_bcast<6>(w23); break;
-      default: b01 = row_bcast<7>(w01); b23 = row_bcast<7>(w23); break;
-    }
-    uint32_t pw[SH::NPAIR];
-    if constexpr (SH::UNROLL == 4) {
-      // keys 4 slot + u: elements (0,1) and (2,3) of the row's score lane
-      pw[0] = b01;
-      pw[1] = b23;
-    } else {
-      // keys 2 slot + u: elements (0,1) for even slots, (2,3) for odd ones
-      pw[0] = (slot & 1) ? b23 : b01;
-    }
-#pragma unroll
-    for (int j = 0; j < SH::NPAIR; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        o[h][2 * w] = dot2_bf16(pw[j], vlo[j][w], o[h][2 * w]);
-        o[h][2 * w + 1] = dot2_bf16(pw[j], vhi[j][w], o[h][2 * w + 1]);
-      }
+  for (int db = 0; db < D / 16; ++db) {
+    const char* src = vbuf + rk * 2 * D + 32 * (db ^ (rk & 3)) + 8 * (lane & 3);
+    const v4i16_dec vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_dec*)(src));
+    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, oacc[db], 0, 0, 0);
   }
 }
 
 template <int N>
 __device__ __forceinline__ float lane_sum_xor(float x) {
-  if constexpr (N == 16 || N == 32) {
-    auto r = N == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false)
-                     : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  } else {
-    static_assert(N == 8, "xor 8, 16 or 32");
-    const float other = dpp_f<0x128>(x);  // row_ror:8 = lane ^ 8
-    return (threadIdx.x & 8) ? other + x : x + other;
-  }
+  static_assert(N == 16 || N == 32, "xor 16 or 32");
+  auto r = N == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false)
+                   : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // The loads a range needs before its first K/V buffer: the page ids of its
@@ -538,157 +519,123 @@ __device__ __forceinline__ DecPre<D, G> decode_prefetch(const AttnArgs& a, const
   return p;
 }
 
-// One decode range on a wave. b0 holds (its loads issued) buffer 0 of the
-// range; the two register buffers alternate, the loads of the next buffer in
-// flight while one computes. The range's last step loads buffer 0 of the next
-// range sn into the other buffer, so the stream does not drain between
-// ranges (after the last range, sn is the range itself: a re-read of one
-// buffer). That is b1 when the range has an odd number of buffers: the
-// caller then passes the buffers swapped for the next range.
+// One decode range on a wave. Buffer 0 of the range has been issued into LDS
+// buffer buf0; the two LDS buffers alternate, the loads of the next buffer in
+// flight while one computes. The range's last step issues buffer 0 of the
+// next range sn, so the stream does not drain between ranges (after the last
+// range, sn is the range itself: a re-read of one buffer). Returns the LDS
+// buffer that holds it.
 template <int D, int G>
-__device__ __forceinline__ void decode_range(const AttnArgs& a, MfmaBuf<D, G>& b0,
-                                             MfmaBuf<D, G>& b1, const DecSeg& d,
-                                             const DecPre<D, G>& pre, const DecSrc& s,
-                                             const DecSrc& sn, const DecLane& ln, uint4* kreg) {
+__device__ __forceinline__ int decode_range(const AttnArgs& a, int buf0, const DecSeg& d,
+                                            const DecPre<D, G>& pre, const DecSrc& s,
+                                            const DecSrc& sn, const DecLane<D, G>& ln) {
   typedef MfmaDecodeShape<D, G> SH;
-  constexpr int LPK = SH::LPK, NSLOT = SH::NSLOT;
   const int lane = threadIdx.x & 63;
   const int rrow = lane >> 4, col = lane & 15;  // score layout: keys 4 rrow.., head col
-  const int slot = lane / LPK, sub = lane % LPK;  // V layout
 
-  // Q^T operand, zero in the lanes of heads >= G
+  // Q^T operand, zero in the lanes of heads >= G. Its loads (and the page ids)
+  // were issued with the previous range: they are waited for here, before the
+  // next buffer's loads are issued, so that wait does not include those.
   uint4 qb[SH::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)
     qb[ks] = col < G ? pre.qb[ks] : make_uint4(0u, 0u, 0u, 0u);
   const float bias = col < G ? 0.f : -INFINITY;
+  __builtin_amdgcn_sched_barrier(0);
 
   float m_run = kNegBig, l_part = 0.f;
-  float o[G][8];
+  f32x4_t oacc[D / 16];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
+  for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const float sl2e = a.scale_log2e;
   const int nb = s.nbuf, kend = d.kend;
-  auto load = [&](MfmaBuf<D, G>& b, int x) {
-    if (x < nb)
-      mfma_load<D, G>(b, a, s, x, ln);
+  int buf = buf0;
+  for (int j = 0; j < nb; ++j) {
+    // the next buffer: of this range, or buffer 0 of the next one
+    if (j + 1 < nb)
+      dec_issue<D, G>(a, s, j + 1, buf ^ 1, ln);
     else
-      mfma_load<D, G>(b, a, sn, x - nb, ln);
-  };
-  for (int j = 0;; j += 2) {
-    load(b1, j + 1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this compute
-    mfma_compute<D, G>(b0, qb, m_run, l_part, o, s.kbeg + 16 * j, kend, rrow, slot, sl2e, bias,
-                       kreg);
-    if (j + 1 >= nb) break;
-    load(b0, j + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_compute<D, G>(b1, qb, m_run, l_part, o, s.kbeg + 16 * (j + 1), kend, rrow, slot, sl2e,
-                       bias, kreg);
-    if (j + 2 >= nb) break;
+      dec_issue<D, G>(a, sn, 0, buf ^ 1, ln);
+    dec_wait<SH::NDMA>();  // buffer j has landed (only the next one's loads remain)
+    mfma_compute<D, G>(ln, buf, qb, m_run, l_part, oacc, s.kbeg + 16 * j, kend, rrow, sl2e,
+                       bias);
+    buf ^= 1;
   }
 
-  // Sums over the lanes of a head (l) and over the V slots (o): one max for
-  // the whole wave, so no rescaling.
+  // The head's weight sum over its four lanes (one max for the whole wave, so
+  // no rescaling); lane (rrow, col) holds the final dims 16 db + 4 rrow .. + 3
+  // of head col.
   float l = lane_sum_xor<16>(l_part);
   l = lane_sum_xor<32>(l);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = o[h][i];
-      if constexpr (LPK <= 8) x = lane_sum_xor<8>(x);
-      x = lane_sum_xor<16>(x);
-      o[h][i] = lane_sum_xor<32>(x);
-    }
-
-  // Slot s writes the heads h with h % NSLOT == s; the head's l and m come
-  // from lane col = h of the row.
-  const size_t row_bytes = (size_t)SH::ROWB;
-  const uint32_t lu = __float_as_uint(l), mu = __float_as_uint(m_run);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    uint32_t lh, mh;
-    switch (h) {
-      case 0: lh = row_bcast<0>(lu); mh = row_bcast<0>(mu); break;
-      case 1: lh = row_bcast<1>(lu); mh = row_bcast<1>(mu); break;
-      case 2: lh = row_bcast<2>(lu); mh = row_bcast<2>(mu); break;
-      case 3: lh = row_bcast<3>(lu); mh = row_bcast<3>(mu); break;
-      case 4: lh = row_bcast<4>(lu); mh = row_bcast<4>(mu); break;
-      case 5: lh = row_bcast<5>(lu); mh = row_bcast<5>(mu); break;
-      case 6: lh = row_bcast<6>(lu); mh = row_bcast<6>(mu); break;
-      default: lh = row_bcast<7>(lu); mh = row_bcast<7>(mu); break;
-    }
-    if (h % NSLOT != slot) continue;
-    const int hq = d.kvh * G + h;
+  if (col < G) {
+    const size_t row_bytes = (size_t)SH::ROWB;
+    const int hq = d.kvh * G + col;
     if (d.nparts == 1) {
-      const float inv = 1.f / __uint_as_float(lh);
-      uint32_t wv[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) wv[w] = pack_bf16x2(o[h][2 * w] * inv, o[h][2 * w + 1] * inv);
+      const float inv = 1.f / l;
       char* orow = (char*)a.out + ((size_t)d.token * a.Hq + hq) * row_bytes;
-      *reinterpret_cast<uint4*>(orow + 16 * sub) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<uint2*>(orow + 2 * (16 * db + 4 * rrow)) =
+            make_uint2(pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv),
+                       pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv));
     } else {
       const size_t pi = ((size_t)d.pslot + d.part) * a.Hq + hq;
-      float* po = a.ws + pi * D + 8 * sub;
-      *reinterpret_cast<float4*>(po) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-      *reinterpret_cast<float4*>(po + 4) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-      if (sub == 0) {
+      float* po = a.ws + pi * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<float4*>(po + 16 * db + 4 * rrow) =
+            make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+      if (rrow == 0) {
         float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
-        *reinterpret_cast<float2*>(ml + 2 * pi) =
-            make_float2(__uint_as_float(mh), __uint_as_float(lh));
+        *reinterpret_cast<float2*>(ml + 2 * pi) = make_float2(m_run, l);
       }
     }
   }
+  return buf;
 }
 
-// A single range (one wave, one work item).
+// A single range (one wave, one work item). region: the wave's
+// dec_region_units<D>() units of LDS.
 template <int D, int G>
 __device__ __forceinline__ void decode_range_alone(const AttnArgs& a, const DecSeg& d,
-                                                   uint4* kreg) {
-  const DecLane ln = dec_lane<D, G>(a);
+                                                   uint4* region) {
+  const DecLane<D, G> ln = dec_lane<D, G>(a, region);
   const DecPre<D, G> p = decode_prefetch<D, G>(a, d);
   const DecSrc s = dec_src<D, G>(a, d, p.page_raw);
-  MfmaBuf<D, G> b0, b1;
-  mfma_load<D, G>(b0, a, s, 0, ln);
-  decode_range<D, G>(a, b0, b1, d, p, s, s, ln, kreg);
+  dec_issue<D, G>(a, s, 0, 0, ln);
+  decode_range<D, G>(a, 0, d, p, s, s, ln);
+  dec_wait<0>();  // the trailing re-read has landed before the region is left
 }
 
 // The decode ranges of wave gw, streamed back to back: each range's page ids
 // and Q are issued while the previous range streams, and its first buffer is
-// loaded during the previous range's last step. lds: kbuf_units<D>() 16-byte
-// units per wave of the workgroup (wave w uses the w-th block).
+// loaded during the previous range's last step. lds: dec_region_units<D>()
+// 16-byte units per wave of the workgroup (wave w uses the w-th region).
 template <int D, int G>
 __device__ __forceinline__ void decode_chunks_mfma(const AttnArgs& a, int wg, uint4* lds) {
-  uint4* kreg = lds + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kbuf_units<D>();
-  const DecLane ln = dec_lane<D, G>(a);
+  uint4* region = lds + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * dec_region_units<D>();
+  const DecLane<D, G> ln = dec_lane<D, G>(a, region);
   DecodeCursor cur(a, wg);
   DecSeg d;
   if (!cur.next(d)) return;
   DecPre<D, G> p = decode_prefetch<D, G>(a, d);
   DecSrc s = dec_src<D, G>(a, d, p.page_raw);
-  MfmaBuf<D, G> b0, b1;
-  mfma_load<D, G>(b0, a, s, 0, ln);
-  bool flip = false;  // the current range's buffer 0 is in b1
+  dec_issue<D, G>(a, s, 0, 0, ln);
+  int buf = 0;  // LDS buffer holding the current range's buffer 0
   for (;;) {
     DecSeg dn;
     const bool more = cur.next(dn);
     if (!more) dn = d;
     const DecPre<D, G> pn = decode_prefetch<D, G>(a, dn);
     const DecSrc sn = dec_src<D, G>(a, dn, pn.page_raw);
-    if (!flip)
-      decode_range<D, G>(a, b0, b1, d, p, s, sn, ln, kreg);
-    else
-      decode_range<D, G>(a, b1, b0, d, p, s, sn, ln, kreg);
+    buf = decode_range<D, G>(a, buf, d, p, s, sn, ln);
     if (!more) break;
-    flip ^= (s.nbuf & 1) != 0;
     d = dn;
     p = pn;
     s = sn;
   }
+  dec_wait<0>();  // the trailing re-read has landed before the region is reused
 }
 
 }  // namespace pa

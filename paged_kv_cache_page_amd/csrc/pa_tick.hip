@@ -42,8 +42,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ PfSmem<D> sm;
   __shared__ int s_next;
   static_assert(kPfThreads == 64 * 4, "decode workers are workgroups of four waves");
-  // decode workers stage K in the (not yet used) prefill tile buffers
-  static_assert(sizeof(sm.k) >= 4 * kbuf_units<D>() * sizeof(uint4), "decode K staging fits");
+  // decode workers keep their K/V buffers in the (not yet used) prefill tile
+  // buffers: sm.k and sm.v, which follow each other
+  static_assert(offsetof(PfSmem<D>, v) == sizeof(sm.k) &&
+                    sizeof(sm.k) + sizeof(sm.v) >= 4 * dec_region_bytes<D>(),
+                "decode K/V buffers fit");
   if ((int)blockIdx.x < a.dec_grid)
     decode_chunks_mfma<D, G>(a, blockIdx.x, reinterpret_cast<uint4*>(sm.k));
 
