@@ -347,6 +347,9 @@ __device__ __forceinline__ DecSrc dec_src(const AttnArgs& a, const DecSeg& d, in
   return s;
 }
 
+// (dec_dma16 names M0 in its clobber list, which the compiler reports.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 // One 16-byte-per-lane load from global memory (wave-uniform base + per-lane
 // 32-bit offset) into LDS (lane j's 16 bytes at byte lds + 16 j; lds in M0).
 // Inline assembly, so the compiler's wait insertion does not make later LDS
@@ -362,6 +365,7 @@ __device__ __forceinline__ void dec_dma16(const char* base, uint32_t voff, uint3
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Wait until at most N of this wave's vector memory operations are
 // outstanding (gfx9 s_waitcnt: vmcnt[3:0] and [15:14]; lgkm and export
