@@ -262,3 +262,26 @@ def test_tick_forward_equals_the_three_calls_bitwise(which):
         assert np.array_equal(_bits(x), _bits(y)), f"{which}: {name} differs"
     if which.startswith("many"):  # these sizes are not among the parity cases above
         check_attention(out, oracle_tick(t), t.dtype, which)
+
+
+@pytest.mark.parametrize("D,G,split,chunks", [(128, 4, 0, False), (128, 4, 16, False),
+                                              (64, 8, 48, False), (128, 1, 0, True),
+                                              (64, 2, 32, True)])
+def test_decode_walk_many_short_rows(D, G, split, chunks):
+    """Decode rows of 1..70 keys on 16-token pages: every decode wave's chunk
+    holds many ranges of one to five 16-key buffers (odd and even counts, so
+    the buffer that holds the next range's first keys alternates, and ragged
+    ends), with automatic and fixed partitions; with `chunks`, two prefill
+    chunks share the tick (the fused kernel's decode workers)."""
+    rng = np.random.default_rng(130 + D + G + split)
+    S = 300
+    sl = [int(x) for x in rng.integers(1, 71, size=S)]
+    ql = [1] * S
+    if chunks:
+        sl += [90, 200]
+        ql += [40, 64]
+    t = W.build_tick(rng, name="short-rows", dtype=W.BF16, Hq=2 * G, Hkv=2, D=D, P=16,
+                     seq_lens=sl, query_lens=ql, theta=1e4, poison=True)
+    say("short rows", D, G, split, chunks)
+    _, out = run_gpu_tick(t, kv_split_tokens=split)
+    check_attention(out, oracle_tick(t), t.dtype, f"short-rows D{D} G{G} split{split}")
