@@ -6,11 +6,13 @@
 // written for that bound: 16-byte row loads through the page table, the next
 // buffer's loads in flight while the current one computes, and the softmax
 // kept online in registers. The float32 path below takes its dot products on
-// VALU; the bf16 path (pa_decode_mfma.h) puts the scores on matrix cores.
+// VALU; the bf16 path (pa_decode_mfma.h) loads K and V straight into the
+// wave's LDS buffers and puts the scores and P.V on matrix cores.
 //
 // Work decomposition. A work item is a key range of one row for one KV head
-// and is owned by ONE wave: no LDS, no workgroup barrier, so a wave never
-// waits for its neighbours. The range's page ids sit in one VGPR (lane i holds
+// and is owned by ONE wave: nothing is shared between waves (the bf16 path's
+// LDS buffers are the wave's own) and there is no workgroup barrier, so a wave
+// never waits for its neighbours. The range's page ids sit in one VGPR (lane i holds
 // the i-th page of the range, at most 64 pages) and each buffer takes its page
 // with a lane read into a scalar register.
 //
@@ -22,7 +24,7 @@
 // a matrix-core kernel, i.e. float32) maps waves to (token, fixed partition,
 // KV head) directly.
 //
-// Inside a wave, LPK lanes hold one key row (16 or 32 bytes each), so a wave
+// float32: inside a wave, LPK lanes hold one key row (16 or 32 bytes each), so a wave
 // covers 64 / LPK keys per step (its "slots") and UNROLL steps per buffer.
 // Each lane keeps its own running (max, sum, output) over the keys of its
 // slot; at the end the slots are merged with a register butterfly
