@@ -254,7 +254,8 @@ def pa_tick_forward(q, k, v, positions, block_tables, seq_lens, query_start_loc,
 
     Same as ``pa_compute_slot_mapping`` + ``pa_rope_and_cache_write`` +
     ``pa_paged_attention_varlen`` with these arguments (q and k are rotated in
-    place); the attention's planning kernel overlaps the first two. Returns
+    place), bit for bit, enqueued as one launch for the slot mapping, the page
+    write and the attention's plan, then the attention kernels. Returns
     ``out``; ``slot_mapping`` ``[T]`` int32 is written (allocated if None).
     """
     torch = _torch()
