@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: one packed continuous-batching tick of paged attention on one MI355X.
 
-A step is one whole tick of the hot path over one batch of synthetic input:
-slot mapping -> RoPE on the new Q/K + K/V page write -> paged attention
-(decode rows with split-KV and its merge, prefill chunks on MFMA).
+A step is one whole tick of the hot path over one batch of synthetic input, one
+pa_tick_forward call: slot mapping -> RoPE on the new Q/K + K/V page write ->
+paged attention (decode rows with split-KV and its merge, prefill chunks on
+MFMA). --separate enqueues the same step as the three separate calls.
 
 Default workload: the Qwen3-4B-shaped packed mixed tick (48 decode rows with
 contexts U[256, 4096] plus prefill chunks of 512/512/1024 tokens after 0-3
