@@ -56,11 +56,14 @@ struct AttnArgs {
 //     piece j | pieces J << 16, first partial slot), in decreasing cost order;
 //     an item (sequence, row tile) of J > 1 pieces owns the partial slots
 //     [slot, slot + J * Hkv): KV head h, piece j at slot + h * J + j
+//   the entries' sequence shapes: cap_pf x (first query row q0, query length
+//     L, keys n clamped as the kernels clamp them, 0), read beside the entry
+//     so that a prefill item does not wait for a second load to learn them
 //   cut prefill items: cap_pf x (sequence, row tile, J, slot), merged by the
 //     prefill merge kernel after the tick
 constexpr int kPlanLine = 32;  // ints per 128-byte cache line
 struct PlanOffsets {
-  size_t rows, nparts, pbase, first_row, pf, merge, total;
+  size_t rows, nparts, pbase, first_row, pf, pf_shape, merge, total;
 };
 __host__ __device__ inline PlanOffsets plan_offsets(long S, long Hq, long cap_dec, long cap_pf) {
   PlanOffsets o;
@@ -69,7 +72,8 @@ __host__ __device__ inline PlanOffsets plan_offsets(long S, long Hq, long cap_de
   o.pbase = o.nparts + (size_t)S;
   o.first_row = o.pbase + (size_t)S;
   o.pf = (o.first_row + (size_t)cap_dec + 3) / 4 * 4;
-  o.merge = o.pf + 4 * (size_t)cap_pf;
+  o.pf_shape = o.pf + 4 * (size_t)cap_pf;
+  o.merge = o.pf_shape + 4 * (size_t)cap_pf;
   o.total = o.merge + 4 * (size_t)cap_pf;
   return o;
 }

@@ -168,6 +168,7 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   int* pbase_of = plan + po.pbase;
   int* first_row = plan + po.first_row;
   int4* pf_items = reinterpret_cast<int4*>(plan + po.pf);
+  int4* pf_shapes = reinterpret_cast<int4*>(plan + po.pf_shape);
   int4* merge_items = reinterpret_cast<int4*>(plan + po.merge);
   // fixed partitions: rows padded to whole partitions; otherwise to 16 keys
   const int A = a.part_tokens > 0 ? a.part_tokens : 16;
@@ -338,7 +339,10 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
       }
       for (int j = 0; j < J; ++j) {
         const int idx = atomicAdd(&s_cur[(j + 1) * t / J - j * t / J], 1);
-        if (idx < cap_pf) pf_items[idx] = make_int4(s, mt, j | (J << 16), slot);
+        if (idx < cap_pf) {
+          pf_items[idx] = make_int4(s, mt, j | (J << 16), slot);
+          pf_shapes[idx] = make_int4(sh.q0, sh.L, sh.n, 0);
+        }
       }
     }
   });

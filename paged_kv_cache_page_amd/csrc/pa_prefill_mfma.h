@@ -400,7 +400,8 @@ __device__ __forceinline__ void tile_compute(const uint16_t* sk, const uint16_t*
 // a piece writes its partial (m, l, o) to slot slot0 + kvh * J + j, and the
 // merge kernel combines the pieces after the tick.
 template <int D, int G>
-__device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, int4 e, int kvh) {
+__device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, int4 e, int4 shape,
+                                             int kvh) {
   // wave-uniform by construction (see the callers); explicit for the compiler
   const int s = __builtin_amdgcn_readfirstlane(e.x), mt = __builtin_amdgcn_readfirstlane(e.y);
   const int ez = __builtin_amdgcn_readfirstlane(e.z), slot0 = __builtin_amdgcn_readfirstlane(e.w);
@@ -420,11 +421,12 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
   const float sl2e = a.scale_log2e;
   const size_t slot_stride = (size_t)a.Hkv * row_bytes;
   const int p_shift = a.p_shift;
-  const int q0 = a.qsl[s];
-  const int L = a.qsl[s + 1] - q0;
+  // the sequence's shape as the plan read it (query_start_loc, seq_lens
+  // clamped to the page table and max_seq_len)
+  const int q0 = __builtin_amdgcn_readfirstlane(shape.x);
+  const int L = __builtin_amdgcn_readfirstlane(shape.y);
+  const int n = __builtin_amdgcn_readfirstlane(shape.z);
   const int i0 = mt * TM;
-  int n = a.seq_lens[s];
-  n = min(min(n, a.max_blocks * a.P), a.max_seq_len);
   if (L <= 1 || i0 >= L || q0 < 0 || q0 + L > a.T || n < L) return;  // uniform per item
   const int i1 = min(L, i0 + TM);
   const int kmax = n - L + i1;          // keys visible to the tile's last row

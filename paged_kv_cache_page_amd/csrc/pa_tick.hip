@@ -50,7 +50,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   if ((int)blockIdx.x < a.dec_grid)
     decode_chunks_mfma<D, G>(a, blockIdx.x, reinterpret_cast<uint4*>(sm.k));
 
-  const int4* items = reinterpret_cast<const int4*>(a.plan + plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf).pf);
+  const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
+  const int4* items = reinterpret_cast<const int4*>(a.plan + po.pf);
+  const int4* shapes = reinterpret_cast<const int4*>(a.plan + po.pf_shape);
   const int n_items = a.plan[1];
   const int home = blockIdx.x % a.Hkv;
   for (int hh = 0; hh < a.Hkv; ++hh) {
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       // loads or MFMAs wait, while the decode waves' deep load queues absorb
       // the delay (measured: the fused tick ~13% shorter, decode unchanged).
       __builtin_amdgcn_s_setprio(2);
-      prefill_item<D, G>(a, sm, items[it], kvh);
+      prefill_item<D, G>(a, sm, items[it], shapes[it], kvh);
       __builtin_amdgcn_s_setprio(0);
       it = __builtin_amdgcn_readfirstlane(pf_take(cursor, &s_next));
     }

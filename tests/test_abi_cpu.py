@@ -107,10 +107,10 @@ def test_attention_empty_tick_is_ok_without_touching_memory():
 def _plan_bytes(S, cap_dec, cap_pf, Hq):
     # header 32, one 32-int line per prefill queue cursor (Hq) and one for the counter
     # of claimed decode chunks, decode rows 4 * S, partitions and first partial slot per row 2 * S,
-    # chunk starts cap_dec, then (16-byte aligned) prefill entries 4 * cap_pf and cut
-    # items 4 * cap_pf (ints), padded to 256 bytes
+    # chunk starts cap_dec, then (16-byte aligned) prefill entries 4 * cap_pf, their
+    # sequence shapes 4 * cap_pf and cut items 4 * cap_pf (ints), padded to 256 bytes
     pf = -(-(32 * (2 + Hq) + 6 * S + cap_dec) // 4) * 4
-    return -(-(pf + 8 * cap_pf) * 4 // 256) * 256
+    return -(-(pf + 12 * cap_pf) * 4 // 256) * 256
 
 
 def test_workspace_size_query():
