@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   }
 }
 
-// K3: one thread per (row, query head, 4 consecutive dims); the body is
+// K3: kMergeLanes threads per (row, query head, 4 consecutive dims); the body is
 // split_reduce_task (pa_decode_mfma.h), shared with the fused tick's reduce.
 template <typename ET, bool TOKEN_MODE>
 __global__ __launch_bounds__(256) void split_reduce_kernel(AttnArgs a) {
@@ -504,7 +504,7 @@ hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipS
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s) {
   const long rows = token_mode ? a.T : a.S;
-  const long threads = rows * a.Hq * (a.D / 4);
+  const long threads = rows * a.Hq * (a.D / 4) * kMergeLanes;
   if (threads == 0 || a.max_parts <= 1) return hipSuccess;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   profile_before(token_mode ? "split_reduce_tokens" : "split_reduce", s);

@@ -58,14 +58,21 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
   return r;
 }
 
-// K3 task idx = (row, query head, 4 consecutive dims): merge the row's
-// split-KV partitions, m* = max_k m_k,
-// o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k (m* taken as a running
-// maximum, the sums rescaled when it grows).
+// K3: merge of a row's split-KV partitions, m* = max_k m_k,
+// o = sum_k 2^(m_k - m*) o_k / sum_k 2^(m_k - m*) l_k. Thread idx =
+// kMergeLanes (row, query head, 4 consecutive dims) + lane: the kMergeLanes
+// adjacent lanes of a group take every kMergeLanes-th partition (m* taken as
+// a running maximum, the sums rescaled when it grows), then combine their
+// three values the same way with lane exchanges (xor 1, then xor 2), so that
+// a row of many partitions waits for a quarter of the dependent loads.
+constexpr int kMergeLanes = 4;
+
 template <typename ET, bool TOKEN_MODE>
 __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
   const int D = a.D;
   const int quads = D / 4;
+  const int lane_k = (int)(idx % kMergeLanes);
+  idx /= kMergeLanes;
   const int d4 = (int)(idx % quads);
   const long rh = idx / quads;
   const int h = (int)(rh % a.Hq);
@@ -94,11 +101,12 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
   if (nparts <= 1) return;
   const float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
   const size_t p0 = slot0 * a.Hq + h;  // partial index of part 0
-  // one pass with a running max: all partitions' loads are independent
+  // one pass with a running max over this lane's partitions: their loads are
+  // independent
   float mn = kNegBig, lt = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int k = 0; k < nparts; ++k) {
+#pragma unroll 2
+  for (int k = lane_k; k < nparts; k += kMergeLanes) {
     const size_t pi = p0 + (size_t)k * a.Hq;
     const float2 mlk = *reinterpret_cast<const float2*>(ml + 2 * pi);
     const float4 ok = *reinterpret_cast<const float4*>(a.ws + pi * D + 4 * d4);
@@ -118,6 +126,21 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
     acc.z = fmaf(ok.z, c, acc.z);
     acc.w = fmaf(ok.w, c, acc.w);
   }
+  // the group's lanes combined (a lane with no partition holds m = kNegBig,
+  // l = 0, o = 0, which the combination weighs with 0 or leaves at 0)
+#pragma unroll
+  for (int x = 1; x < kMergeLanes; x <<= 1) {
+    const float mo = __shfl_xor(mn, x), lo = __shfl_xor(lt, x);
+    const float4 ao = make_float4(__shfl_xor(acc.x, x), __shfl_xor(acc.y, x),
+                                  __shfl_xor(acc.z, x), __shfl_xor(acc.w, x));
+    const float m2 = fmaxf(mn, mo);
+    const float ca = fast_exp2(mn - m2), cb = fast_exp2(mo - m2);
+    lt = lt * ca + lo * cb;
+    acc = make_float4(acc.x * ca + ao.x * cb, acc.y * ca + ao.y * cb, acc.z * ca + ao.z * cb,
+                      acc.w * ca + ao.w * cb);
+    mn = m2;
+  }
+  if (lane_k != 0) return;
   const float inv = 1.f / lt;
   const size_t oi = ((size_t)token * a.Hq + h) * D + 4 * d4;
   if constexpr (ET::kBytes == 2) {

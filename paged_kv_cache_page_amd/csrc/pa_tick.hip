@@ -133,7 +133,8 @@ __device__ __forceinline__ void prefill_merge_row(const AttnArgs& a, int slot0, 
 }
 
 // After the tick: the first dec_blocks workgroups merge the split-KV
-// partitions of the decode rows (one thread per row, head and 4 dims); each
+// partitions of the decode rows (kMergeLanes threads per row, head and 4
+// dims); each
 // of the others merges the pieces of a group of rows of one (cut prefill
 // item, KV head), one thread per row and 4 dims.
 constexpr int kReduceThreads = 256;
@@ -185,7 +186,7 @@ int tick_grid(pa_dtype_t dt, int D, int G) {
 }
 
 hipError_t launch_tick_reduce(const AttnArgs& a, hipStream_t s) {
-  const long dec_threads = a.max_parts > 1 ? (long)a.S * a.Hq * (a.D / 4) : 0;
+  const long dec_threads = a.max_parts > 1 ? (long)a.S * a.Hq * (a.D / 4) * kMergeLanes : 0;
   const int dec_blocks = (int)((dec_threads + kReduceThreads - 1) / kReduceThreads);
   // cut items use at least 2 Hkv partial slots each: at most pf_slots / 2
   // (item, KV head) pairs, kPrefillRows * (D / 4) threads per pair
