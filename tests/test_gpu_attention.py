@@ -230,7 +230,7 @@ def _many_seqs_tick(seed, S):
 
 
 @pytest.mark.parametrize("which", ["cfg4", "cfg3", "cfg5", "small0", "small_f32", "split512",
-                                   "many100", "many1100", "many4500"])
+                                   "many100", "many1100", "many4500", "norope"])
 def test_tick_forward_equals_the_three_calls_bitwise(which):
     """pa_tick_forward (slot mapping, page write and plan in one launch) ==
     the three calls in order; the many-sequence ticks take the token search
@@ -242,6 +242,8 @@ def test_tick_forward_equals_the_three_calls_bitwise(which):
         t = _small(120, *SMALL_CASES[10])
     elif which.startswith("many"):
         t = _many_seqs_tick(122, int(which[4:]))
+    elif which == "norope":  # no cos/sin table: K and V stored as given
+        t = _small(123, *SMALL_CASES[1], theta=None)
     else:
         t = _small(121, *SMALL_CASES[0])
     assert not t.new_in_pool
