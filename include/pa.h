@@ -50,7 +50,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = 1,         /* a host scalar or pointer is invalid */
   PA_ERR_UNSUPPORTED = 2,         /* dtype / head_dim / group / page size has no kernel */
   PA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the size query's answer */
-  PA_ERR_HIP = 4                  /* a HIP call failed */
+  PA_ERR_HIP = 4,                 /* a HIP call failed */
+  PA_ERR_NO_PAGES = 5             /* the block manager has too few free pages (pa_blocks.h) */
 } pa_status_t;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype_t;

@@ -34,6 +34,11 @@ Precision
   that quantisation decision in the same float32 arithmetic.
 * Attention runs in float64 on the stored (already rounded) values.
 
+``blocks.py`` is the reference paged block manager (free list, page tables
+with reservations, refcounts, the prefix cache of chained complete blocks,
+leaf-first eviction); its pins and the library's step-by-step comparison are
+in ``tests/test_block_manager.py``.
+
 Every function has at least one pin in ``tests/test_oracle_*.py`` that does
 not re-type its formula: brute-force loops, closed forms, invariants, a worked
 number from the pages, or a library routine (torch CPU SDPA in float64).

@@ -20,10 +20,12 @@ __all__ = [
     "pa_abi_version", "pa_status_string", "pa_rope_cos_sin_table", "pa_compute_slot_mapping",
     "pa_rope_and_cache_write", "pa_paged_attention_workspace_size", "pa_paged_attention_varlen",
     "pa_tick_forward", "pa_profile_start", "pa_profile_stop", "pa_profile_reset",
+    "BlockManager", "PA_ERR_NO_PAGES",
 ]
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_ERR_NO_PAGES = 5
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libpa.so")
 _lib = None
@@ -46,6 +48,15 @@ SIGNATURES = {
     "pa_tick_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_admit": (_i32, [_vp, ctypes.c_int64, _vp, _i32, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_append": (_i32, [_vp, ctypes.c_int64, _i32]),
+    "pa_bm_finish": (_i32, [_vp, ctypes.c_int64, _i32]),
+    "pa_bm_evict": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_block_table": (_i32, [_vp, ctypes.c_int64, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_stats": (_i32, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pa_bm_refcount": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
     "pa_profile_start": (_i32, [_i32]),
     "pa_profile_stop": (_i32, [ctypes.POINTER(_i32)]),
     "pa_profile_get": (_i32, [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(_f32)]),
@@ -332,3 +343,68 @@ def pa_profile_stop():
 
 def pa_profile_reset():
     _check(lib().pa_profile_reset(), "pa_profile_reset")
+
+
+# ---------------------------------------------------------------- block manager
+class BlockManager:
+    """Host-side paged block manager (``include/pa_blocks.h``): the pool's
+    pages, each request's page table and reservation, and the prefix cache of
+    complete blocks. The block tables it returns feed the attention calls."""
+
+    def __init__(self, num_pages, page_size):
+        h = _vp()
+        _check(lib().pa_bm_create(int(num_pages), int(page_size), ctypes.byref(h)), "pa_bm_create")
+        self._h = h
+        self.num_pages, self.page_size = int(num_pages), int(page_size)
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, req, prompt, max_new_tokens):
+        """Admit request ``req``; returns the prompt tokens already cached."""
+        import numpy as np
+        arr = np.ascontiguousarray(prompt, dtype=np.int32)
+        out = _i32(0)
+        _check(lib().pa_bm_admit(self._h, int(req), arr.ctypes.data_as(_vp), int(arr.size),
+                                 int(max_new_tokens), ctypes.byref(out)), "pa_bm_admit")
+        return out.value
+
+    def append(self, req, n_tokens):
+        _check(lib().pa_bm_append(self._h, int(req), int(n_tokens)), "pa_bm_append")
+
+    def finish(self, req, publish=True):
+        _check(lib().pa_bm_finish(self._h, int(req), 1 if publish else 0), "pa_bm_finish")
+
+    def evict(self, pages):
+        out = _i32(0)
+        _check(lib().pa_bm_evict(self._h, int(pages), ctypes.byref(out)), "pa_bm_evict")
+        return out.value
+
+    def block_table(self, req):
+        """int32 numpy array: the request's pages in order."""
+        import numpy as np
+        out = np.zeros(self.num_pages, dtype=np.int32)
+        n = _i32(0)
+        _check(lib().pa_bm_block_table(self._h, int(req), out.ctypes.data_as(_vp), out.size,
+                                       ctypes.byref(n)), "pa_bm_block_table")
+        return out[:n.value].copy()
+
+    def stats(self):
+        """(free pages, reserved pages, cached blocks)."""
+        f, r, c = _i32(0), _i32(0), _i32(0)
+        _check(lib().pa_bm_stats(self._h, ctypes.byref(f), ctypes.byref(r), ctypes.byref(c)),
+               "pa_bm_stats")
+        return f.value, r.value, c.value
+
+    def refcount(self, page):
+        out = _i32(0)
+        _check(lib().pa_bm_refcount(self._h, int(page), ctypes.byref(out)), "pa_bm_refcount")
+        return out.value

@@ -38,9 +38,16 @@ def hipcc():
     return path
 
 
+# Host-only C++ sources (the block manager) are compiled by the host compiler.
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall"]
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [shutil.which("g++") or "g++", *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -51,9 +58,10 @@ def _compile(src):
 
 
 def build(verbose=False):
-    """Compile every HIP source and link libpa.so. Always rebuilds."""
+    """Compile every HIP (and host C++) source and link libpa.so. Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                     if f.endswith(".hip") or f.endswith(".cpp"))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         results = list(ex.map(_compile, sources))
     for obj, warn in results:

@@ -213,7 +213,7 @@ using namespace pa;
 #pragma GCC visibility push(default)
 extern "C" {
 
-int32_t pa_abi_version(void) { return 2; }
+int32_t pa_abi_version(void) { return 3; }
 
 const char* pa_status_string(pa_status_t status) {
   switch (status) {
@@ -222,6 +222,7 @@ const char* pa_status_string(pa_status_t status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: no kernel for this dtype/shape";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL: workspace below the size query";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP call failed";
+    case PA_ERR_NO_PAGES: return "PA_ERR_NO_PAGES: too few free pages for the reservation";
   }
   return "PA_ERR_UNKNOWN";
 }
