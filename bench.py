@@ -151,6 +151,68 @@ def committed_traffic(kernel, workload):
     return None
 
 
+def bench_block_manager(steps):
+    """Host block manager over a synthetic continuous-batching trace at the Qwen
+    serving shape: 256-token pages, a 4096-page pool, 64 requests live, prompts
+    that share one of four 2048-token prefixes plus U[64, 1024] own tokens,
+    U[64, 512] new tokens each. One tick = admit as many waiting requests as fit
+    (restoring cached prefixes), record one prefill (the uncached prompt) or one
+    decode token per live request, finish the requests that are done (publishing
+    their prompt blocks). Prints one JSON line: ticks/s and manager calls/s."""
+    import paged_kv_cache_page_amd as pa
+    P, N, LIVE = 256, 4096, 64
+    rng = np.random.default_rng(0)
+    prefixes = [rng.integers(0, 150000, 2048).astype(np.int32) for _ in range(4)]
+    bm = pa.BlockManager(N, P)
+    live, next_id, calls = {}, 0, 0
+
+    def tick():
+        nonlocal next_id, calls
+        while len(live) < LIVE:
+            prompt = np.concatenate([prefixes[next_id % 4],
+                                     rng.integers(0, 150000, int(rng.integers(64, 1025)))
+                                     .astype(np.int32)])
+            new = int(rng.integers(64, 513))
+            calls += 1
+            try:
+                cached = bm.admit(next_id, prompt, new)
+            except pa.PaError:
+                calls += 1
+                bm.evict(16)
+                break
+            live[next_id] = [len(prompt) - cached, new]
+            next_id += 1
+        for req in list(live):
+            rest = live[req]
+            calls += 1
+            if rest[0]:
+                bm.append(req, rest[0])
+                rest[0] = 0
+            else:
+                bm.append(req, 1)
+                rest[1] -= 1
+                if rest[1] == 0:
+                    calls += 1
+                    bm.finish(req)
+                    del live[req]
+
+    for _ in range(20):
+        tick()
+    calls = 0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        tick()
+    dt = time.perf_counter() - t0
+    free, reserved, cached = bm.stats()
+    print(json.dumps({"metric": "block_manager_ticks_per_s", "value": round(steps / dt, 1),
+                      "unit": "ticks/s", "calls_per_s": round(calls / dt, 1),
+                      "us_per_call": round(dt / calls * 1e6, 3), "steps": steps,
+                      "config": {"workload": "host block manager, 64 live requests, P=256, "
+                                             "4096 pages, 4 shared 2048-token prefixes",
+                                 "free": free, "reserved": reserved, "cached_blocks": cached},
+                      "note": "includes the ctypes binding's per-call cost"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,7 +227,13 @@ def main():
                          "instead of pa_tick_forward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM traffic counters)")
+    ap.add_argument("--block-manager", action="store_true",
+                    help="only time the host block manager over a synthetic serving trace "
+                         "(no GPU)")
     args = ap.parse_args()
+    if args.block_manager:
+        bench_block_manager(args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
