@@ -151,6 +151,57 @@ def committed_traffic(kernel, workload):
     return None
 
 
+def bench_sample(steps, warmup, with_cpu):
+    """pa_sample_tokens over one logits row per sequence of the packed mixed tick
+    (51 rows) at Qwen3's vocabulary (151936), float32 logits N(0, 4^2), with the
+    request defaults temperature 0.2 and top-p 0.95 (top-k off), a fresh uniform
+    per row. Algorithmic bytes per launch: each logit read once plus the
+    settings and the tokens. Prints one JSON line."""
+    import torch
+    import paged_kv_cache_page_amd as pa
+    R, V = 51, 151936
+    rng = np.random.default_rng(5)
+    logits_h = (rng.standard_normal((R, V)) * 4).astype(np.float32)
+    dev = "cuda:0"
+    logits = torch.from_numpy(logits_h).to(dev)
+    T = torch.full((R,), 0.2, dtype=torch.float32, device=dev)
+    k = torch.zeros(R, dtype=torch.int32, device=dev)
+    p = torch.full((R,), 0.95, dtype=torch.float32, device=dev)
+    u = torch.from_numpy(rng.random(R, dtype=np.float32)).to(dev)
+    out = torch.empty(R, dtype=torch.int32, device=dev)
+    for _ in range(warmup):
+        pa.pa_sample_tokens(logits, T, k, p, u, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        pa.pa_sample_tokens(logits, T, k, p, u, out=out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    nbytes = R * V * 4 + R * 5 * 4
+    rec = {"metric": "sampled rows/s", "value": round(R / (ms * 1e-3), 1), "unit": "rows/s",
+           "ms_per_launch": round(ms, 5), "steps": steps, "warmup": warmup,
+           "config": {"workload": "sampling, 51 rows x 151936 vocab, float32 logits, "
+                                  "temperature 0.2, top-p 0.95", "rows": R, "vocab": V},
+           "roofline": {"bound": "hbm", "kernel": "sample_kernel",
+                        "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": 8000.0,
+                        "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 8e12, 4),
+                        "bytes_per_launch": nbytes, "traffic": None}}
+    if with_cpu:
+        from oracle import sampling as osm
+        n = 8
+        t0 = time.perf_counter()
+        osm.sample_rows(logits_h[:n], np.full(n, 0.2, np.float32), np.zeros(n, np.int32),
+                        np.full(n, 0.95, np.float32), u[:n].cpu().numpy())
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(n / dt, 2), "unit": "rows/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n} of the rows"}
+    got = out.cpu().numpy()
+    rec["tokens_in_range"] = bool(((got >= 0) & (got < V)).all())
+    print(json.dumps(rec))
+
+
 def bench_block_manager(steps):
     """Host block manager over a synthetic continuous-batching trace at the Qwen
     serving shape: 256-token pages, a 4096-page pool, 64 requests live, prompts
@@ -230,7 +281,12 @@ def main():
     ap.add_argument("--block-manager", action="store_true",
                     help="only time the host block manager over a synthetic serving trace "
                          "(no GPU)")
+    ap.add_argument("--sample", action="store_true",
+                    help="only time pa_sample_tokens over one tick's logits rows")
     args = ap.parse_args()
+    if args.sample:
+        bench_sample(args.steps, args.warmup, not args.no_cpu)
+        return
     if args.block_manager:
         bench_block_manager(args.steps)
         return

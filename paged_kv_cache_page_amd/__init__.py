@@ -20,7 +20,7 @@ __all__ = [
     "pa_abi_version", "pa_status_string", "pa_rope_cos_sin_table", "pa_compute_slot_mapping",
     "pa_rope_and_cache_write", "pa_paged_attention_workspace_size", "pa_paged_attention_varlen",
     "pa_tick_forward", "pa_profile_start", "pa_profile_stop", "pa_profile_reset",
-    "BlockManager", "PA_ERR_NO_PAGES",
+    "BlockManager", "PA_ERR_NO_PAGES", "pa_sample_tokens",
 ]
 
 PA_F32 = 0
@@ -57,6 +57,7 @@ SIGNATURES = {
     "pa_bm_block_table": (_i32, [_vp, ctypes.c_int64, _vp, _i32, ctypes.POINTER(_i32)]),
     "pa_bm_stats": (_i32, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "pa_bm_refcount": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_sample_tokens": (_i32, [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pa_profile_start": (_i32, [_i32]),
     "pa_profile_stop": (_i32, [ctypes.POINTER(_i32)]),
     "pa_profile_get": (_i32, [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(_f32)]),
@@ -346,6 +347,31 @@ def pa_profile_reset():
 
 
 # ---------------------------------------------------------------- block manager
+def pa_sample_tokens(logits, temperature, top_k, top_p, uniforms, out=None, stream=None):
+    """Sample one token per row of ``logits`` [rows, vocab] float32 (row stride
+    ``logits.stride(0)``), each row with its own ``temperature``, ``top_k``,
+    ``top_p`` and caller-drawn ``uniforms`` in [0, 1) (float32, int32, float32,
+    float32 [rows]). Greedy when temperature <= 0 or top_k == 1. Returns
+    ``out`` int32 [rows] (allocated if None)."""
+    torch = _torch()
+    _dev(logits, "logits", torch.float32, 2)
+    R, V = logits.shape
+    for t, name, dt in ((temperature, "temperature", torch.float32), (top_k, "top_k", torch.int32),
+                        (top_p, "top_p", torch.float32), (uniforms, "uniforms", torch.float32)):
+        _dev(t, name, dt, 1)
+        if t.shape[0] != R or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [{R}]")
+    if out is None:
+        out = torch.empty(R, dtype=torch.int32, device=logits.device)
+    _dev(out, "out", torch.int32, 1)
+    if out.shape[0] != R:
+        raise ValueError("out must be [rows]")
+    _check(lib().pa_sample_tokens(_ptr(logits), logits.stride(0), R, V, _ptr(temperature),
+                                  _ptr(top_k), _ptr(top_p), _ptr(uniforms), _ptr(out),
+                                  _stream(stream)), "pa_sample_tokens")
+    return out
+
+
 class BlockManager:
     """Host-side paged block manager (``include/pa_blocks.h``): the pool's
     pages, each request's page table and reservation, and the prefix cache of

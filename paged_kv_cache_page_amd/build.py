@@ -21,7 +21,8 @@ ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 # separately, so contraction into fused multiply-adds is off there; it also
 # compiles the plan (pa_plan.h), which the plan kernel's unit then compiles
 # with the same flag.
-EXTRA = {"pa_rope_cache.hip": ["-ffp-contract=off"], "pa_plan.hip": ["-ffp-contract=off"]}
+EXTRA = {"pa_rope_cache.hip": ["-ffp-contract=off"], "pa_plan.hip": ["-ffp-contract=off"],
+         "pa_sample.hip": ["-ffp-contract=off"]}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",

@@ -213,7 +213,7 @@ using namespace pa;
 #pragma GCC visibility push(default)
 extern "C" {
 
-int32_t pa_abi_version(void) { return 3; }
+int32_t pa_abi_version(void) { return 4; }
 
 const char* pa_status_string(pa_status_t status) {
   switch (status) {

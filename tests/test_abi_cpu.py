@@ -11,7 +11,7 @@ import pytest
 import paged_kv_cache_page_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_sample.h")]
 
 OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
 F32, BF16 = pa.PA_F32, pa.PA_BF16
@@ -46,7 +46,7 @@ def test_library_exports_nothing_else():
 
 
 def test_status_strings_and_version():
-    assert pa.pa_abi_version() == 3
+    assert pa.pa_abi_version() == 4
     for code in range(5):
         assert pa.pa_status_string(code).startswith("PA_")
     assert "UNKNOWN" in pa.pa_status_string(99)
@@ -227,3 +227,16 @@ def test_tick_forward_rejects_bad_host_arguments(kw, code):
 
 def test_tick_forward_empty_tick_is_ok_without_touching_memory():
     assert tick(T=0) == OK
+
+
+def test_sample_tokens_rejects_bad_scalars_before_any_launch():
+    lib = pa.lib()
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host checks
+    f = lambda *a: lib.pa_sample_tokens(*a)
+    assert f(p, 10, -1, 10, p, p, p, p, p, None) == INVALID       # rows < 0
+    assert f(p, 10, 1, 0, p, p, p, p, p, None) == INVALID         # vocab < 1
+    assert f(p, 5, 1, 10, p, p, p, p, p, None) == INVALID         # row_stride < vocab
+    assert f(p, 1 << 22, 1, (1 << 21) + 1, p, p, p, p, p, None) == UNSUPPORTED
+    assert f(None, 10, 1, 10, p, p, p, p, p, None) == INVALID     # NULL logits
+    assert f(p, 10, 1, 10, p, p, p, p, None, None) == INVALID     # NULL out
+    assert f(None, 10, 0, 10, None, None, None, None, None, None) == OK   # no rows: nothing to do

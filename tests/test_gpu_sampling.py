@@ -1,0 +1,113 @@
+"""pa_sample_tokens on the GPU against the sampling oracle, token for token.
+
+Every token is an integer decision, so the bar is equality. Both sides take
+the decision on the same integer weights; the one rounding step that can
+differ is the float64 exp of a logit (each side's library exp is within an
+ulp), which changes a token only when a uniform lands within a few parts in
+2**32 of a boundary between tokens, so equality is expected throughout.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sampling as osm
+import paged_kv_cache_page_amd as pa
+from _gpu import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+QWEN_VOCAB = 151936
+
+
+def settings(rng, R, V):
+    T = rng.choice([0.0, 0.2, 0.7, 1.0, 1.5, 2.0], R).astype(np.float32)
+    k = rng.choice([0, 1, 2, 5, 50, 1000, V, V + 7, -1], R).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.9, 0.5, 0.01, 1e-7], R).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    return T, k, p, u
+
+
+def run(logits, T, k, p, u):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    out = pa.pa_sample_tokens(t(logits), t(T), t(k), t(p), t(u))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(logits, T, k, p, u, where):
+    say("sample", where, logits.shape)
+    got = run(logits, T, k, p, u)
+    want = osm.sample_rows(logits, T, k, p, u)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(where, int(r), float(T[r]), int(k[r]), float(p[r]), float(u[r]),
+                            int(got[r]), int(want[r])) for r in bad[:5]]
+    return got
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_qwen_vocab_mixed_settings(seed):
+    rng = np.random.default_rng(100 + seed)
+    R, V = 48, QWEN_VOCAB
+    logits = (rng.standard_normal((R, V)) * 4).astype(np.float32)
+    T, k, p, u = settings(rng, R, V)
+    check(logits, T, k, p, u, f"qwen seed {seed}")
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 1023, 1024, 1025, 3001])
+def test_small_and_ragged_vocab(V):
+    rng = np.random.default_rng(V)
+    R = 24
+    logits = (rng.standard_normal((R, V)) * 2).astype(np.float32)
+    T, k, p, u = settings(rng, R, V)
+    check(logits, T, k, p, u, f"V={V}")
+
+
+def test_ties_signed_zeros_and_minus_inf():
+    rng = np.random.default_rng(7)
+    R, V = 40, 5000
+    logits = (np.round(rng.standard_normal((R, V)) * 2) / 4).astype(np.float32)  # wide tie groups
+    logits[:, ::7] = -np.inf
+    logits[::3, 5] = 0.0
+    logits[::3, 6] = -0.0
+    logits[1, :] = 0.0                                 # a whole row of one value
+    logits[2, :] = -np.inf
+    logits[2, 4321] = 1.0                              # a single finite logit
+    T = np.full(R, 1.0, np.float32)
+    T[::5] = 0.5
+    k = rng.choice([0, 3, 10, 100, 777], R).astype(np.int32)   # cuts through tie groups
+    p = rng.choice([1.0, 0.3, 0.6, 0.99], R).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    u[0], u[3] = 0.0, np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    got = check(logits, T, k, p, u, "ties")
+    assert got[2] == 4321
+
+
+def test_batched_equals_per_row_and_repeats():
+    rng = np.random.default_rng(9)
+    R, V = 16, 32000
+    logits = (rng.standard_normal((R, V)) * 3).astype(np.float32)
+    T, k, p, u = settings(rng, R, V)
+    batched = run(logits, T, k, p, u)
+    for r in range(R):
+        one = run(logits[r:r + 1], T[r:r + 1], k[r:r + 1], p[r:r + 1], u[r:r + 1])
+        assert one[0] == batched[r], r
+    assert np.array_equal(run(logits, T, k, p, u), batched)
+
+
+def test_rows_sharing_settings_sample_their_own_distribution():
+    # 4096 rows of the same logits, one temperature and top-p, uniforms on a grid:
+    # the token counts follow the kept probabilities (inverse transform)
+    rng = np.random.default_rng(11)
+    V, R = 64, 4096
+    row = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    logits = np.tile(row, (R, 1))
+    T = np.full(R, 0.8, np.float32)
+    k = np.zeros(R, np.int32)
+    p = np.full(R, 0.9, np.float32)
+    u = ((np.arange(R) + 0.5) / R).astype(np.float32)
+    got = check(logits, T, k, p, u, "shared settings")
+    kept = osm.kept_tokens(row, 0.8, 0, 0.9)
+    w = osm.weights(row, 0.8)[kept].astype(np.float64)
+    freq = np.bincount(got, minlength=V)[kept] / R
+    assert np.abs(freq - w / w.sum()).max() <= 2.0 / R
