@@ -57,7 +57,9 @@ SIGNATURES = {
     "pa_bm_block_table": (_i32, [_vp, ctypes.c_int64, _vp, _i32, ctypes.POINTER(_i32)]),
     "pa_bm_stats": (_i32, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "pa_bm_refcount": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
-    "pa_sample_tokens": (_i32, [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pa_sample_workspace_size": (ctypes.c_size_t, [_i32]),
+    "pa_sample_tokens": (_i32, [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.c_size_t, _vp]),
     "pa_profile_start": (_i32, [_i32]),
     "pa_profile_stop": (_i32, [ctypes.POINTER(_i32)]),
     "pa_profile_get": (_i32, [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(_f32)]),
@@ -347,7 +349,8 @@ def pa_profile_reset():
 
 
 # ---------------------------------------------------------------- block manager
-def pa_sample_tokens(logits, temperature, top_k, top_p, uniforms, out=None, stream=None):
+def pa_sample_tokens(logits, temperature, top_k, top_p, uniforms, out=None, workspace=None,
+                     stream=None):
     """Sample one token per row of ``logits`` [rows, vocab] float32 (row stride
     ``logits.stride(0)``), each row with its own ``temperature``, ``top_k``,
     ``top_p`` and caller-drawn ``uniforms`` in [0, 1) (float32, int32, float32,
@@ -366,9 +369,14 @@ def pa_sample_tokens(logits, temperature, top_k, top_p, uniforms, out=None, stre
     _dev(out, "out", torch.int32, 1)
     if out.shape[0] != R:
         raise ValueError("out must be [rows]")
+    need = int(lib().pa_sample_workspace_size(R))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=logits.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
     _check(lib().pa_sample_tokens(_ptr(logits), logits.stride(0), R, V, _ptr(temperature),
                                   _ptr(top_k), _ptr(top_p), _ptr(uniforms), _ptr(out),
-                                  _stream(stream)), "pa_sample_tokens")
+                                  _ptr(workspace), workspace.numel(), _stream(stream)),
+           "pa_sample_tokens")
     return out
 
 

@@ -11,9 +11,15 @@
 // key, 10 bits per pass over the row, with per-bucket counts, integer weights
 // (64-bit LDS atomics: exact, so the result does not depend on the order of
 // the adds) and the largest key per bucket, stopping as soon as the chosen
-// bucket holds a single token. A last pass walks the row in index order, tile
-// by tile, with a workgroup prefix sum of the kept weights, and stops at the
-// tile where the running weight passes floor(u * S).
+// bucket holds a single token. A last pass walks the tokens in index order,
+// tile by tile, with a workgroup prefix sum of the kept weights, and stops at
+// the tile where the running weight passes floor(u * S).
+//
+// Only two passes read the whole row: the largest logit, then the list, in
+// LDS and in index order, of the tokens that pass a float32 screen for a
+// positive weight. That list is a leading part of the ranking and holds every
+// token of positive weight, so top-k, top-p and the draw run on it alone; a
+// row whose list would not fit runs them over the row instead.
 //
 // Weights are floor(exp((x - max) / T) * 2^32) in float64: the subtraction and
 // the division are IEEE operations (this file is built without contraction),
@@ -47,7 +53,12 @@ struct SampleArgs {
   int32_t ibits;  // bits of the inverted index under the float bits
 };
 
+constexpr int kPer = 8;      // consecutive tokens per thread in the index-order passes
+constexpr int kList = 4096;  // tokens the LDS list holds; a longer list reads the row again
+
 struct SampleLds {
+  float cx[kList];    // listed tokens: logit
+  int32_t ci[kList];  // and index, in index order
   unsigned int cnt[kBins];
   u64 mass[kBins];
   u64 maxkey[kBins];
@@ -63,8 +74,17 @@ __device__ inline u64 sort_key(float x, int32_t i, int ibits) {
   return ((u64)b << ibits) | (u64)inv;
 }
 
-__device__ inline u64 weight(float x, double m, double T) {
-  const double w = exp(((double)x - m) / T);
+// The row's largest logit and temperature, in the two precisions the weights use.
+struct Scale {
+  double m, T;   // float64: the weight's own arithmetic
+  float mf, zf;  // float32 screen: a logit more than zf = 22.5 T below mf weighs 0
+};
+
+// floor(exp((x - m) / T) * 2^32). The float32 screen is conservative: past it,
+// (x - m) / T < -22.5 (1 - 2^-23) < -32 ln 2, so the float64 result is 0 too.
+__device__ inline u64 weight(float x, const Scale& c) {
+  if (c.mf - x > c.zf) return 0ull;
+  const double w = exp(((double)x - c.m) / c.T);
   return (u64)floor(w * 4294967296.0);
 }
 
@@ -77,16 +97,18 @@ __device__ inline u64 wave_incl_scan(u64 v, int lane) {
   return v;
 }
 
-// Inclusive prefix sum over the workgroup in thread order; *total = the sum.
-__device__ inline u64 block_incl_scan(u64 v, SampleLds& L, u64* total) {
+// Inclusive prefix sum over a workgroup of W waves in thread order; *total =
+// the sum. `wave` is W words of LDS.
+template <int W>
+__device__ inline u64 group_incl_scan(u64 v, u64* wave, u64* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_incl_scan(v, lane);
-  if (lane == 63) L.wave[w] = v;
+  if (lane == 63) wave[w] = v;
   __syncthreads();
   u64 before = 0, tot = 0;
 #pragma unroll
-  for (int j = 0; j < kWaves; ++j) {
-    const u64 x = L.wave[j];
+  for (int j = 0; j < W; ++j) {
+    const u64 x = wave[j];
     before += (j < w) ? x : 0ull;
     tot += x;
   }
@@ -95,30 +117,62 @@ __device__ inline u64 block_incl_scan(u64 v, SampleLds& L, u64* total) {
   return v + before;
 }
 
-__device__ inline u64 block_max(u64 v, SampleLds& L) {
+template <int W>
+__device__ inline u64 group_max(u64 v, u64* wave) {
 #pragma unroll
   for (int o = 32; o; o >>= 1) {
-    const u64 w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
+    const u64 x = __shfl_xor(v, o, 64);
+    v = x > v ? x : v;
   }
-  if ((threadIdx.x & 63) == 0) L.wave[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) wave[threadIdx.x >> 6] = v;
   __syncthreads();
   u64 m = 0;
 #pragma unroll
-  for (int j = 0; j < kWaves; ++j) m = L.wave[j] > m ? L.wave[j] : m;
+  for (int j = 0; j < W; ++j) m = wave[j] > m ? wave[j] : m;
   __syncthreads();
   return m;
 }
+
+__device__ inline u64 block_incl_scan(u64 v, SampleLds& L, u64* total) {
+  return group_incl_scan<kWaves>(v, L.wave, total);
+}
+
+__device__ inline u64 block_max(u64 v, SampleLds& L) { return group_max<kWaves>(v, L.wave); }
+
+// Index of the token a sort key belongs to, clamped into [lo, hi).
+__device__ inline int32_t key_index(u64 key, int ibits, int32_t lo, int32_t hi) {
+  const int32_t i = (int32_t)(((1u << ibits) - 1u) - (uint32_t)(key & ((1ull << ibits) - 1ull)));
+  return (i >= lo && i < hi) ? i : lo;
+}
+
+// Where the tokens of one row come from: the row itself, or the list in LDS
+// of its tokens that pass the weight screen. Both are in index order.
+struct RowSrc {
+  const float* row;
+  int n;
+  __device__ float x(int j) const { return row[j]; }
+  __device__ int idx(int j) const { return j; }
+};
+struct ListSrc {
+  const float* cx;
+  const int32_t* ci;
+  int n;
+  __device__ float x(int j) const { return cx[j]; }
+  __device__ int idx(int j) const { return ci[j]; }
+};
 
 // The cutoff C such that the tokens with key >= C (among those with key >=
 // floor_key) are the shortest leading part of the ranking that holds `target`
 // tokens (BY_WEIGHT false) or reaches weight max(ceil(p * total), 1)
 // (BY_WEIGHT true; the total is taken in the first pass).
-template <bool BY_WEIGHT>
-__device__ u64 select_cutoff(const float* row, const SampleArgs& a, u64 floor_key, double m,
-                             double T, float p, u64 target, SampleLds& L) {
+// By weight, tokens of weight 0 are left out: they rank below every token of
+// positive weight (the weight does not decrease with the logit), so the
+// shortest leading part never ends at one.
+template <bool BY_WEIGHT, class Src>
+__device__ u64 select_cutoff(const Src& src, int ibits, u64 floor_key, const Scale& c, float p,
+                             u64 target, SampleLds& L) {
   const int t = threadIdx.x;
-  const int nbits = 32 + a.ibits;
+  const int nbits = 32 + ibits;
   u64 prefix = 0, rem = target;
   int done = 0;
   for (;;) {
@@ -134,14 +188,18 @@ __device__ u64 select_cutoff(const float* row, const SampleArgs& a, u64 floor_ke
       L.sel[3] = ~0ull;
     }
     __syncthreads();
-    for (int i = t; i < a.V; i += kThreads) {
-      const float x = row[i];
-      const u64 k = sort_key(x, i, a.ibits);
+    for (int j = t; j < src.n; j += kThreads) {
+      const float x = src.x(j);
+      const u64 k = sort_key(x, src.idx(j), ibits);
       if (k < floor_key) continue;
       if (done > 0 && (k >> (shift + width)) != prefix) continue;
       const int d = (int)((k >> shift) & (u64)((1u << width) - 1u));
+      if (BY_WEIGHT) {
+        const u64 w = weight(x, c);
+        if (w == 0ull) continue;
+        atomicAdd(&L.mass[d], w);
+      }
       atomicAdd(&L.cnt[d], 1u);
-      if (BY_WEIGHT) atomicAdd(&L.mass[d], weight(x, m, T));
       atomicMax(&L.maxkey[d], k);
     }
     __syncthreads();
@@ -171,84 +229,251 @@ __device__ u64 select_cutoff(const float* row, const SampleArgs& a, u64 floor_ke
   }
 }
 
-__global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a) {
-  __shared__ SampleLds L;
-  const int r = blockIdx.x;
-  const float* row = a.logits + (int64_t)r * a.row_stride;
-  const int V = a.V;
-
-  u64 best = 0;
-  for (int i = threadIdx.x; i < V; i += kThreads) {
-    const u64 k = sort_key(row[i], i, a.ibits);
-    best = k > best ? k : best;
-  }
-  best = block_max(best, L);
-  int32_t top = (int32_t)(((1u << a.ibits) - 1u) - (uint32_t)(best & ((1ull << a.ibits) - 1ull)));
-  if (top < 0 || top >= V) top = 0;
-
-  const float T = a.temperature[r];
-  const int32_t k = a.top_k[r];
-  const float p = a.top_p[r];
-  if (!(T > 0.f) || k == 1) {
-    if (threadIdx.x == 0) a.out[r] = top;
-    return;
-  }
-  const double m = (double)row[top];
-  const double Td = (double)T;
-
+// Top-k, top-p and the draw over the tokens of `src`, which hold every token
+// of positive weight and are a leading part of the ranking. Returns the token.
+template <class Src>
+__device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, float u,
+                        const Scale& c, int32_t top, SampleLds& L) {
   u64 cut = 0;
-  if (k > 1 && k < V) cut = select_cutoff<false>(row, a, 0ull, m, Td, p, (u64)k, L);
+  if (k > 1 && k < src.n) cut = select_cutoff<false>(src, ibits, 0ull, c, p, (u64)k, L);
   if (p < 1.f) {
-    const u64 c2 = select_cutoff<true>(row, a, cut, m, Td, p, 0ull, L);
+    const u64 c2 = select_cutoff<true>(src, ibits, cut, c, p, 0ull, L);
     cut = c2 > cut ? c2 : cut;
   }
 
   u64 s = 0;
-  for (int i = threadIdx.x; i < V; i += kThreads) {
-    const float x = row[i];
-    if (sort_key(x, i, a.ibits) >= cut) s += weight(x, m, Td);
+  for (int j = threadIdx.x; j < src.n; j += kThreads) {
+    const float x = src.x(j);
+    if (sort_key(x, src.idx(j), ibits) >= cut) s += weight(x, c);
   }
   u64 S;
   (void)block_incl_scan(s, L, &S);
-  double tr = floor((double)a.uniforms[r] * (double)S);
+  double tr = floor((double)u * (double)S);
   if (!(tr >= 0.0)) tr = 0.0;
   if (S > 0 && tr > (double)(S - 1)) tr = (double)(S - 1);
   const u64 target = (u64)tr;
 
+  // index order, kPer consecutive tokens per thread, one workgroup scan per tile
   int32_t pick = top;
   u64 run = 0;
   if (threadIdx.x == 0) L.sel[0] = (u64)top;
-  for (int base = 0; base < V; base += kThreads) {
-    const int i = base + (int)threadIdx.x;
-    u64 q = 0;
-    if (i < V) {
-      const float x = row[i];
-      if (sort_key(x, i, a.ibits) >= cut) q = weight(x, m, Td);
+  for (int base = 0; base < src.n; base += kThreads * kPer) {
+    const int j0 = base + (int)threadIdx.x * kPer;
+    u64 q[kPer];
+    u64 qs = 0;
+#pragma unroll
+    for (int jj = 0; jj < kPer; ++jj) {
+      const int j = j0 + jj;
+      u64 w = 0;
+      if (j < src.n) {
+        const float x = src.x(j);
+        if (sort_key(x, src.idx(j), ibits) >= cut) w = weight(x, c);
+      }
+      q[jj] = w;
+      qs += w;
     }
     u64 tile;
-    const u64 inc = block_incl_scan(q, L, &tile);
+    const u64 inc = block_incl_scan(qs, L, &tile);
     if (run + tile > target) {  // the same decision in every thread
-      if (run + inc > target && run + inc - q <= target) L.sel[0] = (u64)i;
+      if (run + inc > target && run + inc - qs <= target) {
+        u64 acc = run + inc - qs;
+#pragma unroll
+        for (int jj = 0; jj < kPer; ++jj) {
+          acc += q[jj];
+          if (acc > target) {
+            L.sel[0] = (u64)src.idx(j0 + jj);
+            break;
+          }
+        }
+      }
       __syncthreads();
       pick = (int32_t)L.sel[0];
       break;
     }
     run += tile;
   }
-  if (threadIdx.x == 0) a.out[r] = (pick >= 0 && pick < V) ? pick : top;
+  return (pick >= 0 && pick < V) ? pick : top;
+}
+
+// Slices of a row: kSlices workgroups of kScreenThreads threads per row find
+// their slice's largest key and list, in index order, the slice's tokens that
+// pass the weight screen against that local maximum (a superset of what the
+// row's maximum lets through), up to kSliceCap of them.
+constexpr int kSlices = 8;
+constexpr int kScreenThreads = 256;
+constexpr int kSliceCap = 1024;
+
+struct Cand {
+  float x;
+  int32_t i;
+};
+
+struct SampleWs {
+  u64* lmax;      // [rows * kSlices] each slice's largest key
+  int32_t* count;  // [rows * kSlices] tokens the slice let through (may exceed kSliceCap)
+  Cand* cand;     // [rows * kSlices * kSliceCap] those tokens, in index order
+};
+
+__global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArgs a, SampleWs w) {
+  __shared__ u64 s_wave[kScreenThreads / 64];
+  const int r = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
+  const int t = threadIdx.x;
+  const float* row = a.logits + (int64_t)r * a.row_stride;
+  const int Ls = (a.V + kSlices - 1) / kSlices;
+  const int lo = min(a.V, sl * Ls), hi = min(a.V, lo + Ls);
+  const size_t slot = (size_t)r * kSlices + sl;
+
+  u64 best = 0;
+  for (int base = lo; base < hi; base += kScreenThreads * kPer) {
+    const int i0 = base + t * kPer;
+    float xs[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) xs[j] = (i0 + j < hi) ? row[i0 + j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (i0 + j < hi) {
+        const u64 k = sort_key(xs[j], i0 + j, a.ibits);
+        best = k > best ? k : best;
+      }
+    }
+  }
+  best = group_max<kScreenThreads / 64>(best, s_wave);
+  if (t == 0) w.lmax[slot] = best;
+  const float T = a.temperature[r];
+  if (!(T > 0.f) || a.top_k[r] == 1 || hi <= lo) {  // greedy rows need only the maximum
+    if (t == 0) w.count[slot] = 0;
+    return;
+  }
+  const float mf = row[key_index(best, a.ibits, lo, hi)];
+  const float zf = 22.5f * T;
+
+  u64 listed = 0;
+  Cand* out = w.cand + slot * kSliceCap;
+  for (int base = lo; base < hi; base += kScreenThreads * kPer) {
+    const int i0 = base + t * kPer;
+    float xs[kPer];
+    unsigned in = 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) xs[j] = (i0 + j < hi) ? row[i0 + j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const bool keep = (i0 + j < hi) && !(mf - xs[j] > zf);
+      in |= (keep ? 1u : 0u) << j;
+      cnt += keep ? 1 : 0;
+    }
+    u64 tile;
+    const u64 inc = group_incl_scan<kScreenThreads / 64>((u64)cnt, s_wave, &tile);
+    u64 pos = listed + inc - (u64)cnt;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if ((in >> j) & 1u) {
+        if (pos < (u64)kSliceCap) out[pos] = Cand{xs[j], i0 + j};
+        ++pos;
+      }
+    }
+    listed += tile;
+  }
+  if (t == 0) w.count[slot] = (int32_t)(listed < 0x7fffffffull ? listed : 0x7fffffffull);
+}
+
+// One workgroup per row: the row's largest key from its slices; greedy rows
+// end there. Otherwise the slices' tokens that also pass the screen against
+// the row's maximum -- exactly the tokens of the row that pass it, in index
+// order -- go to the LDS list, and top-k, top-p and the draw run on it. A
+// slice that overflowed its capacity, or a list longer than kList, sends the
+// row down the path that reads the row itself.
+__global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, SampleWs w) {
+  __shared__ SampleLds L;
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* row = a.logits + (int64_t)r * a.row_stride;
+  const int V = a.V;
+  const size_t slot0 = (size_t)r * kSlices;
+
+  const u64 best = block_max(t < kSlices ? w.lmax[slot0 + t] : 0ull, L);
+  const int32_t top = key_index(best, a.ibits, 0, V);
+  const float T = a.temperature[r];
+  const int32_t k = a.top_k[r];
+  const float p = a.top_p[r];
+  if (!(T > 0.f) || k == 1) {
+    if (t == 0) a.out[r] = top;
+    return;
+  }
+  Scale c;
+  c.mf = row[top];
+  c.m = (double)c.mf;
+  c.T = (double)T;
+  c.zf = 22.5f * T;
+  const float u = a.uniforms[r];
+
+  const bool overflow =
+      block_max((t < kSlices && w.count[slot0 + t] > kSliceCap) ? 1ull : 0ull, L) != 0ull;
+  if (!overflow) {
+    u64 listed = 0;
+    for (int sl = 0; sl < kSlices; ++sl) {
+      const int n = w.count[slot0 + sl];
+      const Cand* cs = w.cand + (slot0 + sl) * kSliceCap;
+      for (int base = 0; base < n; base += kThreads) {
+        const int j = base + t;
+        Cand e{0.f, 0};
+        bool keep = false;
+        if (j < n) {
+          e = cs[j];
+          keep = !(c.mf - e.x > c.zf);
+        }
+        u64 tot;
+        const u64 inc = block_incl_scan(keep ? 1ull : 0ull, L, &tot);
+        if (keep) {
+          const u64 pos = listed + inc - 1ull;
+          if (pos < (u64)kList) {
+            L.cx[pos] = e.x;
+            L.ci[pos] = e.i;
+          }
+        }
+        listed += tot;
+      }
+    }
+    __syncthreads();
+    if (listed <= (u64)kList) {
+      ListSrc src{L.cx, L.ci, (int)listed};
+      const int32_t pick = draw(src, a.ibits, V, k, p, u, c, top, L);
+      if (t == 0) a.out[r] = pick;
+      return;
+    }
+  }
+  RowSrc src{row, V};
+  const int32_t pick = draw(src, a.ibits, V, k, p, u, c, top, L);
+  if (t == 0) a.out[r] = pick;
+}
+
+// Workspace layout: lmax, count, cand, each region 256-byte aligned.
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t ws_lmax_bytes(int32_t rows) { return align256((size_t)rows * kSlices * sizeof(u64)); }
+size_t ws_count_bytes(int32_t rows) { return align256((size_t)rows * kSlices * sizeof(int32_t)); }
+size_t ws_cand_bytes(int32_t rows) {
+  return align256((size_t)rows * kSlices * kSliceCap * sizeof(Cand));
 }
 
 }  // namespace
 
+extern "C" __attribute__((visibility("default"))) size_t pa_sample_workspace_size(int32_t rows) {
+  if (rows <= 0) return 0;
+  return ws_lmax_bytes(rows) + ws_count_bytes(rows) + ws_cand_bytes(rows);
+}
+
 extern "C" __attribute__((visibility("default"))) pa_status_t pa_sample_tokens(
     const float* logits, int64_t row_stride, int32_t rows, int32_t vocab,
     const float* temperature, const int32_t* top_k, const float* top_p, const float* uniforms,
-    int32_t* out_tokens, void* stream) {
+    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0 || vocab < 1 || row_stride < vocab) return PA_ERR_INVALID_ARG;
   if (vocab > kMaxVocab) return PA_ERR_UNSUPPORTED;
   if (rows == 0) return PA_OK;
-  if (!logits || !temperature || !top_k || !top_p || !uniforms || !out_tokens)
+  if (!logits || !temperature || !top_k || !top_p || !uniforms || !out_tokens || !workspace)
     return PA_ERR_INVALID_ARG;
+  if (rows > (1 << 24)) return PA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < pa_sample_workspace_size(rows)) return PA_ERR_WORKSPACE_TOO_SMALL;
   SampleArgs a;
   a.logits = logits;
   a.row_stride = row_stride;
@@ -261,7 +486,15 @@ extern "C" __attribute__((visibility("default"))) pa_status_t pa_sample_tokens(
   int ibits = 1;
   while ((1 << ibits) < vocab) ++ibits;
   a.ibits = ibits;
-  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)rows), dim3(kThreads), 0,
-                     (hipStream_t)stream, a);
+  char* base = static_cast<char*>(workspace);
+  SampleWs w;
+  w.lmax = reinterpret_cast<u64*>(base);
+  w.count = reinterpret_cast<int32_t*>(base + ws_lmax_bytes(rows));
+  w.cand = reinterpret_cast<Cand*>(base + ws_lmax_bytes(rows) + ws_count_bytes(rows));
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(sample_screen_kernel, dim3((unsigned)rows * kSlices), dim3(kScreenThreads), 0,
+                     st, a, w);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  hipLaunchKernelGGL(sample_draw_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, w);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -231,12 +231,18 @@ def test_tick_forward_empty_tick_is_ok_without_touching_memory():
 
 def test_sample_tokens_rejects_bad_scalars_before_any_launch():
     lib = pa.lib()
-    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host checks
+    p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its host checks
+    ws = lib.pa_sample_workspace_size(4)
+    assert ws > 0 and lib.pa_sample_workspace_size(0) == 0
+    assert lib.pa_sample_workspace_size(8) >= 2 * ws - 1024
     f = lambda *a: lib.pa_sample_tokens(*a)
-    assert f(p, 10, -1, 10, p, p, p, p, p, None) == INVALID       # rows < 0
-    assert f(p, 10, 1, 0, p, p, p, p, p, None) == INVALID         # vocab < 1
-    assert f(p, 5, 1, 10, p, p, p, p, p, None) == INVALID         # row_stride < vocab
-    assert f(p, 1 << 22, 1, (1 << 21) + 1, p, p, p, p, p, None) == UNSUPPORTED
-    assert f(None, 10, 1, 10, p, p, p, p, p, None) == INVALID     # NULL logits
-    assert f(p, 10, 1, 10, p, p, p, p, None, None) == INVALID     # NULL out
-    assert f(None, 10, 0, 10, None, None, None, None, None, None) == OK   # no rows: nothing to do
+    assert f(p, 10, -1, 10, p, p, p, p, p, p, ws, None) == INVALID       # rows < 0
+    assert f(p, 10, 1, 0, p, p, p, p, p, p, ws, None) == INVALID         # vocab < 1
+    assert f(p, 5, 1, 10, p, p, p, p, p, p, ws, None) == INVALID         # row_stride < vocab
+    assert f(p, 1 << 22, 1, (1 << 21) + 1, p, p, p, p, p, p, ws, None) == UNSUPPORTED
+    assert f(None, 10, 1, 10, p, p, p, p, p, p, ws, None) == INVALID     # NULL logits
+    assert f(p, 10, 1, 10, p, p, p, p, None, p, ws, None) == INVALID     # NULL out
+    assert f(p, 10, 1, 10, p, p, p, p, p, None, ws, None) == INVALID     # NULL workspace
+    assert f(p, 10, 1, 10, p, p, p, p, p, ctypes.c_void_p(264), ws, None) == INVALID  # misaligned
+    assert f(p, 10, 4, 10, p, p, p, p, p, p, ws - 1, None) == WS_SMALL
+    assert f(None, 10, 0, 10, None, None, None, None, None, None, 0, None) == OK  # no rows
