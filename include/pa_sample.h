@@ -30,14 +30,15 @@
  * first vocab entries of each row used. temperature, top_p, uniforms: float32
  * [rows]; top_k: int32 [rows]; out_tokens: int32 [rows], written. rows >= 0
  * (0 enqueues nothing); 1 <= vocab <= 2^21 (else PA_ERR_UNSUPPORTED);
- * row_stride >= vocab; rows <= 2^24. workspace: device memory of at least
- * pa_sample_workspace_size(rows) bytes, 256-byte aligned, owned by the caller,
+ * row_stride >= vocab; rows * ceil(vocab / 6144) <= 2^30. workspace: device memory
+ * of at least pa_sample_workspace_size(rows, vocab) bytes, 256-byte aligned, owned by the caller,
  * used only while the call's kernels run (calls that share one workspace must
  * not overlap); it needs no clearing. PA_ERR_INVALID_ARG for a bad scalar, a
  * NULL pointer (when rows > 0) or a misaligned workspace,
  * PA_ERR_WORKSPACE_TOO_SMALL for a short one; nothing is enqueued then.
  * Asynchronous on `stream` (a hipStream_t; NULL = the default stream): two
- * launches, a per-slice screen of the rows, then one workgroup per row.
+ * launches, a screen of 6144-token slices of the rows, then one workgroup per
+ * row.
  */
 #ifndef PA_SAMPLE_H
 #define PA_SAMPLE_H
@@ -51,8 +52,9 @@
 extern "C" {
 #endif
 
-/* Workspace bytes pa_sample_tokens needs for `rows` rows (0 for rows <= 0). */
-size_t pa_sample_workspace_size(int32_t rows);
+/* Workspace bytes pa_sample_tokens needs for `rows` rows of `vocab` logits
+ * (0 for rows <= 0 or a vocab outside [1, 2^21]). */
+size_t pa_sample_workspace_size(int32_t rows, int32_t vocab);
 
 pa_status_t pa_sample_tokens(const float* logits, int64_t row_stride, int32_t rows,
                              int32_t vocab, const float* temperature, const int32_t* top_k,

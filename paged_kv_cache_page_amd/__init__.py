@@ -57,7 +57,7 @@ SIGNATURES = {
     "pa_bm_block_table": (_i32, [_vp, ctypes.c_int64, _vp, _i32, ctypes.POINTER(_i32)]),
     "pa_bm_stats": (_i32, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "pa_bm_refcount": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
-    "pa_sample_workspace_size": (ctypes.c_size_t, [_i32]),
+    "pa_sample_workspace_size": (ctypes.c_size_t, [_i32, _i32]),
     "pa_sample_tokens": (_i32, [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_size_t, _vp]),
     "pa_profile_start": (_i32, [_i32]),
@@ -369,7 +369,7 @@ def pa_sample_tokens(logits, temperature, top_k, top_p, uniforms, out=None, work
     _dev(out, "out", torch.int32, 1)
     if out.shape[0] != R:
         raise ValueError("out must be [rows]")
-    need = int(lib().pa_sample_workspace_size(R))
+    need = int(lib().pa_sample_workspace_size(R, V))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=logits.device)
     _dev(workspace, "workspace", torch.uint8, 1)

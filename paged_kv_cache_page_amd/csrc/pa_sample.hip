@@ -15,9 +15,10 @@
 // tile by tile, with a workgroup prefix sum of the kept weights, and stops at
 // the tile where the running weight passes floor(u * S).
 //
-// Only two passes read the whole row: the largest logit, then the list, in
-// LDS and in index order, of the tokens that pass a float32 screen for a
-// positive weight. That list is a leading part of the ranking and holds every
+// The row is read once, split over workgroups of 6144 tokens each: each
+// finds its slice's largest logit and lists the slice's tokens that pass a
+// float32 screen for a positive weight against it; the row's workgroup then
+// keeps those that pass against the row's maximum, in LDS, in index order. That list is a leading part of the ranking and holds every
 // token of positive weight, so top-k, top-p and the draw run on it alone; a
 // row whose list would not fit runs them over the row instead.
 //
@@ -64,6 +65,7 @@ struct SampleLds {
   u64 maxkey[kBins];
   u64 wave[kWaves];
   u64 sel[4];  // chosen bucket, the target left inside it, its count, its largest key
+  uint32_t off[kThreads];  // where each slice's list starts when laid end to end
 };
 
 __device__ inline u64 sort_key(float x, int32_t i, int ibits) {
@@ -295,13 +297,17 @@ __device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, fl
   return (pick >= 0 && pick < V) ? pick : top;
 }
 
-// Slices of a row: kSlices workgroups of kScreenThreads threads per row find
-// their slice's largest key and list, in index order, the slice's tokens that
-// pass the weight screen against that local maximum (a superset of what the
-// row's maximum lets through), up to kSliceCap of them.
-constexpr int kSlices = 8;
+// Slices of a row: ceil(V / kSliceLen) workgroups of kScreenThreads threads per
+// row, each thread holding kRegs consecutive logits in registers (one read of
+// the row), find their slice's largest key and list, in index order, the
+// slice's tokens that pass the weight screen against that local maximum (a
+// superset of what the row's maximum lets through), up to kSliceCap of them.
 constexpr int kScreenThreads = 256;
+constexpr int kRegs = 24;
+constexpr int kSliceLen = kScreenThreads * kRegs;
 constexpr int kSliceCap = 1024;
+constexpr int kMaxSlices = (kMaxVocab + kSliceLen - 1) / kSliceLen;
+static_assert(kMaxSlices <= kThreads, "one slice per drawing thread");
 
 struct Cand {
   float x;
@@ -309,32 +315,30 @@ struct Cand {
 };
 
 struct SampleWs {
-  u64* lmax;      // [rows * kSlices] each slice's largest key
-  int32_t* count;  // [rows * kSlices] tokens the slice let through (may exceed kSliceCap)
-  Cand* cand;     // [rows * kSlices * kSliceCap] those tokens, in index order
+  u64* lmax;       // [rows * nsl] each slice's largest key
+  int32_t* count;  // [rows * nsl] tokens the slice let through (may exceed kSliceCap)
+  Cand* cand;      // [rows * nsl * kSliceCap] those tokens, in index order
+  int nsl;         // slices per row
 };
 
 __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArgs a, SampleWs w) {
   __shared__ u64 s_wave[kScreenThreads / 64];
-  const int r = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
+  const int r = blockIdx.x / w.nsl, sl = blockIdx.x % w.nsl;
   const int t = threadIdx.x;
   const float* row = a.logits + (int64_t)r * a.row_stride;
-  const int Ls = (a.V + kSlices - 1) / kSlices;
-  const int lo = min(a.V, sl * Ls), hi = min(a.V, lo + Ls);
-  const size_t slot = (size_t)r * kSlices + sl;
+  const int lo = sl * kSliceLen, hi = min(a.V, lo + kSliceLen);
+  const int i0 = lo + t * kRegs;
+  const size_t slot = (size_t)r * w.nsl + sl;
 
+  float xs[kRegs];
+#pragma unroll
+  for (int j = 0; j < kRegs; ++j) xs[j] = (i0 + j < hi) ? row[i0 + j] : 0.f;
   u64 best = 0;
-  for (int base = lo; base < hi; base += kScreenThreads * kPer) {
-    const int i0 = base + t * kPer;
-    float xs[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) xs[j] = (i0 + j < hi) ? row[i0 + j] : 0.f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (i0 + j < hi) {
-        const u64 k = sort_key(xs[j], i0 + j, a.ibits);
-        best = k > best ? k : best;
-      }
+  for (int j = 0; j < kRegs; ++j) {
+    if (i0 + j < hi) {
+      const u64 k = sort_key(xs[j], i0 + j, a.ibits);
+      best = k > best ? k : best;
     }
   }
   best = group_max<kScreenThreads / 64>(best, s_wave);
@@ -347,34 +351,26 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
   const float mf = row[key_index(best, a.ibits, lo, hi)];
   const float zf = 22.5f * T;
 
-  u64 listed = 0;
-  Cand* out = w.cand + slot * kSliceCap;
-  for (int base = lo; base < hi; base += kScreenThreads * kPer) {
-    const int i0 = base + t * kPer;
-    float xs[kPer];
-    unsigned in = 0u;
-    int cnt = 0;
+  unsigned in = 0u;
+  int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) xs[j] = (i0 + j < hi) ? row[i0 + j] : 0.f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const bool keep = (i0 + j < hi) && !(mf - xs[j] > zf);
-      in |= (keep ? 1u : 0u) << j;
-      cnt += keep ? 1 : 0;
-    }
-    u64 tile;
-    const u64 inc = group_incl_scan<kScreenThreads / 64>((u64)cnt, s_wave, &tile);
-    u64 pos = listed + inc - (u64)cnt;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if ((in >> j) & 1u) {
-        if (pos < (u64)kSliceCap) out[pos] = Cand{xs[j], i0 + j};
-        ++pos;
-      }
-    }
-    listed += tile;
+  for (int j = 0; j < kRegs; ++j) {
+    const bool keep = (i0 + j < hi) && !(mf - xs[j] > zf);
+    in |= (keep ? 1u : 0u) << j;
+    cnt += keep ? 1 : 0;
   }
-  if (t == 0) w.count[slot] = (int32_t)(listed < 0x7fffffffull ? listed : 0x7fffffffull);
+  u64 listed;
+  const u64 inc = group_incl_scan<kScreenThreads / 64>((u64)cnt, s_wave, &listed);
+  u64 pos = inc - (u64)cnt;
+  Cand* out = w.cand + slot * kSliceCap;
+#pragma unroll
+  for (int j = 0; j < kRegs; ++j) {
+    if ((in >> j) & 1u) {
+      if (pos < (u64)kSliceCap) out[pos] = Cand{xs[j], i0 + j};
+      ++pos;
+    }
+  }
+  if (t == 0) w.count[slot] = (int32_t)listed;
 }
 
 // One workgroup per row: the row's largest key from its slices; greedy rows
@@ -389,9 +385,10 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, Sam
   const int t = threadIdx.x;
   const float* row = a.logits + (int64_t)r * a.row_stride;
   const int V = a.V;
-  const size_t slot0 = (size_t)r * kSlices;
+  const int nsl = w.nsl;
+  const size_t slot0 = (size_t)r * nsl;
 
-  const u64 best = block_max(t < kSlices ? w.lmax[slot0 + t] : 0ull, L);
+  const u64 best = block_max(t < nsl ? w.lmax[slot0 + t] : 0ull, L);
   const int32_t top = key_index(best, a.ibits, 0, V);
   const float T = a.temperature[r];
   const int32_t k = a.top_k[r];
@@ -407,32 +404,39 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, Sam
   c.zf = 22.5f * T;
   const float u = a.uniforms[r];
 
-  const bool overflow =
-      block_max((t < kSlices && w.count[slot0 + t] > kSliceCap) ? 1ull : 0ull, L) != 0ull;
+  const int32_t n_t = t < nsl ? w.count[slot0 + t] : 0;
+  const bool overflow = block_max(n_t > kSliceCap ? 1ull : 0ull, L) != 0ull;
   if (!overflow) {
+    // the slices' lists laid end to end: slice offsets by one scan, then each
+    // flat position finds its slice by binary search over the offsets
+    u64 n_all;
+    const u64 end_t = block_incl_scan((u64)n_t, L, &n_all);
+    if (t < nsl) L.off[t] = (uint32_t)(end_t - (u64)n_t);
+    __syncthreads();
     u64 listed = 0;
-    for (int sl = 0; sl < kSlices; ++sl) {
-      const int n = w.count[slot0 + sl];
-      const Cand* cs = w.cand + (slot0 + sl) * kSliceCap;
-      for (int base = 0; base < n; base += kThreads) {
-        const int j = base + t;
-        Cand e{0.f, 0};
-        bool keep = false;
-        if (j < n) {
-          e = cs[j];
-          keep = !(c.mf - e.x > c.zf);
+    for (int base = 0; base < (int)n_all; base += kThreads) {
+      const int q = base + t;
+      Cand e{0.f, 0};
+      bool keep = false;
+      if (q < (int)n_all) {
+        int lo_s = 0, hi_s = nsl - 1;  // the last slice whose offset is <= q
+        while (lo_s < hi_s) {
+          const int mid = (lo_s + hi_s + 1) >> 1;
+          if ((int)L.off[mid] <= q) lo_s = mid; else hi_s = mid - 1;
         }
-        u64 tot;
-        const u64 inc = block_incl_scan(keep ? 1ull : 0ull, L, &tot);
-        if (keep) {
-          const u64 pos = listed + inc - 1ull;
-          if (pos < (u64)kList) {
-            L.cx[pos] = e.x;
-            L.ci[pos] = e.i;
-          }
-        }
-        listed += tot;
+        e = w.cand[(slot0 + lo_s) * kSliceCap + (size_t)(q - (int)L.off[lo_s])];
+        keep = !(c.mf - e.x > c.zf);
       }
+      u64 tot;
+      const u64 inc = block_incl_scan(keep ? 1ull : 0ull, L, &tot);
+      if (keep) {
+        const u64 pos = listed + inc - 1ull;
+        if (pos < (u64)kList) {
+          L.cx[pos] = e.x;
+          L.ci[pos] = e.i;
+        }
+      }
+      listed += tot;
     }
     __syncthreads();
     if (listed <= (u64)kList) {
@@ -449,17 +453,18 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, Sam
 
 // Workspace layout: lmax, count, cand, each region 256-byte aligned.
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-size_t ws_lmax_bytes(int32_t rows) { return align256((size_t)rows * kSlices * sizeof(u64)); }
-size_t ws_count_bytes(int32_t rows) { return align256((size_t)rows * kSlices * sizeof(int32_t)); }
-size_t ws_cand_bytes(int32_t rows) {
-  return align256((size_t)rows * kSlices * kSliceCap * sizeof(Cand));
-}
+int slices_for(int32_t vocab) { return (vocab + kSliceLen - 1) / kSliceLen; }
+size_t ws_lmax_bytes(size_t n) { return align256(n * sizeof(u64)); }
+size_t ws_count_bytes(size_t n) { return align256(n * sizeof(int32_t)); }
+size_t ws_cand_bytes(size_t n) { return align256(n * kSliceCap * sizeof(Cand)); }
 
 }  // namespace
 
-extern "C" __attribute__((visibility("default"))) size_t pa_sample_workspace_size(int32_t rows) {
-  if (rows <= 0) return 0;
-  return ws_lmax_bytes(rows) + ws_count_bytes(rows) + ws_cand_bytes(rows);
+extern "C" __attribute__((visibility("default"))) size_t pa_sample_workspace_size(int32_t rows,
+                                                                                  int32_t vocab) {
+  if (rows <= 0 || vocab < 1 || vocab > kMaxVocab) return 0;
+  const size_t n = (size_t)rows * slices_for(vocab);
+  return ws_lmax_bytes(n) + ws_count_bytes(n) + ws_cand_bytes(n);
 }
 
 extern "C" __attribute__((visibility("default"))) pa_status_t pa_sample_tokens(
@@ -471,9 +476,9 @@ extern "C" __attribute__((visibility("default"))) pa_status_t pa_sample_tokens(
   if (rows == 0) return PA_OK;
   if (!logits || !temperature || !top_k || !top_p || !uniforms || !out_tokens || !workspace)
     return PA_ERR_INVALID_ARG;
-  if (rows > (1 << 24)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)rows * slices_for(vocab) > (1ll << 30)) return PA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0u) return PA_ERR_INVALID_ARG;
-  if (workspace_bytes < pa_sample_workspace_size(rows)) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < pa_sample_workspace_size(rows, vocab)) return PA_ERR_WORKSPACE_TOO_SMALL;
   SampleArgs a;
   a.logits = logits;
   a.row_stride = row_stride;
@@ -486,14 +491,16 @@ extern "C" __attribute__((visibility("default"))) pa_status_t pa_sample_tokens(
   int ibits = 1;
   while ((1 << ibits) < vocab) ++ibits;
   a.ibits = ibits;
+  const int nsl = slices_for(vocab);
+  const size_t n = (size_t)rows * nsl;
   char* base = static_cast<char*>(workspace);
   SampleWs w;
   w.lmax = reinterpret_cast<u64*>(base);
-  w.count = reinterpret_cast<int32_t*>(base + ws_lmax_bytes(rows));
-  w.cand = reinterpret_cast<Cand*>(base + ws_lmax_bytes(rows) + ws_count_bytes(rows));
+  w.count = reinterpret_cast<int32_t*>(base + ws_lmax_bytes(n));
+  w.cand = reinterpret_cast<Cand*>(base + ws_lmax_bytes(n) + ws_count_bytes(n));
+  w.nsl = nsl;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(sample_screen_kernel, dim3((unsigned)rows * kSlices), dim3(kScreenThreads), 0,
-                     st, a, w);
+  hipLaunchKernelGGL(sample_screen_kernel, dim3((unsigned)n), dim3(kScreenThreads), 0, st, a, w);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   hipLaunchKernelGGL(sample_draw_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, w);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;

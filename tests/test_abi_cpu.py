@@ -232,9 +232,10 @@ def test_tick_forward_empty_tick_is_ok_without_touching_memory():
 def test_sample_tokens_rejects_bad_scalars_before_any_launch():
     lib = pa.lib()
     p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its host checks
-    ws = lib.pa_sample_workspace_size(4)
-    assert ws > 0 and lib.pa_sample_workspace_size(0) == 0
-    assert lib.pa_sample_workspace_size(8) >= 2 * ws - 1024
+    ws = lib.pa_sample_workspace_size(4, 10)
+    assert ws > 0 and lib.pa_sample_workspace_size(0, 10) == 0
+    assert lib.pa_sample_workspace_size(4, 0) == 0 and lib.pa_sample_workspace_size(4, (1 << 21) + 1) == 0
+    assert lib.pa_sample_workspace_size(4, 151936) > 20 * ws
     f = lambda *a: lib.pa_sample_tokens(*a)
     assert f(p, 10, -1, 10, p, p, p, p, p, p, ws, None) == INVALID       # rows < 0
     assert f(p, 10, 1, 0, p, p, p, p, p, p, ws, None) == INVALID         # vocab < 1
