@@ -184,7 +184,7 @@ def bench_sample(steps, warmup, with_cpu):
            "ms_per_launch": round(ms, 5), "steps": steps, "warmup": warmup,
            "config": {"workload": "sampling, 51 rows x 151936 vocab, float32 logits, "
                                   "temperature 0.2, top-p 0.95", "rows": R, "vocab": V},
-           "roofline": {"bound": "hbm", "kernel": "sample_kernel",
+           "roofline": {"bound": "hbm", "kernel": "sample_screen_kernel + sample_draw_kernel",
                         "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": 8000.0,
                         "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 8e12, 4),
                         "bytes_per_launch": nbytes, "traffic": None}}

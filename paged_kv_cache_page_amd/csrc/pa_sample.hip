@@ -298,8 +298,8 @@ __device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, fl
 }
 
 // Slices of a row: ceil(V / kSliceLen) workgroups of kScreenThreads threads per
-// row, each thread holding kRegs consecutive logits in registers (one read of
-// the row), find their slice's largest key and list, in index order, the
+// row, each thread holding kRegs logits in registers (one read of the row),
+// find their slice's largest key and list, in index order, the
 // slice's tokens that pass the weight screen against that local maximum (a
 // superset of what the row's maximum lets through), up to kSliceCap of them.
 constexpr int kScreenThreads = 256;
@@ -327,17 +327,21 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
   const int t = threadIdx.x;
   const float* row = a.logits + (int64_t)r * a.row_stride;
   const int lo = sl * kSliceLen, hi = min(a.V, lo + kSliceLen);
-  const int i0 = lo + t * kRegs;
   const size_t slot = (size_t)r * w.nsl + sl;
 
+  // token lo + kScreenThreads * j + t in register j of thread t: coalesced loads
   float xs[kRegs];
 #pragma unroll
-  for (int j = 0; j < kRegs; ++j) xs[j] = (i0 + j < hi) ? row[i0 + j] : 0.f;
+  for (int j = 0; j < kRegs; ++j) {
+    const int i = lo + kScreenThreads * j + t;
+    xs[j] = (i < hi) ? row[i] : 0.f;
+  }
   u64 best = 0;
 #pragma unroll
   for (int j = 0; j < kRegs; ++j) {
-    if (i0 + j < hi) {
-      const u64 k = sort_key(xs[j], i0 + j, a.ibits);
+    const int i = lo + kScreenThreads * j + t;
+    if (i < hi) {
+      const u64 k = sort_key(xs[j], i, a.ibits);
       best = k > best ? k : best;
     }
   }
@@ -351,26 +355,43 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
   const float mf = row[key_index(best, a.ibits, lo, hi)];
   const float zf = 22.5f * T;
 
-  unsigned in = 0u;
-  int cnt = 0;
+  // index order is (register, wave, lane): per-(register, wave) counts from
+  // ballots, their exclusive offsets, then each lane's place among its wave's
+  constexpr int kW = kScreenThreads / 64;
+  __shared__ uint32_t s_cnt[kRegs][kW];
+  __shared__ uint32_t s_total;
+  const int lane = t & 63, wv = t >> 6;
+  const u64 below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int j = 0; j < kRegs; ++j) {
-    const bool keep = (i0 + j < hi) && !(mf - xs[j] > zf);
-    in |= (keep ? 1u : 0u) << j;
-    cnt += keep ? 1 : 0;
+    const int i = lo + kScreenThreads * j + t;
+    const u64 bal = __ballot((i < hi) && !(mf - xs[j] > zf));
+    if (lane == 0) s_cnt[j][wv] = (uint32_t)__popcll(bal);
   }
-  u64 listed;
-  const u64 inc = group_incl_scan<kScreenThreads / 64>((u64)cnt, s_wave, &listed);
-  u64 pos = inc - (u64)cnt;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t run = 0;
+    for (int j = 0; j < kRegs; ++j)
+      for (int v = 0; v < kW; ++v) {
+        const uint32_t n = s_cnt[j][v];
+        s_cnt[j][v] = run;
+        run += n;
+      }
+    s_total = run;
+  }
+  __syncthreads();
   Cand* out = w.cand + slot * kSliceCap;
 #pragma unroll
   for (int j = 0; j < kRegs; ++j) {
-    if ((in >> j) & 1u) {
-      if (pos < (u64)kSliceCap) out[pos] = Cand{xs[j], i0 + j};
-      ++pos;
+    const int i = lo + kScreenThreads * j + t;
+    const bool keep = (i < hi) && !(mf - xs[j] > zf);
+    const u64 bal = __ballot(keep);
+    if (keep) {
+      const uint32_t pos = s_cnt[j][wv] + (uint32_t)__popcll(bal & below);
+      if (pos < (uint32_t)kSliceCap) out[pos] = Cand{xs[j], i};
     }
   }
-  if (t == 0) w.count[slot] = (int32_t)listed;
+  if (t == 0) w.count[slot] = (int32_t)s_total;
 }
 
 // One workgroup per row: the row's largest key from its slices; greedy rows

@@ -112,3 +112,21 @@ def test_rows_sharing_settings_sample_their_own_distribution():
     w = osm.weights(row, 0.8)[kept].astype(np.float64)
     freq = np.bincount(got, minlength=V)[kept] / R
     assert np.abs(freq - w / w.sum()).max() <= 2.0 / R
+
+
+@pytest.mark.parametrize("sigma,T,where", [
+    (4.0, 0.2, "short list"),
+    (2.0, 0.2, "list of 1025-4096 tokens, radix descent over the list"),
+    (1.0, 1.0, "slices overflow, radix descent over the row"),
+])
+def test_each_draw_path(sigma, T, where):
+    # 24576 tokens = 4 slices of 6144; the logit spread against the temperature
+    # sets how many tokens pass the weight screen, and so which path a row takes
+    rng = np.random.default_rng(int(sigma * 100))
+    R, V = 24, 24576
+    logits = (rng.standard_normal((R, V)) * sigma).astype(np.float32)
+    Tr = np.full(R, T, np.float32)
+    k = rng.choice([0, 0, 40, 900, 3000], R).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.6, 0.2], R).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    check(logits, Tr, k, p, u, where)
