@@ -2,7 +2,9 @@
 numpy's argmax for greedy rows, a hand-worked top-p example, the sampled
 frequencies over a fine grid of uniforms against probabilities computed by
 brute force with Python floats and sorted(), exact identities of the
-temperature, and the ends of the uniform range."""
+temperature, and the ends of the uniform range. Planted mistakes (tie order,
+top-p and top-k off by one, temperature or max shift dropped, drawing in
+ranking order) are each caught by at least one pin."""
 
 import math
 
@@ -109,3 +111,81 @@ def test_weights_are_exact_integers():
     assert int(w[0]) == 2 ** 32
     assert int(w[1]) == math.floor(math.exp(-1.0) * 2 ** 32)
     assert int(w[2]) == math.floor(math.exp(-2.0) * 2 ** 32)
+
+
+# ------------------------------------------- planted mistakes must be caught
+PINS = [test_greedy_is_numpy_argmax, test_signed_zero_ties_by_index, test_top_p_worked_example,
+        lambda: test_frequencies_match_brute_force_probabilities(0.8, 0, 0.7),
+        lambda: test_frequencies_match_brute_force_probabilities(1.3, 5, 0.9),
+        lambda: test_frequencies_match_brute_force_probabilities(2.0, 0, 1.0),
+        test_temperature_divides_the_logit_gap, test_uniform_ends_pick_first_and_last_kept_index,
+        test_weights_are_exact_integers]
+
+
+def _caught():
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+def _ties_high_index_first(x):
+    x = np.asarray(x, dtype=np.float64) + 0.0
+    return np.lexsort((-np.arange(x.size), -x))
+
+
+def _top_p_one_too_many(x, temperature, top_k, top_p):
+    order = osm.ranking(x)
+    if 0 < top_k < order.size:
+        order = order[:top_k]
+    if top_p < 1.0:
+        w = osm.weights(x, temperature)[order]
+        need = max(math.ceil(float(np.float32(top_p)) * float(int(w.sum()))), 1)
+        cum = np.cumsum(w.astype(object))
+        t = next(i for i, c in enumerate(cum) if c >= need)
+        order = order[:t + 2]
+    return order
+
+
+def _top_k_plus_one(x, temperature, top_k, top_p):
+    return _orig["kept_tokens"](x, temperature, top_k + 1 if top_k > 0 else top_k, top_p)
+
+
+def _no_temperature(x, temperature):
+    return _orig["weights"](x, 1.0)
+
+
+def _no_max_shift(x, temperature):
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        w = np.floor(np.exp(x / np.float64(temperature)) * osm.TWO32)
+        return np.nan_to_num(w, posinf=2.0 ** 63).astype(np.uint64)
+
+
+def _draw_in_ranking_order(x, temperature, top_k, top_p, u):
+    x = np.asarray(x, dtype=np.float32)
+    if not temperature > 0 or top_k == 1:
+        return int(osm.ranking(x)[0])
+    kept = osm.kept_tokens(x, temperature, top_k, top_p)
+    w = osm.weights(x, temperature)
+    S = int(w[kept].sum())
+    target, run = int(math.floor(float(np.float32(u)) * S)), 0
+    for i in kept:
+        run += int(w[i])
+        if run > target:
+            return int(i)
+
+
+_orig = {"ranking": osm.ranking, "kept_tokens": osm.kept_tokens, "weights": osm.weights,
+         "sample_row": osm.sample_row}
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("ranking", _ties_high_index_first), ("kept_tokens", _top_p_one_too_many),
+    ("kept_tokens", _top_k_plus_one), ("weights", _no_temperature), ("weights", _no_max_shift),
+    ("sample_row", _draw_in_ranking_order)])
+def test_planted_mistakes_are_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(osm, name, fn)
+    assert _caught(), f"a mistake in {name} ({fn.__name__}) passes every pin"
