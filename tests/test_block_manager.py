@@ -12,6 +12,10 @@
 * The library (``pa_bm_*`` in libpa.so) equals the oracle step by step on the
   same traces: every return value, error, block table, count and reference
   count.
+* Planted mistakes in the oracle (a FIFO free list, restoring the last
+  token's block, most-recently-used or parent-first eviction, restored pages
+  left unreferenced, partial blocks published) are each caught by a pin that
+  involves the oracle alone.
 """
 
 import random
@@ -355,10 +359,11 @@ def test_library_argument_checks():
 
 
 # ------------------------------------------------------- seeded random traces
-def run_trace(seed, N, P, steps):
+def run_trace(seed, N, P, steps, with_lib=True):
     rng = random.Random(seed)
     docs = [[rng.randrange(1, 50) for _ in range(6 * P)] for _ in range(3)]
-    ora, lib = Ora(N, P), Lib(N, P)
+    ora = Ora(N, P)
+    lib = Lib(N, P) if with_lib else Ora(N, P)
     live, next_id = [], 0
     for _ in range(steps):
         op = rng.random()
@@ -423,3 +428,101 @@ def test_library_equals_oracle_on_random_traces(seed, N, P):
     ora = run_trace(seed, N, P, 300)
     # the traces exercise restores, evictions and refusals
     assert ora.m.next_seq > 0
+
+
+
+# ------------------------------------------- planted mistakes must be caught
+def _oracle_pins():
+    """The pins that involve the oracle alone (no library)."""
+    return [lambda: test_shared_prefix_shares_physical_pages(Ora),
+            lambda: test_partial_and_last_blocks(Ora),
+            lambda: test_only_written_prompt_blocks_are_published(Ora),
+            lambda: test_leaf_first_lru_eviction(Ora),
+            lambda: test_eviction_never_takes_a_held_block_and_restores_refresh_lru(Ora),
+            lambda: test_reservation_keeps_decode_going(Ora),
+            lambda: test_failed_admission_evicts_but_keeps_its_restored_blocks(Ora),
+            lambda: test_release_on_last_reference(Ora),
+            lambda: run_trace(2, 24, 4, 200, with_lib=False),
+            lambda: run_trace(7, 6, 3, 200, with_lib=False)]
+
+
+def _caught():
+    for pin in _oracle_pins():
+        try:
+            pin()
+        except (AssertionError, ValueError, KeyError, IndexError, ob.NoPages):
+            return True
+    return False
+
+
+def _fifo_take(self):
+    p = self.free.pop(0)
+    self.refcount[p] = 1
+    return p
+
+
+def _match_includes_last_token(self, prompt):
+    pages, hashes, key = [], [], 0
+    for b in range(len(prompt) // self.P):
+        blk = list(prompt[b * self.P:(b + 1) * self.P])
+        h = ob.block_hash(key, blk)
+        e = self.cache.get(h)
+        if e is None or e["parent"] != key or e["tokens"] != blk:
+            break
+        pages.append(e["page"])
+        hashes.append(h)
+        key = h
+    return pages, hashes
+
+
+def _evict_most_recent(self):
+    cands = [(-e["last_use"], -e["seq"], h) for h, e in self.cache.items()
+             if e["children"] == 0 and self.refcount[e["page"]] == 1]
+    if not cands:
+        return False
+    h = min(cands)[2]
+    e = self.cache.pop(h)
+    if e["parent"] in self.cache:
+        self.cache[e["parent"]]["children"] -= 1
+    self._drop(e["page"])
+    return True
+
+
+def _evict_ignoring_children(self):
+    cands = [(e["last_use"], e["seq"], h) for h, e in self.cache.items()
+             if self.refcount[e["page"]] == 1]
+    if not cands:
+        return False
+    h = min(cands)[2]
+    e = self.cache.pop(h)
+    self._drop(e["page"])
+    return True
+
+
+_orig_admit = ob.BlockManager.admit
+
+
+def _admit_without_restore_refs(self, req, prompt, max_new_tokens):
+    n = _orig_admit(self, req, prompt, max_new_tokens)
+    for p in self.reqs[req]["pages"]:
+        self.refcount[p] -= 1          # restored pages left unreferenced
+    return n
+
+
+def _publish_partial_blocks(self, req, publish=True):
+    r = self.reqs[req]
+    r["prompt"] = r["prompt"] + [0] * (-len(r["prompt"]) % self.P)   # the partial block, padded
+    r["tokens"] += -r["tokens"] % self.P                             # counted as written
+    return _orig_finish(self, req, publish)
+
+
+_orig_finish = ob.BlockManager.finish
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("_take", _fifo_take), ("_match", _match_includes_last_token),
+    ("_evict_one", _evict_most_recent), ("_evict_one", _evict_ignoring_children),
+    ("admit", _admit_without_restore_refs), ("finish", _publish_partial_blocks)])
+def test_planted_mistakes_are_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(ob.BlockManager, name, fn)
+    assert _caught(), f"a mistake in {name} ({fn.__name__}) passes every oracle pin"
