@@ -30,14 +30,14 @@
  * first vocab entries of each row used. temperature, top_p, uniforms: float32
  * [rows]; top_k: int32 [rows]; out_tokens: int32 [rows], written. rows >= 0
  * (0 enqueues nothing); 1 <= vocab <= 2^21 (else PA_ERR_UNSUPPORTED);
- * row_stride >= vocab; rows * ceil(vocab / 6144) <= 2^30. workspace: device memory
+ * row_stride >= vocab; rows * ceil(vocab / 3072) <= 2^30. workspace: device memory
  * of at least pa_sample_workspace_size(rows, vocab) bytes, 256-byte aligned, owned by the caller,
  * used only while the call's kernels run (calls that share one workspace must
  * not overlap); it needs no clearing. PA_ERR_INVALID_ARG for a bad scalar, a
  * NULL pointer (when rows > 0) or a misaligned workspace,
  * PA_ERR_WORKSPACE_TOO_SMALL for a short one; nothing is enqueued then.
  * Asynchronous on `stream` (a hipStream_t; NULL = the default stream): two
- * launches, a screen of 6144-token slices of the rows, then one workgroup per
+ * launches, a screen of 3072-token slices of the rows, then one workgroup per
  * row.
  */
 #ifndef PA_SAMPLE_H

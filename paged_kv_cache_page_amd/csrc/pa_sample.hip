@@ -15,7 +15,7 @@
 // tile by tile, with a workgroup prefix sum of the kept weights, and stops at
 // the tile where the running weight passes floor(u * S).
 //
-// The row is read once, split over workgroups of 6144 tokens each: each
+// The row is read once, split over workgroups of 3072 tokens each: each
 // finds its slice's largest logit and lists the slice's tokens that pass a
 // float32 screen for a positive weight against it; the row's workgroup then
 // keeps those that pass against the row's maximum, in LDS, in index order. That list is a leading part of the ranking and holds every
@@ -303,7 +303,7 @@ __device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, fl
 // slice's tokens that pass the weight screen against that local maximum (a
 // superset of what the row's maximum lets through), up to kSliceCap of them.
 constexpr int kScreenThreads = 256;
-constexpr int kRegs = 24;
+constexpr int kRegs = 12;
 constexpr int kSliceLen = kScreenThreads * kRegs;
 constexpr int kSliceCap = 1024;
 constexpr int kMaxSlices = (kMaxVocab + kSliceLen - 1) / kSliceLen;

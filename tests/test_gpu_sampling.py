@@ -120,7 +120,7 @@ def test_rows_sharing_settings_sample_their_own_distribution():
     (1.0, 1.0, "slices overflow, radix descent over the row"),
 ])
 def test_each_draw_path(sigma, T, where):
-    # 24576 tokens = 4 slices of 6144; the logit spread against the temperature
+    # 24576 tokens = 8 slices of 3072; the logit spread against the temperature
     # sets how many tokens pass the weight screen, and so which path a row takes
     rng = np.random.default_rng(int(sigma * 100))
     R, V = 24, 24576
