@@ -11,20 +11,28 @@ contexts U[256, 4096] plus prefill chunks of 512/512/1024 tokens after 0-3
 cached 256-token pages; 32 query / 8 KV heads, head_dim 128, bf16, seed 1004).
 Inputs sit in HBM before timing starts; three copies of every buffer are
 rotated between steps so no step finds the previous step's pages in the
-256 MB Infinity Cache.
+256 MB Infinity Cache ("cold"); the same steps on one copy are reported as
+"warm".
 
 Prints ONE JSON line. `value` = tick tokens per second. `roofline` refers to
-the dominant kernel (for a mixed tick the fused decode + prefill kernel, an HBM
-stream), timed per launch with HIP events the library records on its launch
-stream; `legs` times the same tick's decode rows alone and prefill chunks alone
-(attention only). `cpu_baseline` = the CPU oracle (RoPE + write + float64
-attention) on the same tick.
+the dominant kernel of the step (the fused decode + prefill kernel), timed per
+launch with HIP events the library records on its launch stream: its HBM
+fraction counts the decode rows' algorithmic bytes (unique physical pages) over
+the kernel's median duration; the prefill chunks' work is flops, scored on
+their own leg. `legs` times, attention only, the same tick's decode rows alone
+(HBM) and prefill chunks alone (MFMA), and the Qwen3-4B decode tick and the
+prefix-shared long-context tick whole (their decode kernel's HBM fraction on
+unique pages, logical bytes beside it). `practical_peak` is a plain read-only
+stream over 2 GiB on the same GPU. `cpu_baseline` = the CPU oracle (RoPE +
+write + float64 attention) on the same tick.
 """
 
 import argparse
 import json
 import math
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -36,44 +44,281 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-attn KV read GB/s (% HBM peak) + packed-tick attn tokens/s, Qwen3-4B"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+MFMA_BF16_FLOP_PER_CLK_CU = 4096  # 4 SIMDs x 1024 dense bf16 flops per clock (gfx950)
 WORKLOADS = {"cfg2": 2, "cfg3": 3, "cfg4": 4, "cfg5": 5}
 ROTATE = 3
+ATTN_NAMES = ("tick_attention", "decode_attention", "prefill_attention_mfma")
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(t):
-    """Bytes / flops the method itself must move / compute (no re-reads, no scratch).
+# ----------------------------------------------------------------- accounting
+def decode_work(t):
+    """Algorithmic bytes of the tick's decode rows (query length 1).
 
-    Decode row of a sequence with n keys: K and V rows n*Hkv*D*e each, the
-    query and output rows Hq*D*e each, and 4 bytes per page-table entry used.
-    Prefill chunk of L rows after P0 cached keys: 4*D*Hq*pairs flops over the
-    unmasked (row, key) pairs, pairs = L*P0 + L(L+1)/2; its bytes are the K and
-    V rows of its n = P0 + L keys read once per KV head, its query and output
-    rows, and its page-table entries.
+    Per row with n keys: its K and V rows (n*Hkv*D*e each), its query and
+    output rows (Hq*D*e each) and 4 bytes per page-table entry used. `unique`
+    counts each physical page's rows once however many sequences read it
+    (pages shared by a prefix are read by every sharer, but a kernel that
+    streams them from HBM once per tick needs them once); `logical` sums every
+    row's own K/V bytes.
     """
     e = 2 if t.dtype == "bf16" else 4
-    dec_bytes = 0
-    dec_kv = 0
-    flops = 0
-    pf_bytes = 0
+    row_bytes = t.Hkv * t.D * e
+    rows_of_page = {}
+    logical_kv = 0
+    other = 0
+    n_rows = 0
     for s in range(t.S):
         n, L = int(t.seq_lens[s]), int(t.query_lens[s])
-        if L == 1:
-            kv = 2 * n * t.Hkv * t.D * e
-            dec_kv += kv
-            dec_bytes += kv + 2 * t.Hq * t.D * e + 4 * math.ceil(n / t.P)
-        elif L > 1:
+        if L != 1:
+            continue
+        n_rows += 1
+        logical_kv += 2 * n * row_bytes
+        pages = math.ceil(n / t.P)
+        other += 2 * t.Hq * t.D * e + 4 * pages
+        for j in range(pages):
+            pg = int(t.block_tables[s, j])
+            rows_of_page[pg] = max(rows_of_page.get(pg, 0), min(t.P, n - j * t.P))
+    unique_kv = 2 * row_bytes * sum(rows_of_page.values())
+    return {"rows": n_rows, "unique_kv_bytes": unique_kv, "logical_kv_bytes": logical_kv,
+            "bytes": unique_kv + other, "logical_bytes": logical_kv + other}
+
+
+def prefill_work(t):
+    """Flops of the tick's prefill chunks: 4*D*Hq per unmasked (row, key) pair,
+    pairs = L*P0 + L(L+1)/2 for a chunk of L rows after P0 cached keys."""
+    flops = 0
+    for s in range(t.S):
+        n, L = int(t.seq_lens[s]), int(t.query_lens[s])
+        if L > 1:
             p0 = n - L
-            pairs = L * p0 + L * (L + 1) // 2
-            flops += 4 * t.D * t.Hq * pairs
-            pf_bytes += 2 * n * t.Hkv * t.D * e + 2 * L * t.Hq * t.D * e + 4 * math.ceil(n / t.P)
-    T = t.T
-    k1_bytes = T * ((t.Hq + 2 * t.Hkv) * t.D * e + 8 + t.D * 4) + T * (t.Hq + 3 * t.Hkv) * t.D * e
-    return {"decode_bytes": dec_bytes, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
-            "prefill_bytes": pf_bytes, "k1_bytes": k1_bytes}
+            flops += 4 * t.D * t.Hq * (L * p0 + L * (L + 1) // 2)
+    return flops
+
+
+def k1_bytes(t):
+    """RoPE + page write per token: reads q, k, v rows, the position and slot and
+    the cos/sin row; writes q and k back and K/V into the pools."""
+    e = 2 if t.dtype == "bf16" else 4
+    return t.T * ((t.Hq + 2 * t.Hkv) * t.D * e + 8 + t.D * 4) + t.T * (t.Hq + 3 * t.Hkv) * t.D * e
+
+
+def stats(v):
+    a = np.asarray(v, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 5), "min_ms": round(float(a.min()), 5),
+            "p90_ms": round(float(np.percentile(a, 90)), 5), "mean_ms": round(float(a.mean()), 5),
+            "launches": int(a.size)}
+
+
+def kernel_stats(recs):
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    return {n: stats(v) for n, v in per.items()}
+
+
+# --------------------------------------------------------------- the machine
+def rocminfo_peaks():
+    """CU count and peak engine clock of the gfx950 agent from rocminfo, and
+    the bf16 dense MFMA peak they give (CUs x clock x 4096 flops/clock)."""
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception as e:  # noqa: BLE001 - reported, not fatal
+        return {"error": f"rocminfo: {e}"}
+    for agent in out.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"compute_units": cus, "max_clock_mhz": clk,
+                    "mfma_bf16_dense_tflops": round(cus * clk * 1e6 * MFMA_BF16_FLOP_PER_CLK_CU
+                                                    / 1e12, 1)}
+    return {"error": "no gfx950 agent in rocminfo"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def practical_peak(pa, torch, dev, steps):
+    """A plain read-only stream over 2 GiB (16-byte loads, the whole GPU):
+    median bandwidth over `steps` launches."""
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    sink = None
+    for _ in range(3):
+        sink = pa.pa_probe_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    pa.pa_profile_start(steps + 4)
+    for _ in range(steps):
+        pa.pa_probe_stream_read(buf, sink)
+    recs = pa.pa_profile_stop()
+    pa.pa_profile_reset()
+    ms = float(np.median([m for _, m in recs]))
+    del buf, sink
+    return {"read_only_gbps": round((2 << 30) / (ms / 1e3) / 1e9, 1),
+            "bytes": 2 << 30, "median_ms": round(ms, 5), "kernel": "stream_read"}
+
+
+# ------------------------------------------------------------------ the tick
+class DeviceTick:
+    """`copies` copies of a tick's buffers in HBM, and one step of it."""
+
+    def __init__(self, t, torch, pa, dev, copies, kv_split, separate=False):
+        self.t, self.torch, self.pa = t, torch, pa
+        self.kv_split, self.separate = kv_split, separate
+
+        def st(a):
+            if t.dtype == "f32":
+                return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+        self.copies = []
+        for _ in range(copies):
+            self.copies.append({
+                "q": st(t.q), "k": st(t.k), "v": st(t.v), "kp": st(t.k_pool),
+                "vp": st(t.v_pool), "bt": i32(t.block_tables), "sl": i32(t.seq_lens),
+                "qsl": i32(t.qsl), "pos": i32(t.positions),
+                "slots": torch.empty(t.T, dtype=torch.int32, device=dev),
+                "out": torch.empty((t.T, t.Hq, t.D), dtype=torch.bfloat16 if t.dtype == "bf16"
+                                   else torch.float32, device=dev),
+            })
+        self.table = pa.pa_rope_cos_sin_table(t.max_pos, t.D, t.theta, device=dev)
+        self.dt = pa.PA_BF16 if t.dtype == "bf16" else pa.PA_F32
+        ws = pa.pa_paged_attention_workspace_size(t.S, t.T, t.Hq, t.D, t.max_query_len,
+                                                  t.max_seq_len, t.P, kv_split, self.dt)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i):
+        t, pa, c = self.t, self.pa, self.copies[i % len(self.copies)]
+        if not self.separate:
+            pa.pa_tick_forward(c["q"], c["k"], c["v"], c["pos"], c["bt"], c["sl"], c["qsl"],
+                               self.table, c["kp"], c["vp"], t.max_query_len, t.max_seq_len,
+                               scale=t.scale, kv_split_tokens=self.kv_split, out=c["out"],
+                               slot_mapping=c["slots"], workspace=self.ws, stream=self.stream)
+            return
+        pa.pa_compute_slot_mapping(c["bt"], c["qsl"], c["pos"], t.P, t.num_pages, out=c["slots"],
+                                   stream=self.stream)
+        pa.pa_rope_and_cache_write(c["q"], c["k"], c["v"], c["pos"], c["slots"], self.table,
+                                   c["kp"], c["vp"], stream=self.stream)
+        pa.pa_paged_attention_varlen(c["q"], c["kp"], c["vp"], c["bt"], c["sl"], c["qsl"],
+                                     t.max_query_len, t.max_seq_len, scale=t.scale,
+                                     kv_split_tokens=self.kv_split, out=c["out"],
+                                     workspace=self.ws, stream=self.stream)
+
+    def sub(self, mask):
+        """Attention-only steps over the sequences in `mask` (rows, tables and
+        lengths selected; the pools of each copy shared)."""
+        t, torch, pa = self.t, self.torch, self.pa
+        seqs = np.nonzero(mask)[0]
+        rows = np.concatenate([np.arange(t.qsl[s], t.qsl[s + 1]) for s in seqs]).astype(np.int64)
+        ql = t.query_lens[seqs].astype(np.int64)
+        qsl = np.zeros(len(seqs) + 1, np.int32)
+        qsl[1:] = np.cumsum(ql)
+        dev = self.copies[0]["q"].device
+        ridx = torch.from_numpy(rows).to(dev)
+        sidx = torch.from_numpy(seqs.astype(np.int64)).to(dev)
+        subs = []
+        for c in self.copies:
+            q = c["q"].index_select(0, ridx).contiguous()
+            subs.append({"q": q, "out": torch.empty_like(q),
+                         "bt": c["bt"].index_select(0, sidx).contiguous(),
+                         "sl": c["sl"].index_select(0, sidx).contiguous(),
+                         "qsl": torch.from_numpy(qsl).to(dev)})
+        S, T = int(len(seqs)), int(qsl[-1])
+        mql, msl = int(ql.max()), int(t.seq_lens[seqs].max())
+        ws = torch.empty(max(pa.pa_paged_attention_workspace_size(
+            S, T, t.Hq, t.D, mql, msl, t.P, self.kv_split, self.dt), 1), dtype=torch.uint8,
+            device=dev)
+
+        def sub_step(i):
+            c, u = self.copies[i % len(self.copies)], subs[i % len(subs)]
+            pa.pa_paged_attention_varlen(u["q"], c["kp"], c["vp"], u["bt"], u["sl"], u["qsl"],
+                                         mql, msl, scale=t.scale, kv_split_tokens=self.kv_split,
+                                         out=u["out"], workspace=ws, stream=self.stream)
+        return sub_step
+
+
+def timed(torch, step, steps, warmup, stream, wall=None):
+    """Warm-up, then `steps` steps between two events (synchronised on both
+    sides): ms per step. `wall`, a list, receives the host seconds of the
+    timed region."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    if wall is not None:
+        wall.append(time.perf_counter() - w0)
+    return ev0.elapsed_time(ev1) / steps
+
+
+def profiled(pa, torch, step, steps):
+    """The same steps again with the library's per-launch events."""
+    torch.cuda.synchronize()
+    pa.pa_profile_start(16 * steps + 16)
+    for i in range(steps):
+        step(i)
+    recs = pa.pa_profile_stop()
+    pa.pa_profile_reset()
+    return kernel_stats(recs)
+
+
+def hbm_entry(kernel, ks, nbytes, extra=None):
+    ms = ks[kernel]["median_ms"]
+    gbps = nbytes / (ms / 1e3) / 1e9
+    e = {"kernel": kernel, "bound": "hbm", "bytes_per_launch": int(nbytes),
+         "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), **ks[kernel]}
+    if extra:
+        e.update(extra)
+    return e
+
+
+def dominant(ks):
+    return max((n for n in ks if n in ATTN_NAMES), key=lambda n: ks[n]["median_ms"], default=None)
+
+
+def decode_config_leg(cfg, pa, torch, W, dev, steps, warmup, kv_split):
+    """A whole decode tick of workload `cfg` (pa_tick_forward), and its decode
+    kernel against the HBM roofline on unique and logical bytes."""
+    t = W.make_config(cfg, poison=False)
+    dt_ = DeviceTick(t, torch, pa, dev, ROTATE, kv_split)
+    ms = timed(torch, dt_.step, steps, warmup, dt_.stream)
+    ks = profiled(pa, torch, dt_.step, steps)
+    work = decode_work(t)
+    k = dominant(ks)
+    kms = ks[k]["median_ms"]
+    leg = hbm_entry(k, ks, work["bytes"], {
+        "workload": t.name, "ms_per_step": round(ms, 5),
+        "tick_tokens_per_s": round(t.T / (ms / 1e3), 1),
+        "unique_kv_bytes": work["unique_kv_bytes"], "logical_kv_bytes": work["logical_kv_bytes"],
+        "logical_gbps": round(work["logical_bytes"] / (kms / 1e3) / 1e9, 1),
+        "all_kernels": ks})
+    del dt_
+    torch.cuda.empty_cache()
+    return leg
 
 
 def cpu_baseline(t, reps):
@@ -82,7 +327,7 @@ def cpu_baseline(t, reps):
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
+    except Exception:  # noqa: BLE001
         threads = 1
     table = oracle.rope_table(t.max_pos, t.D, t.theta) if t.theta is not None else None
     times = []
@@ -96,27 +341,8 @@ def cpu_baseline(t, reps):
     return {"value": t.T / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"the full tick ({t.T} query rows, {t.S} sequences), {len(times)} runs, median "
                       f"{med:.2f} s per tick; numpy float32 RoPE + float64 attention",
-            "seconds_per_tick": med,
-            "host_cpus": len(os.sched_getaffinity(0))}
-
-
-def sub_tick(t, c, mask, dev):
-    """Device tensors of the tick restricted to the sequences in `mask` (rows,
-    page tables and lengths selected; the pools are shared)."""
-    import torch
-    seqs = np.nonzero(mask)[0]
-    rows = np.concatenate([np.arange(t.qsl[s], t.qsl[s + 1]) for s in seqs]).astype(np.int64)
-    ql = t.query_lens[seqs].astype(np.int64)
-    qsl = np.zeros(len(seqs) + 1, np.int32)
-    qsl[1:] = np.cumsum(ql)
-    ridx = torch.from_numpy(rows).to(dev)
-    sidx = torch.from_numpy(seqs.astype(np.int64)).to(dev)
-    q = c["q"].index_select(0, ridx).contiguous()
-    return {"q": q, "out": torch.empty_like(q),
-            "bt": c["bt"].index_select(0, sidx).contiguous(),
-            "sl": c["sl"].index_select(0, sidx).contiguous(),
-            "qsl": torch.from_numpy(qsl).to(dev), "S": int(len(seqs)), "T": int(qsl[-1]),
-            "mql": int(ql.max()), "msl": int(t.seq_lens[seqs].max())}
+            "seconds_per_tick": med, "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model()}
 
 
 def kernel_sources_digest():
@@ -151,6 +377,7 @@ def committed_traffic(kernel, workload):
     return None
 
 
+# ------------------------------------------------------------- other benches
 def bench_sample(steps, warmup, with_cpu):
     """pa_sample_tokens over one logits row per sequence of the packed mixed tick
     (51 rows) at Qwen3's vocabulary (151936), float32 logits N(0, 4^2), with the
@@ -264,6 +491,7 @@ def bench_block_manager(steps):
                       "note": "includes the ctypes binding's per-call cost"}))
 
 
+# ---------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +501,11 @@ def main():
     ap.add_argument("--kv-split", type=int, default=0)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="time the step only (no decode/prefill legs, no other workloads)")
+    ap.add_argument("--only", choices=["step", "decode-rows", "prefill-chunks"], default=None,
+                    help="run just this part of the default workload (for profiler runs): the "
+                         "whole step, or its decode rows or prefill chunks alone")
     ap.add_argument("--separate", action="store_true",
                     help="enqueue the step as three calls (slot mapping, RoPE + write, attention) "
                          "instead of pa_tick_forward")
@@ -318,163 +551,101 @@ def main():
     cfg = WORKLOADS[args.workload]
     log("generating", W.CONFIG_NAMES[cfg])
     t = W.make_config(cfg, poison=False)
+    tick = DeviceTick(t, torch, pa, dev, ROTATE, args.kv_split, args.separate)
 
-    def dev_st(a):
-        if t.dtype == W.F32:
-            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    if args.only in ("decode-rows", "prefill-chunks"):
+        mask = t.query_lens == 1 if args.only == "decode-rows" else t.query_lens > 1
+        sub = tick.sub(mask)
+        ms = timed(torch, sub, args.steps, args.warmup, tick.stream)
+        print(json.dumps({"only": args.only, "workload": t.name, "ms_per_call": round(ms, 5),
+                          "steps": args.steps}), flush=True)
+        return
 
-    def dev_i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
-
-    copies = []
-    for r in range(ROTATE):
-        copies.append({
-            "q": dev_st(t.q), "k": dev_st(t.k), "v": dev_st(t.v),
-            "kp": dev_st(t.k_pool), "vp": dev_st(t.v_pool),
-            "bt": dev_i32(t.block_tables), "sl": dev_i32(t.seq_lens), "qsl": dev_i32(t.qsl),
-            "pos": dev_i32(t.positions), "slots": torch.empty(t.T, dtype=torch.int32, device=dev),
-            "out": torch.empty((t.T, t.Hq, t.D), dtype=torch.bfloat16 if t.dtype == W.BF16
-                               else torch.float32, device=dev),
-        })
-    table = pa.pa_rope_cos_sin_table(t.max_pos, t.D, t.theta, device=dev)
-    dt = pa.PA_BF16 if t.dtype == W.BF16 else pa.PA_F32
-    ws_bytes = pa.pa_paged_attention_workspace_size(t.S, t.T, t.Hq, t.D, t.max_query_len,
-                                                    t.max_seq_len, t.P, args.kv_split, dt)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        c = copies[i % ROTATE]
-        if not args.separate:
-            pa.pa_tick_forward(c["q"], c["k"], c["v"], c["pos"], c["bt"], c["sl"], c["qsl"], table,
-                               c["kp"], c["vp"], t.max_query_len, t.max_seq_len, scale=t.scale,
-                               kv_split_tokens=args.kv_split, out=c["out"],
-                               slot_mapping=c["slots"], workspace=ws, stream=stream)
-            return
-        pa.pa_compute_slot_mapping(c["bt"], c["qsl"], c["pos"], t.P, t.num_pages, out=c["slots"],
-                                   stream=stream)
-        pa.pa_rope_and_cache_write(c["q"], c["k"], c["v"], c["pos"], c["slots"], table, c["kp"],
-                                   c["vp"], stream=stream)
-        pa.pa_paged_attention_varlen(c["q"], c["kp"], c["vp"], c["bt"], c["sl"], c["qsl"],
-                                     t.max_query_len, t.max_seq_len, scale=t.scale,
-                                     kv_split_tokens=args.kv_split, out=c["out"], workspace=ws,
-                                     stream=stream)
-
-    log("warmup", args.warmup)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    log("timed", args.steps, "steps")
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-
-    # second pass with per-kernel events (recorded by the library on its stream)
+    log("warmup", args.warmup, "+ timed", args.steps, "steps (cold: 3 rotated copies)")
+    walls = []
+    ms_per_step = timed(torch, tick.step, args.steps, args.warmup, tick.stream, walls)
+    wall = walls[0]
+    if args.only == "step":
+        print(json.dumps({"only": "step", "workload": t.name, "ms_per_step": round(ms_per_step, 5),
+                          "steps": args.steps}), flush=True)
+        return
     log("per-kernel timing pass")
-    pa.pa_profile_start(16 * args.steps + 16)
-    for i in range(args.steps):
-        step(i)
-    recs = pa.pa_profile_stop()
-    pa.pa_profile_reset()
-    per = {}
-    for name, ms in recs:
-        per.setdefault(name, []).append(ms)
-    kernels = {n: {"avg_ms": float(np.mean(v)), "launches": len(v)} for n, v in per.items()}
+    kernels = profiled(pa, torch, tick.step, args.steps)
+    log("warm pass (one copy)")
+    warm_ms = timed(torch, lambda i: tick.step(0), args.steps, args.warmup, tick.stream)
 
-    work = algorithmic_work(t)
+    dec = decode_work(t)
+    flops = prefill_work(t)
     tokens_per_s = t.T / (ms_per_step / 1e3)
-    attn_names = ("tick_attention", "decode_attention", "prefill_attention_mfma")
-    dominant = max((n for n in kernels if n in attn_names), key=lambda n: kernels[n]["avg_ms"],
-                   default=None)
+    dom = dominant(kernels)
     roof = None
-    extra = {}
-    if dominant is not None:
-        dms = kernels[dominant]["avg_ms"]
-        if dominant == "prefill_attention_mfma":
-            tf = work["prefill_flops"] / (dms / 1e3) / 1e12
-            roof = {"bound": "mfma", "kernel": dominant, "achieved": round(tf, 1),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "flops_per_launch": work["prefill_flops"]}
-        else:
-            # decode rows (and, in the fused tick, the prefill chunks' K/V, Q
-            # and output) are one HBM stream; the chunks' flops would take
-            # prefill_flops / MFMA peak, far below bytes / HBM peak here
-            nbytes = work["decode_bytes"] + (work["prefill_bytes"] if dominant == "tick_attention"
-                                             else 0)
-            gbps = nbytes / (dms / 1e3) / 1e9
-            roof = {"bound": "hbm", "kernel": dominant, "achieved": round(gbps, 1),
+    if dom is not None:
+        dms = kernels[dom]["median_ms"]
+        if dec["rows"]:
+            gbps = dec["bytes"] / (dms / 1e3) / 1e9
+            roof = {"bound": "hbm", "kernel": dom, "achieved": round(gbps, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                    "bytes_per_launch": nbytes}
-            if dominant == "tick_attention" and work["prefill_flops"]:
-                t_roof = max(nbytes / (HBM_PEAK_GBPS * 1e9),
-                             work["prefill_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-                roof["flops_per_launch"] = work["prefill_flops"]
-                roof["time_bound_frac"] = round(t_roof / (dms / 1e3), 4)
-        roof["traffic"] = committed_traffic(dominant, t.name)
-    attn_ms = sum(v["avg_ms"] for n, v in kernels.items() if n not in
-                  ("slot_mapping", "rope_cache_write"))
-    extra["attention_only_tokens_per_s"] = round(t.T / (attn_ms / 1e3), 1) if attn_ms else None
-
-    # the same tick's decode rows alone and prefill chunks alone, attention only
-    # (their K/V are in the pools since the steps above)
-    legs = {}
-    ql = t.query_lens
-    for leg, mask in (("decode_rows_only", ql == 1), ("prefill_chunks_only", ql > 1)):
-        if not mask.any() or mask.all():
-            continue
-        subs = [sub_tick(t, c, mask, dev) for c in copies]
-        sw = torch.empty(max(pa.pa_paged_attention_workspace_size(
-            subs[0]["S"], subs[0]["T"], t.Hq, t.D, subs[0]["mql"], subs[0]["msl"], t.P,
-            args.kv_split, dt), 1), dtype=torch.uint8, device=dev)
-
-        def sub_step(i, subs=subs, sw=sw):
-            c, u = copies[i % ROTATE], subs[i % ROTATE]
-            pa.pa_paged_attention_varlen(u["q"], c["kp"], c["vp"], u["bt"], u["sl"], u["qsl"],
-                                         u["mql"], u["msl"], scale=t.scale,
-                                         kv_split_tokens=args.kv_split, out=u["out"],
-                                         workspace=sw, stream=stream)
-
-        for i in range(args.warmup):
-            sub_step(i)
-        torch.cuda.synchronize()
-        pa.pa_profile_start(16 * args.steps + 16)
-        for i in range(args.steps):
-            sub_step(i)
-        rec = pa.pa_profile_stop()
-        pa.pa_profile_reset()
-        ks = {}
-        for name, ms in rec:
-            ks.setdefault(name, []).append(ms)
-        ks = {n: float(np.mean(v)) for n, v in ks.items()}
-        main_k = max((n for n in ks if n in attn_names), key=lambda n: ks[n])
-        entry = {"kernel": main_k, "avg_ms": round(ks[main_k], 5),
-                 "all_kernels_ms": {n: round(v, 5) for n, v in ks.items()}}
-        if leg == "decode_rows_only":
-            gbps = work["decode_bytes"] / (ks[main_k] / 1e3) / 1e9
-            entry.update({"bound": "hbm", "bytes_per_launch": work["decode_bytes"],
-                          "achieved_gbps": round(gbps, 1),
-                          "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                          "kv_read_gbps": round(work["decode_kv_bytes"] / (ks[main_k] / 1e3) / 1e9,
-                                                1)})
+                    "bytes_per_launch": dec["bytes"], "duration_ms": dms,
+                    "note": "decode rows' algorithmic bytes (unique pages) over the fused "
+                            "kernel's median duration; its prefill flops are scored on the "
+                            "prefill leg"}
+            if flops:
+                t_hbm = dec["bytes"] / (HBM_PEAK_GBPS * 1e9)
+                t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                roof["flops_per_launch"] = flops
+                # the kernel's floor if its HBM stream and its MFMA work never
+                # overlapped (sum) or overlapped perfectly (max), over its duration
+                roof["sum_bound_frac"] = round((t_hbm + t_mfma) / (dms / 1e3), 4)
+                roof["max_bound_frac"] = round(max(t_hbm, t_mfma) / (dms / 1e3), 4)
         else:
-            tf = work["prefill_flops"] / (ks[main_k] / 1e3) / 1e12
-            entry.update({"bound": "mfma", "flops_per_launch": work["prefill_flops"],
-                          "achieved_tflops": round(tf, 1),
-                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
-        legs[leg] = entry
-    if legs:
-        extra["legs"] = legs
+            tf = flops / (dms / 1e3) / 1e12
+            roof = {"bound": "mfma", "kernel": dom, "achieved": round(tf, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                    "duration_ms": dms}
+        roof["traffic"] = committed_traffic(dom, t.name)
+    attn_ms = sum(v["median_ms"] for n, v in kernels.items() if n not in
+                  ("slot_mapping", "rope_cache_write"))
+    extra = {"attention_only_tokens_per_s": round(t.T / (attn_ms / 1e3), 1) if attn_ms else None,
+             "warm_ms_per_step": round(warm_ms, 5),
+             "warm_tokens_per_s": round(t.T / (warm_ms / 1e3), 1),
+             "k1_bytes_per_step": k1_bytes(t)}
+
+    legs = {}
+    if not args.no_legs:
+        ql = t.query_lens
+        for leg, mask in (("decode_rows_only", ql == 1), ("prefill_chunks_only", ql > 1)):
+            if not mask.any() or mask.all():
+                continue
+            log("leg", leg)
+            sub = tick.sub(mask)
+            timed(torch, sub, args.steps, args.warmup, tick.stream)
+            ks = profiled(pa, torch, sub, args.steps)
+            k = dominant(ks)
+            if leg == "decode_rows_only":
+                legs[leg] = hbm_entry(k, ks, dec["bytes"], {"all_kernels": ks})
+            else:
+                tf = flops / (ks[k]["median_ms"] / 1e3) / 1e12
+                legs[leg] = {"kernel": k, "bound": "mfma", "flops_per_launch": flops,
+                             "achieved_tflops": round(tf, 1),
+                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), **ks[k],
+                             "all_kernels": ks}
+        if cfg == 4:
+            for name, c in (("cfg3_decode", 3), ("cfg5_decode", 5)):
+                log("leg", name)
+                legs[name] = decode_config_leg(c, pa, torch, W, dev, args.steps, args.warmup,
+                                               args.kv_split)
+        if legs:
+            extra["legs"] = legs
+        log("practical peak (read-only stream)")
+        extra["practical_peak"] = practical_peak(pa, torch, dev, max(10, args.steps // 2))
+        pp = extra["practical_peak"]["read_only_gbps"]
+        for v in list(legs.values()) + ([roof] if roof and roof["bound"] == "hbm" else []):
+            g = v.get("achieved_gbps", v.get("achieved")) if v else None
+            if g and v.get("bound") == "hbm":
+                v["frac_of_practical_peak"] = round(g / pp, 4)
+    extra["peaks"] = {"hbm_gbps": HBM_PEAK_GBPS, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFLOPS,
+                      "source": "MI355X vendor figures", "rocminfo": rocminfo_peaks()}
 
     cpu = None
     if not args.no_cpu:

@@ -17,10 +17,11 @@
  * - Return value: PA_OK, or an error code. A PA_ERR_INVALID_ARG or
  *   PA_ERR_UNSUPPORTED return enqueues nothing. Nothing aborts, throws or
  *   prints. PA_ERR_HIP means a HIP launch failed after checks passed.
- * - Device metadata (page tables, lengths, slots) is NOT read by the host.
- *   Out-of-range values there cannot make a kernel read or write outside the
- *   buffers described here (indices are clamped or the row is skipped), but
- *   the results for such rows are unspecified.
+ * - Device metadata (page tables, lengths, slots) is NOT read by the host,
+ *   unless validation is on (pa_set_validation). Out-of-range values there
+ *   cannot make a kernel read or write outside the buffers described here
+ *   (indices are clamped or the row is skipped), but the results for such
+ *   rows are unspecified.
  * - Layouts are dense row-major, innermost dimension last:
  *     q, out   [T, Hq, D]             new query rows of the tick, packed
  *     k, v     [T, Hkv, D]            new key/value rows of the tick, packed
@@ -61,6 +62,42 @@ int32_t pa_abi_version(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pa_status_string(pa_status_t status);
+
+/*
+ * pa_set_validation -- opt-in checking of the device metadata, process-wide
+ * (off by default; on = any nonzero value). A failing request is reported by
+ * name, the way the pages' engines report a failed request with its id
+ * (Helios README, "Diagnostics and logs").
+ *
+ * While on, pa_compute_slot_mapping, pa_rope_and_cache_write,
+ * pa_paged_attention_varlen and pa_tick_forward first synchronise `stream`
+ * and copy their metadata to the host (query_start_loc, seq_lens, the
+ * block tables, positions or slot_mapping: a few KB per call, and the
+ * copy waits for the work already queued on the stream), then check every
+ * precondition the kernels otherwise take on trust, and return
+ * PA_ERR_INVALID_ARG with nothing enqueued if one fails:
+ *   - query_start_loc starts at 0, never decreases and ends at T;
+ *   - for every sequence with rows: L <= seq_len <= max_seq_len,
+ *     L <= max_query_len, ceil(seq_len / P) <= max_blocks_per_seq, and those
+ *     first block-table entries are page ids in [0, num_pages);
+ *   - pa_tick_forward: row i of a sequence with L rows and n keys is at
+ *     position n - L + i (this tick's tokens are the sequence's last keys),
+ *     inside the cos/sin table when one is given, and the page it is written
+ *     to is used by no other sequence of the tick (shared pages are full and
+ *     read-only: Helios blog, "Prefix caching");
+ *   - pa_rope_and_cache_write: no two rows write the same pool slot.
+ * Validation copies and checks on the host; the calls are otherwise unchanged
+ * (same kernels, same results). Not meant for the timed serving loop.
+ */
+void pa_set_validation(int32_t on);
+
+/*
+ * pa_validation_message -- why the last call on the calling thread failed
+ * validation, naming the sequence, row or token ("" when the last checked
+ * call passed or validation is off). Points to thread-local storage that the
+ * next call on the same thread overwrites.
+ */
+const char* pa_validation_message(void);
 
 /*
  * pa_rope_cos_sin_table -- build the cached cos/sin table for RoPE
@@ -221,6 +258,20 @@ pa_status_t pa_profile_start(int32_t capacity);
 pa_status_t pa_profile_stop(int32_t* num_records);
 pa_status_t pa_profile_get(int32_t index, char* name, int32_t name_len, float* milliseconds);
 pa_status_t pa_profile_reset(void);
+
+/*
+ * Measurement helpers (not part of a tick).
+ *
+ * pa_probe_stream_read -- read `bytes` of device memory at `buf` once, as a
+ * plain stream of 16-byte loads over the whole GPU, and write one 32-bit word
+ * per thread to `sink` (pa_probe_sink_words() words of device memory): the
+ * practical read bandwidth of this GPU, against which the HBM-bound kernels'
+ * achieved bandwidth is read. bytes > 0 and a multiple of 16, buf 16-byte
+ * aligned, sink 4-byte aligned, else PA_ERR_INVALID_ARG. Asynchronous on
+ * `stream`; recorded by the profile hook under "stream_read".
+ */
+size_t pa_probe_sink_words(void);
+pa_status_t pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

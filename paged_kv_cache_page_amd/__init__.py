@@ -20,7 +20,8 @@ __all__ = [
     "pa_abi_version", "pa_status_string", "pa_rope_cos_sin_table", "pa_compute_slot_mapping",
     "pa_rope_and_cache_write", "pa_paged_attention_workspace_size", "pa_paged_attention_varlen",
     "pa_tick_forward", "pa_profile_start", "pa_profile_stop", "pa_profile_reset",
-    "BlockManager", "PA_ERR_NO_PAGES", "pa_sample_tokens",
+    "BlockManager", "PA_ERR_NO_PAGES", "pa_sample_tokens", "pa_set_validation",
+    "pa_validation_message", "pa_probe_stream_read",
 ]
 
 PA_F32 = 0
@@ -64,13 +65,19 @@ SIGNATURES = {
     "pa_profile_stop": (_i32, [ctypes.POINTER(_i32)]),
     "pa_profile_get": (_i32, [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(_f32)]),
     "pa_profile_reset": (_i32, []),
+    "pa_set_validation": (None, [_i32]),
+    "pa_probe_sink_words": (_sz, []),
+    "pa_probe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "pa_validation_message": (ctypes.c_char_p, []),
 }
 
 
 class PaError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {pa_status_string(status)} (status {status})")
+        detail = pa_validation_message() if status == 1 else ""
+        super().__init__(f"{where}: {pa_status_string(status)} (status {status})"
+                         + (f": {detail}" if detail else ""))
 
 
 def lib():
@@ -143,12 +150,24 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A new tensor owned by the stream the kernels run on: the caching
+    allocator then hands its bytes to no other stream until that stream's work
+    on them is done (allocated on another stream, the bytes could be reused
+    while the library's kernels still read or write them)."""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 # ---------------------------------------------------------------- entry points
 def pa_rope_cos_sin_table(max_pos, head_dim, theta, device="cuda", out=None, stream=None):
     """float32 ``[max_pos, head_dim]`` cos/sin table built on the GPU."""
     torch = _torch()
     if out is None:
-        out = torch.empty((max_pos, head_dim), dtype=torch.float32, device=device)
+        out = _empty((max_pos, head_dim), torch.float32, device, stream)
     _dev(out, "out", torch.float32, 2)
     _check(lib().pa_rope_cos_sin_table(_ptr(out), int(max_pos), int(head_dim), float(theta),
                                        _stream(stream)), "pa_rope_cos_sin_table")
@@ -167,7 +186,7 @@ def pa_compute_slot_mapping(block_tables, query_start_loc, positions, page_size,
     if query_start_loc.shape[0] != S + 1:
         raise ValueError("query_start_loc must have S + 1 entries")
     if out is None:
-        out = torch.empty(T, dtype=torch.int32, device=positions.device)
+        out = _empty(T, torch.int32, positions.device, stream)
     _dev(out, "out", torch.int32, 1)
     _check(lib().pa_compute_slot_mapping(_ptr(block_tables), _ptr(query_start_loc),
                                          _ptr(positions), _ptr(out), S, T, max_blocks,
@@ -243,12 +262,12 @@ def pa_paged_attention_varlen(q, k_pool, v_pool, block_tables, seq_lens, query_s
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(tuple(q.shape), q.dtype, q.device, stream)
     _dev(out, "out", q.dtype, 3)
     need = pa_paged_attention_workspace_size(S, T, Hq, D, int(max_query_len), int(max_seq_len),
                                              P, int(kv_split_tokens), dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace")
@@ -303,17 +322,17 @@ def pa_tick_forward(q, k, v, positions, block_tables, seq_lens, query_start_loc,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(tuple(q.shape), q.dtype, q.device, stream)
     _dev(out, "out", q.dtype, 3)
     if slot_mapping is None:
-        slot_mapping = torch.empty(T, dtype=torch.int32, device=q.device)
+        slot_mapping = _empty(T, torch.int32, q.device, stream)
     _dev(slot_mapping, "slot_mapping", torch.int32, 1)
     if slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping needs one entry per token")
     need = pa_paged_attention_workspace_size(S, T, Hq, D, int(max_query_len), int(max_seq_len),
                                              P, int(kv_split_tokens), dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace")
@@ -325,6 +344,32 @@ def pa_tick_forward(q, k, v, positions, block_tables, seq_lens, query_start_loc,
         int(max_seq_len), max_pos, float(scale), int(kv_split_tokens), dt, _ptr(workspace),
         ws_bytes, _stream(stream)), "pa_tick_forward")
     return out
+
+
+def pa_set_validation(on):
+    """Turn the library's opt-in metadata validation on or off (process-wide).
+    While on, the attention and tick calls copy their device metadata to the
+    host (synchronising the stream) and reject inconsistent metadata with
+    PA_ERR_INVALID_ARG before anything is enqueued; the raised PaError then
+    names the offending sequence or token."""
+    lib().pa_set_validation(1 if on else 0)
+
+
+def pa_validation_message():
+    """Why the last call on this thread failed validation ('' if it did not)."""
+    return lib().pa_validation_message().decode()
+
+
+def pa_probe_stream_read(buf, sink=None, stream=None):
+    """Read the GPU tensor ``buf`` once as a plain 16-byte-load stream (a
+    measurement of the practical read bandwidth). Returns the sink tensor."""
+    torch = _torch()
+    _dev(buf, "buf")
+    if sink is None:
+        sink = _empty(int(lib().pa_probe_sink_words()), torch.int32, buf.device, stream)
+    _check(lib().pa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                      _stream(stream)), "pa_probe_stream_read")
+    return sink
 
 
 def pa_profile_start(capacity=4096):
@@ -365,13 +410,13 @@ def pa_sample_tokens(logits, temperature, top_k, top_p, uniforms, out=None, work
         if t.shape[0] != R or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [{R}]")
     if out is None:
-        out = torch.empty(R, dtype=torch.int32, device=logits.device)
+        out = _empty(R, torch.int32, logits.device, stream)
     _dev(out, "out", torch.int32, 1)
     if out.shape[0] != R:
         raise ValueError("out must be [rows]")
     need = int(lib().pa_sample_workspace_size(R, V))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=logits.device)
+        workspace = _empty(max(need, 1), torch.uint8, logits.device, stream)
     _dev(workspace, "workspace", torch.uint8, 1)
     _check(lib().pa_sample_tokens(_ptr(logits), logits.stride(0), R, V, _ptr(temperature),
                                   _ptr(top_k), _ptr(top_p), _ptr(uniforms), _ptr(out),

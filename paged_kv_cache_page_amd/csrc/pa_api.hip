@@ -2,13 +2,18 @@
 // sizing, launch dispatch, and the optional kernel-timing hook.
 //
 // No entry point reads device memory from the host, allocates, frees or
-// synchronises (the profiling calls aside). Every check happens before the
-// first HIP call, so argument errors are reported without touching a GPU.
+// synchronises (the profiling calls and the opt-in validation mode aside).
+// Every host-scalar check happens before the first HIP call, so argument
+// errors are reported without touching a GPU.
 #include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "pa_device.h"
@@ -205,6 +210,125 @@ size_t workspace_bytes_for(int S, int T, int Hq, int D, int max_query_len, int m
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// ------------------------------------------------------- validation -----
+// Opt-in checks of the device metadata (pa_set_validation): the metadata is
+// copied to the host on the call's stream (which is synchronised first, so the
+// values checked are the ones the kernels would read) and every precondition
+// the kernels otherwise take on trust is tested before anything is enqueued.
+// A failure returns PA_ERR_INVALID_ARG and leaves its reason, naming the
+// sequence or token, in a per-thread message (the pages' engines report a
+// failing request by name: Helios README, "Diagnostics and logs").
+std::atomic<int> g_validate{0};
+thread_local char g_vmsg[256] = "";
+
+pa_status_t vfail(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_vmsg, sizeof g_vmsg, fmt, ap);
+  va_end(ap);
+  return PA_ERR_INVALID_ARG;
+}
+
+bool validating() { return g_validate.load(std::memory_order_relaxed) != 0; }
+
+template <typename T>
+pa_status_t fetch(std::vector<T>& h, const T* d, size_t n, hipStream_t s) {
+  h.resize(n);
+  if (n == 0) return PA_OK;
+  return from_hip(hipMemcpyAsync(h.data(), d, n * sizeof(T), hipMemcpyDeviceToHost, s));
+}
+
+// The sequences' metadata on the host.
+struct HostMeta {
+  std::vector<int32_t> qsl, seq_lens, bt, pos, slots;
+};
+
+// query_start_loc of S sequences over T rows: starts at 0, never decreases,
+// ends at T.
+pa_status_t check_qsl(const HostMeta& m, int S, int T) {
+  if (m.qsl[0] != 0) return vfail("query_start_loc[0] = %d, not 0", m.qsl[0]);
+  for (int s = 0; s < S; ++s)
+    if (m.qsl[s + 1] < m.qsl[s])
+      return vfail("query_start_loc decreases at sequence %d (%d -> %d)", s, m.qsl[s],
+                   m.qsl[s + 1]);
+  if (m.qsl[S] != T) return vfail("query_start_loc[S] = %d, not T = %d", m.qsl[S], T);
+  return PA_OK;
+}
+
+// Every sequence with rows: L <= n <= max_seq_len, L <= max_query_len, and the
+// first ceil(n / P) entries of its page-table row valid page ids.
+pa_status_t check_seqs(const HostMeta& m, int S, int P, int num_pages, int max_blocks,
+                       int max_query_len, int max_seq_len) {
+  for (int s = 0; s < S; ++s) {
+    const int L = m.qsl[s + 1] - m.qsl[s], n = m.seq_lens[s];
+    if (n < 0) return vfail("sequence %d: seq_len %d < 0", s, n);
+    if (L == 0) continue;
+    if (L > n) return vfail("sequence %d: %d query rows > seq_len %d", s, L, n);
+    if (n > max_seq_len) return vfail("sequence %d: seq_len %d > max_seq_len %d", s, n, max_seq_len);
+    if (L > max_query_len)
+      return vfail("sequence %d: %d query rows > max_query_len %d", s, L, max_query_len);
+    const long pages = ((long)n + P - 1) / P;
+    if (pages > max_blocks)
+      return vfail("sequence %d: seq_len %d needs %ld pages > max_blocks_per_seq %d", s, n, pages,
+                   max_blocks);
+    for (long j = 0; j < pages; ++j) {
+      const int pg = m.bt[(size_t)s * max_blocks + j];
+      if (pg < 0 || pg >= num_pages)
+        return vfail("sequence %d: block_tables[%d][%ld] = %d outside [0, %d)", s, s, j, pg,
+                     num_pages);
+    }
+  }
+  return PA_OK;
+}
+
+// The rows of a tick: row i of sequence s (L rows, n keys) is the token at
+// position n - L + i, its slot is a pool slot, and the page it is written to
+// belongs to no other sequence (pages shared between sequences are full and
+// read-only: Helios blog, "Prefix caching").
+pa_status_t check_tick_rows(const HostMeta& m, int S, int P, int max_blocks, int max_pos,
+                            bool rope) {
+  std::unordered_map<int, int> owner;  // page -> the one sequence that uses it, or -1
+  for (int s = 0; s < S; ++s) {
+    if (m.qsl[s + 1] == m.qsl[s]) continue;
+    const long pages = ((long)m.seq_lens[s] + P - 1) / P;
+    for (long j = 0; j < pages; ++j) {
+      const int pg = m.bt[(size_t)s * max_blocks + j];
+      auto it = owner.find(pg);
+      if (it == owner.end()) owner[pg] = s;
+      else if (it->second != s) it->second = -1;
+    }
+  }
+  for (int s = 0; s < S; ++s) {
+    const int q0 = m.qsl[s], L = m.qsl[s + 1] - q0, n = m.seq_lens[s];
+    for (int i = 0; i < L; ++i) {
+      const int t = q0 + i, p = m.pos[t];
+      if (p != n - L + i)
+        return vfail("token %d (sequence %d, row %d of %d): position %d, not seq_len - L + row "
+                     "= %d", t, s, i, L, p, n - L + i);
+      if (rope && p >= max_pos)
+        return vfail("token %d (sequence %d): position %d outside the cos/sin table (%d rows)",
+                     t, s, p, max_pos);
+      const int pg = m.bt[(size_t)s * max_blocks + p / P];
+      if (owner[pg] != s)
+        return vfail("token %d (sequence %d): writes page %d, which another sequence also uses",
+                     t, s, pg);
+    }
+  }
+  return PA_OK;
+}
+
+// No two rows write the same pool slot.
+pa_status_t check_slots_unique(const std::vector<int32_t>& slots, long pool_slots) {
+  std::unordered_map<int, int> seen;
+  for (size_t t = 0; t < slots.size(); ++t) {
+    const int sl = slots[t];
+    if (sl < 0 || sl >= pool_slots) continue;  // skipped rows
+    auto r = seen.emplace(sl, (int)t);
+    if (!r.second) return vfail("tokens %d and %zu write the same slot %d", r.first->second, t, sl);
+  }
+  return PA_OK;
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -213,7 +337,11 @@ using namespace pa;
 #pragma GCC visibility push(default)
 extern "C" {
 
-int32_t pa_abi_version(void) { return 4; }
+int32_t pa_abi_version(void) { return 5; }
+
+void pa_set_validation(int32_t on) { g_validate.store(on ? 1 : 0, std::memory_order_relaxed); }
+
+const char* pa_validation_message(void) { return g_vmsg; }
 
 const char* pa_status_string(pa_status_t status) {
   switch (status) {
@@ -277,6 +405,16 @@ pa_status_t pa_compute_slot_mapping(const int32_t* block_tables, const int32_t* 
                                             slot_mapping, S, T, max_blocks_per_seq, page_size,
                                             num_pages);
   if (st != PA_OK) return st;
+  g_vmsg[0] = '\0';
+  if (validating() && T > 0) {
+    HostMeta m;
+    const hipStream_t hs = (hipStream_t)stream;
+    if (fetch(m.qsl, query_start_loc, (size_t)S + 1, hs) != PA_OK ||
+        hipStreamSynchronize(hs) != hipSuccess)
+      return PA_ERR_HIP;
+    const pa_status_t vs = check_qsl(m, S, T);
+    if (vs != PA_OK) return vs;
+  }
   return from_hip(launch_slot_mapping(block_tables, query_start_loc, positions, slot_mapping, S,
                                       T, max_blocks_per_seq, page_size, num_pages,
                                       (hipStream_t)stream));
@@ -291,6 +429,16 @@ pa_status_t pa_rope_and_cache_write(void* q, void* k, const void* v, const int32
   const pa_status_t st = rope_check(q, k, v, positions, slot_mapping, cos_sin, k_pool, v_pool, T,
                                     Hq, Hkv, head_dim, page_size, num_pages, max_pos, dtype);
   if (st != PA_OK || T == 0) return st;
+  g_vmsg[0] = '\0';
+  if (validating()) {
+    HostMeta m;
+    const hipStream_t hs = (hipStream_t)stream;
+    if (fetch(m.slots, slot_mapping, (size_t)T, hs) != PA_OK ||
+        hipStreamSynchronize(hs) != hipSuccess)
+      return PA_ERR_HIP;
+    const pa_status_t vs = check_slots_unique(m.slots, (long)num_pages * page_size);
+    if (vs != PA_OK) return vs;
+  }
   return from_hip(launch_rope_cache_write(dtype, q, k, v, positions, slot_mapping, cos_sin,
                                           k_pool, v_pool, T, Hq, Hkv, head_dim, page_size,
                                           num_pages, max_pos, (hipStream_t)stream));
@@ -438,6 +586,27 @@ pa_status_t attention_run(const AttnCall& c, hipStream_t s) {
   return PA_OK;
 }
 
+// Validation of an attention call's metadata (and, for a tick, of its rows'
+// positions and pages); PA_OK when validation is off.
+pa_status_t validate_call(const int32_t* block_tables, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, const int32_t* positions, int S, int T,
+                          int P, int num_pages, int max_blocks, int max_query_len,
+                          int max_seq_len, int max_pos, bool rope, hipStream_t s) {
+  g_vmsg[0] = '\0';
+  if (!validating() || S == 0 || T == 0) return PA_OK;
+  HostMeta m;
+  if (fetch(m.qsl, query_start_loc, (size_t)S + 1, s) != PA_OK ||
+      fetch(m.seq_lens, seq_lens, (size_t)S, s) != PA_OK ||
+      fetch(m.bt, block_tables, (size_t)S * max_blocks, s) != PA_OK ||
+      (positions && fetch(m.pos, positions, (size_t)T, s) != PA_OK) ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return PA_ERR_HIP;
+  pa_status_t st = check_qsl(m, S, T);
+  if (st == PA_OK) st = check_seqs(m, S, P, num_pages, max_blocks, max_query_len, max_seq_len);
+  if (st == PA_OK && positions) st = check_tick_rows(m, S, P, max_blocks, max_pos, rope);
+  return st;
+}
+
 }  // namespace
 
 pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const void* v_pool,
@@ -456,6 +625,9 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
                                    kv_split_tokens, dtype, workspace, workspace_bytes, c);
   if (st != PA_OK || c.empty) return st;
   const hipStream_t s = (hipStream_t)stream;
+  st = validate_call(block_tables, seq_lens, query_start_loc, nullptr, S, T, page_size,
+                     num_pages, max_blocks_per_seq, max_query_len, max_seq_len, 0, false, s);
+  if (st != PA_OK) return st;
   st = attention_plan(c, s);
   return st != PA_OK ? st : attention_run(c, s);
 }
@@ -482,6 +654,10 @@ pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* posi
                        Hkv, head_dim, page_size, num_pages, max_blocks_per_seq, max_query_len,
                        max_seq_len, scale, kv_split_tokens, dtype, workspace, workspace_bytes, c);
   if (st != PA_OK || T == 0) return st;
+  st = validate_call(block_tables, seq_lens, query_start_loc, positions, S, T, page_size,
+                     num_pages, max_blocks_per_seq, max_query_len, max_seq_len, max_pos,
+                     cos_sin != nullptr, (hipStream_t)stream);
+  if (st != PA_OK) return st;
 
   // One launch for the slot mapping, the page write and (seq mode) the plan,
   // which reads only query_start_loc and seq_lens; then the attention kernels.

@@ -7,6 +7,7 @@ import sys
 import numpy as np
 import torch
 
+import oracle
 import paged_kv_cache_page_amd as pa
 from paged_kv_cache_page_amd import workloads as W
 
@@ -67,11 +68,22 @@ class DevTick:
         self.table = None
         self.slots = None
 
+    def oracle_table(self):
+        """The oracle's cos/sin table on the device (None without RoPE): the
+        call input both sides share, so that the rotated q/k and the stored K
+        can be compared bit for bit. The library's own table builder is
+        checked against this table separately."""
+        t = self.t
+        if t.theta is None:
+            return None
+        return torch.from_numpy(oracle.rope_table(t.max_pos, t.D, t.theta)).to(DEV)
+
     def write(self):
-        """Table (if RoPE), slot mapping, RoPE + page write. Returns self."""
+        """Table (the oracle's, if RoPE), slot mapping, RoPE + page write.
+        Returns self."""
         t = self.t
         if t.theta is not None:
-            self.table = pa.pa_rope_cos_sin_table(t.max_pos, t.D, t.theta, device=DEV)
+            self.table = self.oracle_table()
         self.slots = pa.pa_compute_slot_mapping(self.block_tables, self.qsl, self.positions,
                                                 t.P, t.num_pages)
         if not t.new_in_pool:
@@ -95,16 +107,37 @@ def run_gpu_tick(tick, kv_split_tokens=0):
     return d, out
 
 
+def fp32_errors(g, ref):
+    """Relative errors of a float32 output against the float64 oracle:
+    norm-wise (max |g - o| / max |o| over the config), per output row (the
+    same ratio within each (token, head) row of D values, worst row), and
+    elementwise where |o| > 1e-3."""
+    err = np.abs(g - ref)
+    rel = err.max() / max(np.abs(ref).max(), 1e-30)
+    row_scale = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    row = (err.max(axis=-1) / row_scale).max()
+    big = np.abs(ref) > 1e-3
+    elem = (err[big] / np.abs(ref[big])).max() if big.any() else 0.0
+    return float(rel), float(row), float(elem)
+
+
 def check_attention(got, ref, dtype, where=""):
-    """got: GPU output tensor; ref: float64 oracle output. Returns error stats."""
+    """got: GPU output tensor; ref: float64 oracle output. Returns error stats.
+
+    float32: the norm-wise and the per-row relative error must each be at
+    most 1e-5; the elementwise relative error where |o| > 1e-3 is reported
+    (it grows without bound as |o| nears 0, whatever the arithmetic)."""
     g = host_f32(got).astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.isfinite(g).all(), f"{where}: non-finite GPU output"
     err = np.abs(g - ref)
     if dtype == W.F32:
-        rel = err.max() / max(np.abs(ref).max(), 1e-30)
+        rel, row, elem = fp32_errors(g, ref)
+        say(f"{where}: fp32 relative error norm-wise {rel:.3e}, worst row {row:.3e}, "
+            f"elementwise (|o| > 1e-3) {elem:.3e}")
         assert rel <= F32_REL, f"{where}: fp32 norm-wise relative error {rel:.3e} > {F32_REL}"
-        return {"rel": float(rel)}
+        assert row <= F32_REL, f"{where}: fp32 per-row relative error {row:.3e} > {F32_REL}"
+        return {"rel": rel, "row_rel": row, "elem_rel": elem}
     mx, mean = float(err.max()), float(err.mean())
     assert mx <= BF16_MAX_ABS, f"{where}: bf16 max abs error {mx:.4e} > {BF16_MAX_ABS}"
     assert mean <= BF16_MEAN_ABS, f"{where}: bf16 mean abs error {mean:.4e} > {BF16_MEAN_ABS}"

@@ -46,7 +46,7 @@ def test_library_exports_nothing_else():
 
 
 def test_status_strings_and_version():
-    assert pa.pa_abi_version() == 4
+    assert pa.pa_abi_version() == 5
     for code in range(5):
         assert pa.pa_status_string(code).startswith("PA_")
     assert "UNKNOWN" in pa.pa_status_string(99)
@@ -247,3 +247,19 @@ def test_sample_tokens_rejects_bad_scalars_before_any_launch():
     assert f(p, 10, 1, 10, p, p, p, p, p, ctypes.c_void_p(264), ws, None) == INVALID  # misaligned
     assert f(p, 10, 4, 10, p, p, p, p, p, p, ws - 1, None) == WS_SMALL
     assert f(None, 10, 0, 10, None, None, None, None, None, None, 0, None) == OK  # no rows
+
+
+def test_validation_switch_keeps_host_checks_first():
+    # with validation on, bad host scalars are still rejected before any copy
+    # of device metadata (no GPU needed), and an empty tick enqueues nothing
+    assert pa.pa_validation_message() == ""
+    pa.pa_set_validation(True)
+    try:
+        assert attn(Hq=6, Hkv=4) == INVALID
+        assert attn(max_seq_len=4096) == WS_SMALL
+        assert tick(q=None) == INVALID
+        assert attn(T=0) == OK and tick(T=0) == OK
+        assert cache_write(T=0) == OK
+        assert pa.pa_validation_message() == ""
+    finally:
+        pa.pa_set_validation(False)

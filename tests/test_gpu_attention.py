@@ -91,6 +91,45 @@ def test_split_count_invariance(split):
     check_attention(out, oracle_tick(t), t.dtype, f"split{split}")
 
 
+def _one_partition_tick(seed, Hq, Hkv, D, P, chunks):
+    """Decode rows of 241..256 keys: each pads to 256 keys on the decode key
+    axis, so with the automatic split (chunks of at least 256 keys, here
+    exactly 256 since the tick has fewer rows than decode waves per KV head)
+    every row is exactly one chunk, one partition; with chunks, two short
+    prefill chunks (at most 4 key tiles, never cut into pieces) share the
+    tick."""
+    rng = np.random.default_rng(seed)
+    S = 40
+    sl = [int(x) for x in rng.integers(241, 257, size=S)]
+    ql = [1] * S
+    if chunks:
+        sl += [200, 90]
+        ql += [64, 90]
+    return W.build_tick(rng, name="one-partition", dtype=W.BF16, Hq=Hq, Hkv=Hkv, D=D, P=P,
+                        seq_lens=sl, query_lens=ql, theta=1e4, poison=True)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,P,chunks", [(8, 2, 128, 16, False), (32, 8, 128, 256, False),
+                                               (32, 4, 64, 16, True), (8, 8, 128, 256, True)])
+def test_single_partition_rows_equal_the_merge_free_run_bitwise(Hq, Hkv, D, P, chunks):
+    """Split-KV pin: rows that are one partition under the automatic split
+    give the same bits as a run with partitions of 65536 keys, whose every row
+    is one partition and which launches no merge kernel at all."""
+    t = _one_partition_tick(140 + D + Hkv, Hq, Hkv, D, P, chunks)
+    say("one-partition pin", Hq, Hkv, D, P, chunks)
+    d = DevTick(t).write()
+    auto = d.attend(0)
+    torch.cuda.synchronize()
+    pa.pa_profile_start(64)
+    whole = d.attend(65536)
+    rec = pa.pa_profile_stop()
+    pa.pa_profile_reset()
+    names = [n for n, _ in rec]
+    assert not any("reduce" in n for n in names), names
+    assert np.array_equal(_bits(auto), _bits(whole))
+    check_attention(whole, oracle_tick(t), t.dtype, "one-partition")
+
+
 def test_page_permutation_bitwise():
     t = W.make_config(4, poison=True)
     say("page permutation")
@@ -252,7 +291,7 @@ def test_tick_forward_equals_the_three_calls_bitwise(which):
     a = DevTick(t).write()
     ref = a.attend(split)
     b = DevTick(t)
-    table = pa.pa_rope_cos_sin_table(t.max_pos, t.D, t.theta, device=DEV) if t.theta else None
+    table = b.oracle_table()
     slots = torch.full((t.T,), -7, dtype=torch.int32, device=DEV)
     out = pa.pa_tick_forward(b.q, b.k, b.v, b.positions, b.block_tables, b.seq_lens, b.qsl,
                              table, b.k_pool, b.v_pool, t.max_query_len, t.max_seq_len,
@@ -262,6 +301,16 @@ def test_tick_forward_equals_the_three_calls_bitwise(which):
                        ("k", a.k, b.k), ("k_pool", a.k_pool, b.k_pool),
                        ("v_pool", a.v_pool, b.v_pool)):
         assert np.array_equal(_bits(x), _bits(y)), f"{which}: {name} differs"
+    # and the write side equals the oracle's bit for bit (same cos/sin table)
+    res = oracle.run_tick(t.dtype, t.q, t.k, t.v, t.positions, t.block_tables, t.qsl,
+                          t.seq_lens, t.k_pool, t.v_pool,
+                          oracle.rope_table(t.max_pos, t.D, t.theta) if t.theta else None,
+                          t.scale)
+    for name, x in (("slots", slots), ("q", b.q), ("k", b.k), ("k_pool", b.k_pool),
+                    ("v_pool", b.v_pool)):
+        want = res["slots" if name == "slots" else name]
+        got = _bits(x).reshape(want.shape)
+        assert np.array_equal(got, want.view(got.dtype)), f"{which}: {name} != oracle"
     if which.startswith("many"):  # these sizes are not among the parity cases above
         check_attention(out, oracle_tick(t), t.dtype, which)
 
@@ -287,3 +336,28 @@ def test_decode_walk_many_short_rows(D, G, split, chunks):
     say("short rows", D, G, split, chunks)
     _, out = run_gpu_tick(t, kv_split_tokens=split)
     check_attention(out, oracle_tick(t), t.dtype, f"short-rows D{D} G{G} split{split}")
+
+
+def test_side_stream_with_binding_allocated_buffers():
+    """The binding allocates the workspace, out and the slots on the stream the
+    kernels run on: work queued meanwhile on the current stream, allocating
+    and filling fresh memory, cannot take those bytes while the tick runs."""
+    t = W.make_config(4, poison=True)
+    ref_d = DevTick(t).write()
+    ref = ref_d.attend()
+    torch.cuda.synchronize()
+    d = DevTick(t)
+    table = d.oracle_table()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    say("side stream tick")
+    out = pa.pa_tick_forward(d.q, d.k, d.v, d.positions, d.block_tables, d.seq_lens, d.qsl,
+                             table, d.k_pool, d.v_pool, t.max_query_len, t.max_seq_len,
+                             scale=t.scale, stream=side)
+    for _ in range(8):
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device=DEV)
+        junk.fill_(0xFF)
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -130,3 +130,22 @@ def test_each_draw_path(sigma, T, where):
     p = rng.choice([1.0, 0.95, 0.6, 0.2], R).astype(np.float32)
     u = rng.random(R, dtype=np.float32)
     check(logits, Tr, k, p, u, where)
+
+
+def test_long_merged_list_without_slice_overflow():
+    # 8 slices of 3072 tokens; each slice lists about 800 tokens near the row
+    # maximum (below its 1024-token capacity), so no slice overflows, while the
+    # merged list (about 6400 tokens) exceeds the draw kernel's 4096-token LDS
+    # list: the row path, reached without an overflowing slice
+    rng = np.random.default_rng(13)
+    R, V = 12, 24576
+    logits = np.full((R, V), -200.0, np.float32) + rng.standard_normal((R, V)).astype(np.float32)
+    for r in range(R):
+        for sl in range(V // 3072):
+            idx = sl * 3072 + rng.choice(3072, 800, replace=False)
+            logits[r, idx] = rng.standard_normal(800).astype(np.float32)
+    T = np.full(R, 1.0, np.float32)
+    k = rng.choice([0, 0, 5000, 6000, 100], R).astype(np.int32)
+    p = rng.choice([1.0, 0.99, 0.9, 0.5], R).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    check(logits, T, k, p, u, "long merged list")
