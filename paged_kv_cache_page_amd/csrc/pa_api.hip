@@ -179,6 +179,22 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
   w.part_slots = (long)(w.token_mode ? T : S) * w.max_parts;
   if (!w.token_mode) {
     w.cap_dec = (long)S * w.max_parts;
+    if (pt == 0) {
+      // Automatic partitions: the plan cuts the decode key axis (at most S rows
+      // of round_up(max_seq_len, 16) keys) into chunks of at least one decode
+      // wave's share, so there are at most as many chunks as decode waves per
+      // KV head (at most dec_grid * 4 * 8 / Hq: a group has at most 8 heads),
+      // unless the largest partition caps the chunk, and then at most
+      // keys / split_max chunks. A row has one partition per chunk it overlaps,
+      // and the rows and chunks tile the same axis, so the rows' partitions
+      // number at most rows + chunks.
+      const long waves = ((long)decode_grid_max(dt, D) * 4 * 8 + Hq - 1) / Hq;
+      const long keys = (long)S * (((long)max_seq_len + 15) / 16 * 16);
+      const long by_cap = (keys + split_max(P) - 1) / split_max(P);
+      const long chunks = waves > by_cap ? waves : by_cap;
+      if (chunks < w.cap_dec) w.cap_dec = chunks;
+      if ((long)S + chunks < w.part_slots) w.part_slots = (long)S + chunks;
+    }
     if (max_query_len > 1) {
       // a tile holds at least kPrefillRows / 8 tokens (the largest supported group is 8)
       const int tm = kPrefillRows / 8;
@@ -632,15 +648,19 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
   return st != PA_OK ? st : attention_run(c, s);
 }
 
-pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* positions,
-                            const int32_t* block_tables, const int32_t* seq_lens,
-                            const int32_t* query_start_loc, const float* cos_sin, void* k_pool,
-                            void* v_pool, void* out, int32_t* slot_mapping, int32_t S, int32_t T,
-                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                            int32_t num_pages, int32_t max_blocks_per_seq,
-                            int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
-                            float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// pa_tick_forward's checks and, when `enqueue`, its launches.
+pa_status_t tick_forward_impl(void* q, void* k, const void* v, const int32_t* positions,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* query_start_loc, const float* cos_sin, void* k_pool,
+                              void* v_pool, void* out, int32_t* slot_mapping, int32_t S,
+                              int32_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              int32_t page_size, int32_t num_pages, int32_t max_blocks_per_seq,
+                              int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
+                              float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              bool enqueue) {
   // every check of the three calls before anything is enqueued
   if (T > 0 && !q) return PA_ERR_INVALID_ARG;
   pa_status_t st = slot_mapping_check(block_tables, query_start_loc, positions, slot_mapping, S,
@@ -653,7 +673,7 @@ pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* posi
   st = attention_setup(q, k_pool, v_pool, block_tables, seq_lens, query_start_loc, out, S, T, Hq,
                        Hkv, head_dim, page_size, num_pages, max_blocks_per_seq, max_query_len,
                        max_seq_len, scale, kv_split_tokens, dtype, workspace, workspace_bytes, c);
-  if (st != PA_OK || T == 0) return st;
+  if (st != PA_OK || T == 0 || !enqueue) return st;
   st = validate_call(block_tables, seq_lens, query_start_loc, positions, S, T, page_size,
                      num_pages, max_blocks_per_seq, max_query_len, max_seq_len, max_pos,
                      cos_sin != nullptr, (hipStream_t)stream);
@@ -668,6 +688,24 @@ pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* posi
                        c.a.cap_pf, kPrefillRows / c.G, (hipStream_t)stream) != hipSuccess)
     return PA_ERR_HIP;
   return attention_run(c, (hipStream_t)stream);
+}
+
+}  // namespace
+
+pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* positions,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, const float* cos_sin, void* k_pool,
+                            void* v_pool, void* out, int32_t* slot_mapping, int32_t S, int32_t T,
+                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_blocks_per_seq,
+                            int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
+                            float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return tick_forward_impl(q, k, v, positions, block_tables, seq_lens, query_start_loc, cos_sin,
+                           k_pool, v_pool, out, slot_mapping, S, T, Hq, Hkv, head_dim, page_size,
+                           num_pages, max_blocks_per_seq, max_query_len, max_seq_len, max_pos,
+                           scale, kv_split_tokens, dtype, workspace, workspace_bytes, stream,
+                           true);
 }
 
 pa_status_t pa_profile_start(int32_t capacity) {

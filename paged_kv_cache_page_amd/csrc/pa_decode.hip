@@ -484,6 +484,12 @@ int decode_grid(pa_dtype_t dt, int D, int G) {
   return 8;
 }
 
+int decode_grid_max(pa_dtype_t dt, int D) {
+  int g = 8;
+  for (int G = 1; G <= 8; G *= 2) g = max(g, decode_grid(dt, D, G));
+  return g;
+}
+
 hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   if (dt == PA_F32) {

@@ -134,8 +134,10 @@ hipError_t launch_tick_prep(pa_dtype_t dt, void* q, void* k, const void* v, cons
 // (query length 1; other sequences skipped). token_mode = true: one row per
 // query token of every sequence (the VALU path for prefill rows).
 bool decode_supported(pa_dtype_t dt, int D, int G);
-// Workgroups of the persistent decode grid (resident count, a multiple of 8).
+// Workgroups of the persistent decode grid (resident count, a multiple of 8),
+// and the largest of them over the supported groups G.
 int decode_grid(pa_dtype_t dt, int D, int G);
+int decode_grid_max(pa_dtype_t dt, int D);
 hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipStream_t s);
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s);

@@ -111,33 +111,40 @@ def fp32_errors(g, ref):
     """Relative errors of a float32 output against the float64 oracle:
     norm-wise (max |g - o| / max |o| over the config), per output row (the
     same ratio within each (token, head) row of D values, worst row), and
-    elementwise where |o| > 1e-3."""
+    elementwise where |o| > 1e-3 and where |o| >= 0.1."""
     err = np.abs(g - ref)
     rel = err.max() / max(np.abs(ref).max(), 1e-30)
     row_scale = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
     row = (err.max(axis=-1) / row_scale).max()
-    big = np.abs(ref) > 1e-3
-    elem = (err[big] / np.abs(ref[big])).max() if big.any() else 0.0
-    return float(rel), float(row), float(elem)
+
+    def elem_where(mask):
+        return float((err[mask] / np.abs(ref[mask])).max()) if mask.any() else 0.0
+    return (float(rel), float(row), elem_where(np.abs(ref) > 1e-3),
+            elem_where(np.abs(ref) >= 0.1))
 
 
 def check_attention(got, ref, dtype, where=""):
     """got: GPU output tensor; ref: float64 oracle output. Returns error stats.
 
-    float32: the norm-wise and the per-row relative error must each be at
-    most 1e-5; the elementwise relative error where |o| > 1e-3 is reported
-    (it grows without bound as |o| nears 0, whatever the arithmetic)."""
+    float32: the norm-wise and the per-row relative error, and the
+    elementwise relative error where |o| >= 0.1, must each be at most 1e-5.
+    The elementwise error where |o| > 1e-3 is reported: float32 sums over
+    hundreds of keys leave an absolute error near 1e-7 of the row's scale, so
+    an element of 1e-3 carries about 1e-4 relative error whatever the
+    kernel."""
     g = host_f32(got).astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.isfinite(g).all(), f"{where}: non-finite GPU output"
     err = np.abs(g - ref)
     if dtype == W.F32:
-        rel, row, elem = fp32_errors(g, ref)
+        rel, row, elem, elem_big = fp32_errors(g, ref)
         say(f"{where}: fp32 relative error norm-wise {rel:.3e}, worst row {row:.3e}, "
-            f"elementwise (|o| > 1e-3) {elem:.3e}")
+            f"elementwise (|o| > 1e-3) {elem:.3e}, elementwise (|o| >= 0.1) {elem_big:.3e}")
         assert rel <= F32_REL, f"{where}: fp32 norm-wise relative error {rel:.3e} > {F32_REL}"
         assert row <= F32_REL, f"{where}: fp32 per-row relative error {row:.3e} > {F32_REL}"
-        return {"rel": rel, "row_rel": row, "elem_rel": elem}
+        assert elem_big <= F32_REL, (f"{where}: fp32 elementwise relative error (|o| >= 0.1) "
+                                     f"{elem_big:.3e} > {F32_REL}")
+        return {"rel": rel, "row_rel": row, "elem_rel": elem, "elem_rel_big": elem_big}
     mx, mean = float(err.max()), float(err.mean())
     assert mx <= BF16_MAX_ABS, f"{where}: bf16 max abs error {mx:.4e} > {BF16_MAX_ABS}"
     assert mean <= BF16_MEAN_ABS, f"{where}: bf16 mean abs error {mean:.4e} > {BF16_MEAN_ABS}"

@@ -113,15 +113,36 @@ def _plan_bytes(S, cap_dec, cap_pf, Hq):
     return -(-(pf + 12 * cap_pf) * 4 // 256) * 256
 
 
+def _auto_slots(S, Hq, max_seq_len, P, max_parts, dec_grid=256):
+    """Partial slots with automatic partitions: at most max_parts per row, and
+    at most rows + chunks, the chunks of the decode key axis numbering at most
+    the decode waves per KV head (dec_grid * 4 waves over at least Hq / 8 KV
+    heads; without a GPU the library assumes 256 compute units) or the axis
+    over the largest partition (63 pages, at most 65536 keys)."""
+    waves = -(-(dec_grid * 4 * 8) // Hq)
+    split_max = min(63 * P, 65536) // 16 * 16
+    by_cap = -(-(S * (-(-max_seq_len // 16) * 16)) // split_max)
+    chunks = max(waves, by_cap)
+    return min(S * max_parts, chunks), min(S * max_parts, S + chunks)
+
+
 def test_workspace_size_query():
     lib = pa.lib()
     ws = lib.pa_paged_attention_workspace_size
     # automatic split: decode rows share one key axis cut into chunks of at least 256
     # keys (P = 256), so a row of n keys has at most ceil(n / 256) + 1 partials
+    cap, slots = _auto_slots(64, 32, 256, 256, 2)
     assert ws(64, 64, 32, 128, 1, 256, 256, 0, BF16) == (
-        _plan_bytes(64, 64 * 2, 0, 32) + 64 * 2 * 32 * 130 * 4)
+        _plan_bytes(64, cap, 0, 32) + slots * 32 * 130 * 4)
+    cap, slots = _auto_slots(64, 32, 4096, 256, 17)
+    assert (cap, slots) == (256, 320)
     n = ws(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
-    assert n == _plan_bytes(64, 64 * 17, 0, 32) + 64 * 17 * 32 * 130 * 4
+    assert n == _plan_bytes(64, cap, 0, 32) + slots * 32 * 130 * 4
+    # long rows: 36 rows of up to 32768 keys with Hq = 32 (at most 256 waves per KV head)
+    cap, slots = _auto_slots(36, 32, 32768, 256, 129)
+    assert (cap, slots) == (256, 292)
+    assert ws(36, 36, 32, 128, 1, 32768, 256, 0, BF16) == (
+        _plan_bytes(36, cap, 0, 32) + slots * 32 * 130 * 4)
     # an explicit split of 1024 keys: partitions aligned to the row start, 4 partials
     assert ws(64, 64, 32, 128, 1, 4096, 256, 1024, BF16) == (
         _plan_bytes(64, 64 * 4, 0, 32) + 64 * 4 * 32 * 130 * 4)
@@ -133,9 +154,10 @@ def test_workspace_size_query():
     # partitions long items may be cut into pieces: 512 partial slots of 128 rows
     # (D + 2 floats each), one more entry per slot at most
     pf_bytes = -(-(512 * 128 * 130 * 4) // 256) * 256
+    cap, slots = _auto_slots(51, 32, 4096, 256, 17)
     assert ws(51, 2096, 32, 128, 1024, 4096, 256, 0, BF16) == (
-        _plan_bytes(51, 51 * 17, min(51 * 64, 2096 // 16 + 51) + 512, 32)
-        + 51 * 17 * 32 * 130 * 4 + pf_bytes)
+        _plan_bytes(51, cap, min(51 * 64, 2096 // 16 + 51) + 512, 32)
+        + slots * 32 * 130 * 4 + pf_bytes)
     # a fixed split never cuts prefill items
     assert ws(51, 2096, 32, 128, 1024, 4096, 256, 1024, BF16) == (
         _plan_bytes(51, 51 * 4, min(51 * 64, 2096 // 16 + 51), 32) + 51 * 4 * 32 * 130 * 4)
@@ -263,3 +285,4 @@ def test_validation_switch_keeps_host_checks_first():
         assert pa.pa_validation_message() == ""
     finally:
         pa.pa_set_validation(False)
+
