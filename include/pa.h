@@ -246,6 +246,36 @@ pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* posi
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_tick_forward_noalloc -- pa_tick_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc. Same arguments as pa_tick_forward without
+ * the workspace, same results bit for bit (the same kernels).
+ *
+ * Scratch: one fixed array of 64 MiB of device memory that the library holds
+ * on every GPU it runs on until the process ends; its address on a GPU is
+ * looked up at the first call there. A tick whose workspace
+ * (pa_paged_attention_workspace_size with the same arguments) exceeds
+ * 64 MiB returns PA_ERR_WORKSPACE_TOO_SMALL with nothing enqueued, and
+ * pa_validation_message() then gives the bytes it needs. Every other check is
+ * pa_tick_forward's, and all of them run before any HIP call.
+ * The call allocates and frees nothing (no hipMalloc, no hipFree, no
+ * allocating library routine). All calls on one GPU share its array; each
+ * call writes every part of it that it reads, so nothing needs clearing, but
+ * calls that overlap in time on one GPU (two streams, or two host threads)
+ * race and give unspecified results. Calls on one stream are ordered and safe.
+ */
+pa_status_t pa_tick_forward_noalloc(void* q, void* k, const void* v, const int32_t* positions,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    const int32_t* query_start_loc, const float* cos_sin,
+                                    void* k_pool, void* v_pool, void* out,
+                                    int32_t* slot_mapping, int32_t S, int32_t T, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, int32_t page_size,
+                                    int32_t num_pages, int32_t max_blocks_per_seq,
+                                    int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
+                                    float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
+                                    void* stream);
+
+/*
  * Kernel timing for benchmarks (not part of the tick). While on, every kernel
  * the library enqueues is bracketed by two hipEvents recorded on the same
  * stream, for up to `capacity` launches. pa_profile_stop waits for the last

@@ -21,7 +21,7 @@ __all__ = [
     "pa_rope_and_cache_write", "pa_paged_attention_workspace_size", "pa_paged_attention_varlen",
     "pa_tick_forward", "pa_profile_start", "pa_profile_stop", "pa_profile_reset",
     "BlockManager", "PA_ERR_NO_PAGES", "pa_sample_tokens", "pa_set_validation",
-    "pa_validation_message", "pa_probe_stream_read",
+    "pa_validation_message", "pa_probe_stream_read", "pa_tick_forward_noalloc",
 ]
 
 PA_F32 = 0
@@ -49,6 +49,9 @@ SIGNATURES = {
     "pa_tick_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_tick_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _f32, _i32, _i32, _vp]),
     "pa_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_admit": (_i32, [_vp, ctypes.c_int64, _vp, _i32, _i32, ctypes.POINTER(_i32)]),
@@ -75,7 +78,7 @@ SIGNATURES = {
 class PaError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        detail = pa_validation_message() if status == 1 else ""
+        detail = pa_validation_message() if status in (1, 3) else ""
         super().__init__(f"{where}: {pa_status_string(status)} (status {status})"
                          + (f": {detail}" if detail else ""))
 
@@ -370,6 +373,53 @@ def pa_probe_stream_read(buf, sink=None, stream=None):
     _check(lib().pa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                       _stream(stream)), "pa_probe_stream_read")
     return sink
+
+
+def pa_tick_forward_noalloc(q, k, v, positions, block_tables, seq_lens, query_start_loc,
+                            cos_sin, k_pool, v_pool, max_query_len, max_seq_len, out, slot_mapping,
+                            scale=None, kv_split_tokens=0, stream=None):
+    """``pa_tick_forward`` on the library's fixed scratch: no workspace, and
+    the caller passes ``out`` and ``slot_mapping`` (nothing is allocated here
+    or in the library). Raises PaError (PA_ERR_WORKSPACE_TOO_SMALL) when the
+    tick needs more scratch than the library holds."""
+    torch = _torch()
+    _dev(q, "q", ndim=3)
+    dt = _dtype_code(q)
+    for t, name in ((k, "k"), (v, "v"), (out, "out")):
+        _dev(t, name, q.dtype, 3)
+    _dev(k_pool, "k_pool", q.dtype, 4)
+    _dev(v_pool, "v_pool", q.dtype, 4)
+    for t, name in ((positions, "positions"), (seq_lens, "seq_lens"),
+                    (query_start_loc, "query_start_loc"), (slot_mapping, "slot_mapping")):
+        _dev(t, name, torch.int32, 1)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    if cos_sin is not None:
+        _dev(cos_sin, "cos_sin", torch.float32, 2)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    S, max_blocks = block_tables.shape
+    if (tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D)
+            or tuple(out.shape) != (T, Hq, D)):
+        raise ValueError("q/k/v/out shapes disagree")
+    if tuple(k_pool.shape) != (num_pages, P, Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("pool shape must be [num_pages, P, Hkv, D]")
+    if positions.shape[0] != T or slot_mapping.shape[0] != T:
+        raise ValueError("positions and slot_mapping need one entry per token")
+    if seq_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("seq_lens needs S entries and query_start_loc S + 1")
+    max_pos = cos_sin.shape[0] if cos_sin is not None else 0
+    if cos_sin is not None and cos_sin.shape[1] != D:
+        raise ValueError("cos_sin must be [max_pos, head_dim]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(lib().pa_tick_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(block_tables), _ptr(seq_lens),
+        _ptr(query_start_loc), _ptr(cos_sin), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+        _ptr(slot_mapping), S, T, Hq, Hkv, D, P, num_pages, max_blocks, int(max_query_len),
+        int(max_seq_len), max_pos, float(scale), int(kv_split_tokens), dt, _stream(stream)),
+        "pa_tick_forward_noalloc")
+    return out
 
 
 def pa_profile_start(capacity=4096):

@@ -348,6 +348,42 @@ pa_status_t check_slots_unique(const std::vector<int32_t>& slots, long pool_slot
 }  // namespace
 }  // namespace pa
 
+namespace pa {
+namespace {
+
+// ------------------------------------------------ fixed scratch -----
+// The scratch of pa_tick_forward_noalloc: one fixed array per GPU, for callers
+// that cannot allocate (graph capture, serving loops without hipMalloc). The
+// runtime places it in each GPU's memory when the library's code is loaded
+// there, and it stays until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: host code uses only the device
+// address looked up below, once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr size_t kScratchAlign = 256;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_of;  // device -> address of its `scratch`
+
+pa_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_of.find(dev);
+  if (it == g_scratch_of.end()) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr ||
+        ((uintptr_t)ptr % kScratchAlign) != 0)
+      return PA_ERR_HIP;
+    it = g_scratch_of.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
 using namespace pa;
 
 #pragma GCC visibility push(default)
@@ -705,6 +741,44 @@ pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* posi
                            k_pool, v_pool, out, slot_mapping, S, T, Hq, Hkv, head_dim, page_size,
                            num_pages, max_blocks_per_seq, max_query_len, max_seq_len, max_pos,
                            scale, kv_split_tokens, dtype, workspace, workspace_bytes, stream,
+                           true);
+}
+
+pa_status_t pa_tick_forward_noalloc(void* q, void* k, const void* v, const int32_t* positions,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    const int32_t* query_start_loc, const float* cos_sin,
+                                    void* k_pool, void* v_pool, void* out,
+                                    int32_t* slot_mapping, int32_t S, int32_t T, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, int32_t page_size,
+                                    int32_t num_pages, int32_t max_blocks_per_seq,
+                                    int32_t max_query_len, int32_t max_seq_len, int32_t max_pos,
+                                    float scale, int32_t kv_split_tokens, pa_dtype_t dtype,
+                                    void* stream) {
+  g_vmsg[0] = '\0';
+  // Every check first, with a stand-in scratch address (aligned, never
+  // dereferenced): a bad or oversized call returns before any HIP call.
+  void* const stand_in = reinterpret_cast<void*>((uintptr_t)kScratchAlign);
+  pa_status_t st = tick_forward_impl(q, k, v, positions, block_tables, seq_lens,
+                                     query_start_loc, cos_sin, k_pool, v_pool, out, slot_mapping,
+                                     S, T, Hq, Hkv, head_dim, page_size, num_pages,
+                                     max_blocks_per_seq, max_query_len, max_seq_len, max_pos,
+                                     scale, kv_split_tokens, dtype, stand_in, kScratchBytes,
+                                     stream, false);
+  if (st == PA_ERR_WORKSPACE_TOO_SMALL) {
+    const size_t need = workspace_bytes_for(S, T, Hq, head_dim, max_query_len, max_seq_len,
+                                            page_size, kv_split_tokens, dtype);
+    vfail("the tick needs %zu bytes of scratch; the fixed scratch holds %zu", need,
+          kScratchBytes);
+    return st;
+  }
+  if (st != PA_OK || T == 0) return st;
+  void* scratch_ptr = nullptr;
+  st = scratch_address(&scratch_ptr);
+  if (st != PA_OK) return st;
+  return tick_forward_impl(q, k, v, positions, block_tables, seq_lens, query_start_loc, cos_sin,
+                           k_pool, v_pool, out, slot_mapping, S, T, Hq, Hkv, head_dim, page_size,
+                           num_pages, max_blocks_per_seq, max_query_len, max_seq_len, max_pos,
+                           scale, kv_split_tokens, dtype, scratch_ptr, kScratchBytes, stream,
                            true);
 }
 

@@ -286,3 +286,36 @@ def test_validation_switch_keeps_host_checks_first():
     finally:
         pa.pa_set_validation(False)
 
+
+def tick_noalloc(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, bt=FAKE, seq_lens=FAKE, qsl=FAKE, cs=FAKE,
+                kp=FAKE, vp=FAKE, out=ctypes.c_void_p(0x900000000), slots=FAKE, S=4, T=4, Hq=8,
+                Hkv=2, D=128, P=256, num_pages=64, max_blocks=16, max_query_len=1,
+                max_seq_len=256, max_pos=4096, scale=0.1, split=0, dtype=BF16, stream=None)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_tick_forward_noalloc(
+        a["q"], a["k"], a["v"], a["pos"], a["bt"], a["seq_lens"], a["qsl"], a["cs"], a["kp"],
+        a["vp"], a["out"], a["slots"], a["S"], a["T"], a["Hq"], a["Hkv"], a["D"], a["P"],
+        a["num_pages"], a["max_blocks"], a["max_query_len"], a["max_seq_len"], a["max_pos"],
+        a["scale"], a["split"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(Hq=7), INVALID),
+    (dict(P=24), UNSUPPORTED),
+    (dict(split=20), INVALID),
+    # a fixed 16-key split over 4096-key rows: 64 x 256 partials of 32 heads, about
+    # 272 MB of scratch, past the library's fixed 64 MiB
+    (dict(S=64, T=64, Hq=32, Hkv=8, max_seq_len=4096, split=16), WS_SMALL),
+])
+def test_noalloc_tick_checks_everything_before_any_hip_call(kw, code):
+    assert tick_noalloc(**kw) == code
+    if code == WS_SMALL:
+        msg = pa.pa_validation_message()
+        assert "needs" in msg and str(64 << 20) in msg, msg
+
+
+def test_noalloc_empty_tick_is_ok_without_touching_memory():
+    assert tick_noalloc(T=0) == OK
