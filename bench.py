@@ -345,14 +345,19 @@ def cpu_baseline(t, reps):
             "cpu_model": cpu_model()}
 
 
+# The sources of the kernels a tick runs (and their launch set-up): a counter
+# summary taken on other sources no longer describes these kernels.
+TICK_SOURCES = ("pa_api.hip", "pa_decode.hip", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h",
+                "pa_plan.h", "pa_plan.hip", "pa_prefill_mfma.h", "pa_rope_cache.hip", "pa_tick.hip")
+
+
 def kernel_sources_digest():
-    """sha256 over the library's kernel sources (csrc/*.hip, csrc/*.h, include/pa.h)."""
-    import glob
+    """sha256 over the sources of the tick's kernels (TICK_SOURCES in csrc/, and
+    include/pa.h)."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_page_amd", "csrc", "*.hip")) +
-                   glob.glob(os.path.join(ROOT, "paged_kv_cache_page_amd", "csrc", "*.h")) +
-                   [os.path.join(ROOT, "include", "pa.h")])
+    files = [os.path.join(ROOT, "paged_kv_cache_page_amd", "csrc", f) for f in TICK_SOURCES]
+    files.append(os.path.join(ROOT, "include", "pa.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -360,21 +365,25 @@ def kernel_sources_digest():
     return h.hexdigest()
 
 
-def committed_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/<kernel>_<workload>_traffic.md, a line `traffic-json: {...}`),
-    or None when there is none or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+def committed_record(path, tag):
+    """The `<tag>: {...}` JSON record of a committed counter summary under
+    profiles/, or None when there is none or the tick's kernel sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", path)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         for line in f:
-            if line.startswith("traffic-json:"):
+            if line.startswith(tag + ":"):
                 rec = json.loads(line.split(":", 1)[1])
-                if rec.get("sources_sha256") != kernel_sources_digest():
-                    return None
-                return rec.get("bytes_per_launch")
+                return rec if rec.get("sources_sha256") == kernel_sources_digest() else None
     return None
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` (profiles/<kernel>_<workload>_traffic.md)."""
+    rec = committed_record(f"{kernel}_{workload}_traffic.md", "traffic-json")
+    return rec.get("bytes_per_launch") if rec else None
 
 
 # ------------------------------------------------------------- other benches
@@ -623,13 +632,19 @@ def main():
             ks = profiled(pa, torch, sub, args.steps)
             k = dominant(ks)
             if leg == "decode_rows_only":
-                legs[leg] = hbm_entry(k, ks, dec["bytes"], {"all_kernels": ks})
+                legs[leg] = hbm_entry(k, ks, dec["bytes"], {
+                    "all_kernels": ks,
+                    "traffic": committed_traffic("decode_attention", t.name + "-decode-rows")})
             else:
                 tf = flops / (ks[k]["median_ms"] / 1e3) / 1e12
                 legs[leg] = {"kernel": k, "bound": "mfma", "flops_per_launch": flops,
                              "achieved_tflops": round(tf, 1),
                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), **ks[k],
-                             "all_kernels": ks}
+                             "all_kernels": ks,
+                             # MFMA busy cycles / (active cycles x SIMDs) and the bf16 MFMA
+                             # flops the counters saw, from the committed summary
+                             "counters": committed_record(
+                                 f"prefill_chunks_{t.name}_mfma-counters.md", "counters-json")}
         if cfg == 4:
             for name, c in (("cfg3_decode", 3), ("cfg5_decode", 5)):
                 log("leg", name)

@@ -14,7 +14,11 @@ constexpr int kProbeUnroll = 8;  // 16-byte loads in flight per thread
 
 // Every thread reads kProbeUnroll 16-byte vectors per step, grid-stride over
 // the buffer, and folds them with XOR; one word per thread goes to the sink so
-// the loads cannot be dropped.
+// the loads cannot be dropped. One workgroup per compute unit: of the shapes
+// measured on MI355X over 2 GiB (1-16 workgroups of 256 or 512 threads per
+// unit, 4-16 loads in flight, grid-stride or contiguous per workgroup), this
+// one and its neighbours read at 6.2-6.35 TB/s; 8 or 16 grid-stride
+// workgroups per unit fell to 5.1-5.4 TB/s.
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4* __restrict__ buf,
                                                                     size_t n16,
                                                                     uint32_t* __restrict__ sink) {
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4*
 
 }  // namespace
 
-int probe_grid() { return cu_count() * 8; }
+int probe_grid() { return cu_count(); }
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
   profile_before("stream_read", s);
