@@ -218,22 +218,33 @@ pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const v
                                       void* stream);
 
 /*
- * pa_tick_forward -- one layer's whole tick in one call: exactly
+ * pa_tick_forward -- one layer's whole tick in one call: the results of
  *   pa_compute_slot_mapping(block_tables, query_start_loc, positions,
  *                           slot_mapping, ...),
  *   pa_rope_and_cache_write(q, k, v, positions, slot_mapping, cos_sin,
  *                           k_pool, v_pool, ...),
  *   pa_paged_attention_varlen(q, k_pool, v_pool, block_tables, seq_lens,
  *                             query_start_loc, out, ...)
- * in that order, with the same arguments, layouts, preconditions and results
- * (q must not be NULL; slot_mapping [T] int32 is written), bit for bit. The
- * tick's new K/V are stored before any attention read (Helios blog,
- * "Continuous batching": all the tick's rows, prefill and decode, go through
- * one forward). Enqueued as two launches fewer: the slot mapping, the page
- * write and the attention call's planning (which reads only
- * query_start_loc and seq_lens) share one launch, then the attention
- * kernels follow on `stream`. Every check of the three calls is made before
- * anything is enqueued.
+ * in that order, with the same arguments, layouts and preconditions (q must
+ * not be NULL; slot_mapping [T] int32 is written): out, slot_mapping, k_pool
+ * and v_pool bit for bit. The tick's new K/V are stored before any attention
+ * read that needs them (Helios blog, "Continuous batching": all the tick's
+ * rows, prefill and decode, go through one forward). Every check of the three
+ * calls is made before anything is enqueued.
+ *
+ * q and k are inputs here, not results. bf16 ticks leave them unchanged:
+ * one launch before the attention holds the slot mapping, the page writes
+ * (each token's K rotated into its slot, q and k left as given), the rotation
+ * of the decode rows' queries into their rows of `out` (where the decode
+ * kernel reads them before it writes the results there) and the attention
+ * call's planning (which reads only query_start_loc and seq_lens); the
+ * attention kernels rotate each prefill row's query where they read it, with
+ * the page writer's arithmetic. For that rotation row i of a sequence with
+ * L rows and n keys is taken to be at position n - L + i: the tick's rows are
+ * the sequence's last keys (pa_set_validation checks it); with other positions
+ * the prefill rows' results are unspecified. float32 ticks run the three
+ * calls' kernels (the page write then rotates q and k in place), with the
+ * slot mapping, page write and planning in one launch.
  */
 pa_status_t pa_tick_forward(void* q, void* k, const void* v, const int32_t* positions,
                             const int32_t* block_tables, const int32_t* seq_lens,

@@ -288,11 +288,12 @@ def pa_tick_forward(q, k, v, positions, block_tables, seq_lens, query_start_loc,
                     out=None, slot_mapping=None, workspace=None, stream=None):
     """One layer's tick in one call: slot mapping, RoPE + page write, attention.
 
-    Same as ``pa_compute_slot_mapping`` + ``pa_rope_and_cache_write`` +
-    ``pa_paged_attention_varlen`` with these arguments (q and k are rotated in
-    place), bit for bit, enqueued as one launch for the slot mapping, the page
-    write and the attention's plan, then the attention kernels. Returns
-    ``out``; ``slot_mapping`` ``[T]`` int32 is written (allocated if None).
+    ``out``, the slots and the pools are those of ``pa_compute_slot_mapping`` +
+    ``pa_rope_and_cache_write`` + ``pa_paged_attention_varlen`` with these
+    arguments, bit for bit. bf16 ticks leave ``q`` and ``k`` unchanged (the
+    attention rotates what it reads); float32 ticks rotate them in place as
+    the page write does. Returns ``out``; ``slot_mapping`` ``[T]`` int32 is
+    written (allocated if None).
     """
     torch = _torch()
     _dev(q, "q", ndim=3)

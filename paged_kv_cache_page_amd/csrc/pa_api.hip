@@ -389,7 +389,7 @@ using namespace pa;
 #pragma GCC visibility push(default)
 extern "C" {
 
-int32_t pa_abi_version(void) { return 5; }
+int32_t pa_abi_version(void) { return 6; }
 
 void pa_set_validation(int32_t on) { g_validate.store(on ? 1 : 0, std::memory_order_relaxed); }
 
@@ -606,6 +606,13 @@ pa_status_t attention_setup(const void* q, const void* k_pool, const void* v_poo
   a.pf_slots = wl.pf_slots;
   a.pf_ws = (float*)((char*)workspace + wl.plan_bytes + wl.partial_bytes);
   a.pf_workers = (!wl.token_mode && wl.cap_pf > 0) ? tick_grid(dtype, head_dim, G) : 1;
+  // not a fused tick unless pa_tick_forward says so
+  a.fused = 0;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.positions = nullptr;
+  a.cos_sin = nullptr;
+  a.max_pos = 0;
 
   return PA_OK;
 }
@@ -717,11 +724,24 @@ pa_status_t tick_forward_impl(void* q, void* k, const void* v, const int32_t* po
 
   // One launch for the slot mapping, the page write and (seq mode) the plan,
   // which reads only query_start_loc and seq_lens; then the attention kernels.
+  // bf16 ticks are fused: the first launch writes only the prefill chunks'
+  // pages (and the slots and the plan), the attention kernels rotate the query
+  // rows they read and write the decode rows' pages themselves, and q and k
+  // are left as given.
   const bool plan = !c.empty && !c.wl.token_mode;
+  const bool fused = plan && dtype == PA_BF16;
+  if (fused) {
+    c.a.fused = 1;
+    c.a.k_new = k;
+    c.a.v_new = v;
+    c.a.positions = positions;
+    c.a.cos_sin = cos_sin;
+    c.a.max_pos = max_pos;
+  }
   if (launch_tick_prep(dtype, q, k, v, positions, block_tables, query_start_loc, slot_mapping,
                        cos_sin, k_pool, v_pool, S, T, Hq, Hkv, head_dim, page_size, num_pages,
                        max_blocks_per_seq, max_pos, plan ? &c.a : nullptr, c.a.cap_dec,
-                       c.a.cap_pf, kPrefillRows / c.G, (hipStream_t)stream) != hipSuccess)
+                       c.a.cap_pf, kPrefillRows / c.G, fused, (hipStream_t)stream) != hipSuccess)
     return PA_ERR_HIP;
   return attention_run(c, (hipStream_t)stream);
 }

@@ -538,7 +538,11 @@ __device__ __forceinline__ DecPre<D, G> decode_prefetch(const AttnArgs& a, const
   const int* bt_row = a.block_tables + (size_t)d.seq * a.max_blocks;
   p.page_raw = bt_row[pg0 + (lane < npg ? lane : 0)];
   const size_t row_bytes = (size_t)SH::ROWB;
-  const char* qrow = (const char*)a.q + ((size_t)d.token * a.Hq + (size_t)d.kvh * G) * row_bytes;
+  // the fused tick's page-write launch left the row's rotated query in its
+  // output row (q itself is the unrotated input); that row's result is written
+  // only once every range of the row has read it
+  const char* qbase = a.fused ? (const char*)a.out : (const char*)a.q;
+  const char* qrow = qbase + ((size_t)d.token * a.Hq + (size_t)d.kvh * G) * row_bytes;
   const int hq = col < G ? col : 0;
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)

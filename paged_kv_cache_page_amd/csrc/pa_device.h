@@ -85,4 +85,41 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// RoPE on 8 rotation pairs of bf16 values: a holds x1 = x[i .. i + 7], b the
+// partners x2 = x[i + D/2 .. i + D/2 + 7], c and s the cos and sin of the
+// token's angles for i .. i + 7. x1' = x1 c - x2 s, x2' = x2 c + x1 s, each
+// product and each sum rounded to float32 on its own (no fused multiply-add,
+// whatever the unit's contraction setting), then rounded to nearest-even
+// bf16. Every kernel that rotates Q or K uses this one definition, so a key
+// rotated in the attention kernel has the bits of the key the page writer
+// stores.
+__device__ __forceinline__ void rope_bf16x8(uint4& a, uint4& b, const float* c, const float* s) {
+#pragma clang fp contract(off)
+  uint32_t* aw = reinterpret_cast<uint32_t*>(&a);
+  uint32_t* bw = reinterpret_cast<uint32_t*>(&b);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x1l = bf16_lo(aw[w]), x1h = bf16_hi(aw[w]);
+    const float x2l = bf16_lo(bw[w]), x2h = bf16_hi(bw[w]);
+    const float cl = c[2 * w], ch = c[2 * w + 1], sl = s[2 * w], sh = s[2 * w + 1];
+    const float p1l = x1l * cl, q1l = x2l * sl, p2l = x2l * cl, q2l = x1l * sl;
+    const float p1h = x1h * ch, q1h = x2h * sh, p2h = x2h * ch, q2h = x1h * sh;
+    aw[w] = pack_bf16x2(p1l - q1l, p1h - q1h);
+    bw[w] = pack_bf16x2(p2l + q2l, p2h + q2h);
+  }
+}
+
+// The cos and sin of dims i .. i + 7 at table row p (float32 [max_pos, D]:
+// cos in columns [0, D/2), sin in [D/2, D)), for rope_bf16x8.
+__device__ __forceinline__ void rope_load8(const float* cs, int D, int p, int i, float* c,
+                                           float* s) {
+  const float4* cp = reinterpret_cast<const float4*>(cs + (size_t)p * D + i);
+  const float4* sp = reinterpret_cast<const float4*>(cs + (size_t)p * D + D / 2 + i);
+  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w; c[4] = c1.x; c[5] = c1.y; c[6] = c1.z;
+  c[7] = c1.w;
+  s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w; s[4] = s1.x; s[5] = s1.y; s[6] = s1.z;
+  s[7] = s1.w;
+}
+
 }  // namespace pa

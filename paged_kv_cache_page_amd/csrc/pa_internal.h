@@ -35,6 +35,16 @@ struct AttnArgs {
   float* pf_ws;         // partials: o [pf_slots][kPrefillRows][D], then (m, l) [pf_slots][kPrefillRows]
   int32_t pf_slots;     // partial slots (0 = never split)
   int32_t pf_workers;   // workgroups of the kernel that runs the prefill items
+  // The fused tick (bf16): the attention kernels rotate every query row they
+  // read (q is the unrotated input), and the wave that holds a decode row's
+  // last keys rotates that row's new key, writes its K/V page slot and uses
+  // the new rows from registers. Null / 0 otherwise.
+  int32_t fused;
+  const void* k_new;          // [T, Hkv, D] this tick's K rows, unrotated
+  const void* v_new;          // [T, Hkv, D] this tick's V rows
+  const int32_t* positions;   // [T]
+  const float* cos_sin;       // [max_pos, D] or null (no RoPE)
+  int32_t max_pos;
 };
 
 // Plan layout, in ints from the start of the workspace:
@@ -128,7 +138,7 @@ hipError_t launch_tick_prep(pa_dtype_t dt, void* q, void* k, const void* v, cons
                             const float* cs, void* k_pool, void* v_pool, int S, int T, int Hq,
                             int Hkv, int D, int P, int num_pages, int max_blocks, int max_pos,
                             const AttnArgs* plan_args, int cap_dec, int cap_pf, int TM,
-                            hipStream_t s);
+                            bool fused, hipStream_t s);
 
 // K2 + K3 (pa_decode.hip). token_mode = false: one row per decode sequence
 // (query length 1; other sequences skipped). token_mode = true: one row per

@@ -451,10 +451,27 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
     const int tq = row_ok[b] ? tok[b] : i1 - 1;  // rows past the chunk read a valid row, zeroed
     const char* qrow = (const char*)a.q + ((size_t)(q0 + tq) * Hq + head[b]) * row_bytes;
 #pragma unroll
-    for (int ds = 0; ds < DSTEPS; ++ds) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
-      qop[b][ds] = keep_if(x, row_ok[b]);
+    for (int ds = 0; ds < DSTEPS; ++ds)
+      qop[b][ds] = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
+    if (a.fused && a.cos_sin) {
+      // the fused tick's q is the unrotated input: rotate the lane's dims
+      // grp * 8 + 32 ds (pairs ds, ds + DSTEPS / 2) at the row's position,
+      // exactly as the page writer rotates a stored key. Row i of a chunk of
+      // L rows over n keys is the token at position n - L + i (the tick's
+      // rows are the sequence's last keys), so the cos/sin loads go out with
+      // the query loads instead of after a load of the position.
+      const int pos = last_key + tq;
+      if (pos >= 0 && pos < a.max_pos) {
+#pragma unroll
+        for (int ds = 0; ds < DSTEPS / 2; ++ds) {
+          float c[8], sn[8];
+          rope_load8(a.cos_sin, D, pos, grp * 8 + 32 * ds, c, sn);
+          rope_bf16x8(qop[b][ds], qop[b][ds + DSTEPS / 2], c, sn);
+        }
+      }
     }
+#pragma unroll
+    for (int ds = 0; ds < DSTEPS; ++ds) qop[b][ds] = keep_if(qop[b][ds], row_ok[b]);
   }
 
   f32x4_t acc_o[2][DBLK];

@@ -99,19 +99,7 @@ template <>
 struct RotPair<BF16> {
   static constexpr int VP = 8;
   __device__ static void rotate(uint4& a, uint4& b, const float* c, const float* s) {
-#pragma clang fp contract(off)
-    uint32_t* aw = reinterpret_cast<uint32_t*>(&a);
-    uint32_t* bw = reinterpret_cast<uint32_t*>(&b);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float x1l = bf16_lo(aw[w]), x1h = bf16_hi(aw[w]);
-      const float x2l = bf16_lo(bw[w]), x2h = bf16_hi(bw[w]);
-      const float cl = c[2 * w], ch = c[2 * w + 1], sl = s[2 * w], sh = s[2 * w + 1];
-      const float p1l = x1l * cl, q1l = x2l * sl, p2l = x2l * cl, q2l = x1l * sl;
-      const float p1h = x1h * ch, q1h = x2h * sh, p2h = x2h * ch, q2h = x1h * sh;
-      aw[w] = pack_bf16x2(p1l - q1l, p1h - q1h);
-      bw[w] = pack_bf16x2(p2l + q2l, p2h + q2h);
-    }
+    rope_bf16x8(a, b, c, s);
   }
 };
 
@@ -143,11 +131,18 @@ struct RopeArgs {
   char* k_pool;
   char* v_pool;
   int Hq, Hkv, D, P, num_pages, max_pos;
+  char* q_out;  // the fused tick: where the decode rows' rotated queries go (their out rows)
 };
 
 // K1 for token t, whose page slot is `slot` (stored only when in the pool).
-template <typename ET>
-__device__ __forceinline__ void rope_token(const RopeArgs& r, int t, long slot) {
+// IN_PLACE: q and k are rotated in place (pa_rope_and_cache_write). Otherwise
+// (the fused tick) k is left as it is and its rotated rows go to the pool
+// only, and the rotated query rows go to r.q_out's row t when q_to_out (a
+// decode row, whose attention reads them there) or nowhere (a prefill row: the
+// attention kernel rotates those where it reads them).
+template <typename ET, bool IN_PLACE = true>
+__device__ __forceinline__ void rope_token(const RopeArgs& r, int t, long slot,
+                                           bool q_to_out = false) {
   constexpr int EB = ET::kBytes;
   constexpr int VP = RotPair<ET>::VP;       // elements per 16-byte vector
   const int D = r.D, Hkv = r.Hkv;
@@ -158,7 +153,7 @@ __device__ __forceinline__ void rope_token(const RopeArgs& r, int t, long slot) 
   const int p = r.pos[t];
   const bool rotate = r.cs != nullptr && p >= 0 && p < r.max_pos;
   const bool store = slot >= 0 && slot < (long)r.num_pages * r.P;
-  const int nq = r.q ? r.Hq : 0;
+  const int nq = r.q && (IN_PLACE || q_to_out) ? r.Hq : 0;
   const int rot_tasks = (nq + Hkv) * vec_half;
   const int tasks = rot_tasks + Hkv * vec_row;
   // The block size is a multiple of vec_half (see the launch), so a
@@ -186,10 +181,17 @@ __device__ __forceinline__ void rope_token(const RopeArgs& r, int t, long slot) 
       uint4* p1 = reinterpret_cast<uint4*>(row + (size_t)c * 16);
       uint4* p2 = reinterpret_cast<uint4*>(row + (size_t)half * EB + (size_t)c * 16);
       uint4 a = *p1, b = *p2;
-      if (rotate) {
-        RotPair<ET>::rotate(a, b, cv, sv);
-        *p1 = a;
-        *p2 = b;
+      if (rotate) RotPair<ET>::rotate(a, b, cv, sv);
+      if (IN_PLACE) {
+        if (rotate) {
+          *p1 = a;
+          *p2 = b;
+        }
+      } else if (!is_k) {
+        // (q_to_out) the query row, rotated or as given, in the output row
+        char* orow = r.q_out + ((size_t)t * r.Hq + h) * row_bytes;
+        *reinterpret_cast<uint4*>(orow + (size_t)c * 16) = a;
+        *reinterpret_cast<uint4*>(orow + (size_t)half * EB + (size_t)c * 16) = b;
       }
       if (is_k && store) {
         char* dst = r.k_pool + ((size_t)slot * Hkv + kh) * row_bytes;
@@ -271,7 +273,14 @@ __device__ __forceinline__ int wave_find_seq(const int32_t* __restrict__ qsl, in
 // compute unit's slots (8 KiB of cost bins + 12 B per cached sequence).
 constexpr int kPrepCachedSeqs = 960;
 
-template <typename ET>
+// FUSED (the bf16 tick): q and k are left as they are. Every token rotates
+// its k into the pool only; a token that is a decode row of the plan (query
+// length 1, at least one key) also puts its rotated query rows in its output
+// row, where the decode kernel reads them (a few hundred KB: one row per
+// decode sequence); the prefill chunks' query rows are rotated by the
+// attention kernel where it reads them, so the chunks' queries (most of q)
+// are read once instead of read, written and read again.
+template <typename ET, bool FUSED>
 __global__ __launch_bounds__(kRopeThreads) void tick_prep_kernel(
     RopeArgs r, const int32_t* __restrict__ bt, const int32_t* __restrict__ qsl,
     int32_t* __restrict__ slots, int S, int max_blocks, AttnArgs a, int cap_dec, int cap_pf,
@@ -293,7 +302,13 @@ __global__ __launch_bounds__(kRopeThreads) void tick_prep_kernel(
     }
   }
   if (threadIdx.x == 0) slots[t] = slot;
-  rope_token<ET>(r, t, slot);
+  if constexpr (FUSED) {
+    // (seq is the same in every lane and wave of the workgroup)
+    const SeqShape sh = seq_shape(a, seq);
+    rope_token<ET, false>(r, t, slot, sh.L == 1 && sh.n >= 1 && sh.q0 == t);
+  } else {
+    rope_token<ET>(r, t, slot);
+  }
 }
 
 hipError_t launch_tick_prep(pa_dtype_t dt, void* q, void* k, const void* v, const int32_t* pos,
@@ -301,22 +316,27 @@ hipError_t launch_tick_prep(pa_dtype_t dt, void* q, void* k, const void* v, cons
                             const float* cs, void* k_pool, void* v_pool, int S, int T, int Hq,
                             int Hkv, int D, int P, int num_pages, int max_blocks, int max_pos,
                             const AttnArgs* plan_args, int cap_dec, int cap_pf, int TM,
-                            hipStream_t s) {
+                            bool fused, hipStream_t s) {
   const int plan_blocks = plan_args ? 1 : 0;
   if (T + plan_blocks == 0) return hipSuccess;
-  const RopeArgs r{(char*)q, (char*)k, (const char*)v, pos, cs, (char*)k_pool, (char*)v_pool,
+  if (fused && (!plan_args || dt != PA_BF16)) return hipErrorInvalidValue;
+  RopeArgs r{(char*)q, (char*)k, (const char*)v, pos, cs, (char*)k_pool, (char*)v_pool,
                    Hq, Hkv, D, P, num_pages, max_pos};
+  r.q_out = fused && plan_args ? (char*)plan_args->out : nullptr;
   AttnArgs a{};
   if (plan_args) a = *plan_args;
   const int threads = rope_threads(dt, D);
   const dim3 grid((unsigned)(T + plan_blocks));
-  profile_before("tick_prep", s);
-  if (dt == PA_BF16)
-    hipLaunchKernelGGL(tick_prep_kernel<BF16>, grid, dim3(threads), 0, s, r, bt, qsl, slots, S,
-                       max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
+  profile_before(fused ? "tick_plan_write" : "tick_prep", s);
+  if (fused)
+    hipLaunchKernelGGL((tick_prep_kernel<BF16, true>), grid, dim3(threads), 0, s, r, bt, qsl,
+                       slots, S, max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
+  else if (dt == PA_BF16)
+    hipLaunchKernelGGL((tick_prep_kernel<BF16, false>), grid, dim3(threads), 0, s, r, bt, qsl,
+                       slots, S, max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
   else
-    hipLaunchKernelGGL(tick_prep_kernel<F32>, grid, dim3(threads), 0, s, r, bt, qsl, slots, S,
-                       max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
+    hipLaunchKernelGGL((tick_prep_kernel<F32, false>), grid, dim3(threads), 0, s, r, bt, qsl,
+                       slots, S, max_blocks, a, cap_dec, cap_pf, TM, plan_blocks);
   profile_after(s);
   return hipGetLastError();
 }

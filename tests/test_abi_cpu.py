@@ -46,7 +46,7 @@ def test_library_exports_nothing_else():
 
 
 def test_status_strings_and_version():
-    assert pa.pa_abi_version() == 5
+    assert pa.pa_abi_version() == 6
     for code in range(5):
         assert pa.pa_status_string(code).startswith("PA_")
     assert "UNKNOWN" in pa.pa_status_string(99)

@@ -297,20 +297,25 @@ def test_tick_forward_equals_the_three_calls_bitwise(which):
                              table, b.k_pool, b.v_pool, t.max_query_len, t.max_seq_len,
                              scale=t.scale, kv_split_tokens=split, slot_mapping=slots)
     torch.cuda.synchronize()
-    for name, x, y in (("out", ref, out), ("slots", a.slots, slots), ("q", a.q, b.q),
-                       ("k", a.k, b.k), ("k_pool", a.k_pool, b.k_pool),
-                       ("v_pool", a.v_pool, b.v_pool)):
+    for name, x, y in (("out", ref, out), ("slots", a.slots, slots),
+                       ("k_pool", a.k_pool, b.k_pool), ("v_pool", a.v_pool, b.v_pool)):
         assert np.array_equal(_bits(x), _bits(y)), f"{which}: {name} differs"
     # and the write side equals the oracle's bit for bit (same cos/sin table)
     res = oracle.run_tick(t.dtype, t.q, t.k, t.v, t.positions, t.block_tables, t.qsl,
                           t.seq_lens, t.k_pool, t.v_pool,
                           oracle.rope_table(t.max_pos, t.D, t.theta) if t.theta else None,
                           t.scale)
-    for name, x in (("slots", slots), ("q", b.q), ("k", b.k), ("k_pool", b.k_pool),
-                    ("v_pool", b.v_pool)):
-        want = res["slots" if name == "slots" else name]
+    for name, x in (("slots", slots), ("k_pool", b.k_pool), ("v_pool", b.v_pool)):
+        want = res[name]
         got = _bits(x).reshape(want.shape)
         assert np.array_equal(got, want.view(got.dtype)), f"{which}: {name} != oracle"
+    # q and k: the fused bf16 tick rotates them where it reads them and leaves
+    # the inputs as they are; a float32 tick rotates them in place, as the
+    # three calls do
+    for name, x, given, rotated in (("q", b.q, t.q, res["q"]), ("k", b.k, t.k, res["k"])):
+        want = given if t.dtype == W.BF16 else rotated
+        got = _bits(x).reshape(want.shape)
+        assert np.array_equal(got, want.view(got.dtype)), f"{which}: {name}"
     if which.startswith("many"):  # these sizes are not among the parity cases above
         check_attention(out, oracle_tick(t), t.dtype, which)
 

@@ -37,7 +37,7 @@ def _both(t, split=0):
     torch.cuda.synchronize()
     for name, x, y in (("out", ref, out), ("slots", ref_slots, slots), ("q", a.q, b.q),
                        ("k", a.k, b.k), ("k_pool", a.k_pool, b.k_pool),
-                       ("v_pool", a.v_pool, b.v_pool)):
+                       ("v_pool", a.v_pool, b.v_pool)):  # (q, k: as each call leaves them)
         assert np.array_equal(_bits(x), _bits(y)), f"{t.name}: {name} differs"
 
 
