@@ -99,11 +99,22 @@ def prefill_work(t):
     return flops
 
 
-def k1_bytes(t):
-    """RoPE + page write per token: reads q, k, v rows, the position and slot and
-    the cos/sin row; writes q and k back and K/V into the pools."""
+def prep_bytes(t):
+    """Algorithmic bytes of the launch before the attention (slot mapping, RoPE,
+    page write). Every token reads its k and v rows, its position, cos/sin row
+    and page-table entry, and writes its slot and its K and V rows into the
+    pools. A bf16 tick leaves q and k as they are and stages each decode row's
+    rotated query in `out` (read q row, write out row); the prefill rows'
+    queries are rotated by the attention kernel where it reads them. A float32
+    tick reads and writes q and k back in place."""
     e = 2 if t.dtype == "bf16" else 4
-    return t.T * ((t.Hq + 2 * t.Hkv) * t.D * e + 8 + t.D * 4) + t.T * (t.Hq + 3 * t.Hkv) * t.D * e
+    kv = 2 * t.Hkv * t.D * e
+    per_token = kv + 4 + 4 * t.D + 4 + 4 + kv
+    if t.dtype == "bf16":
+        qrow = t.Hq * t.D * e
+        dec = int((t.query_lens == 1).sum())
+        return t.T * per_token + dec * 2 * qrow
+    return t.T * (per_token + (2 * t.Hq + t.Hkv) * t.D * e)  # q read and written, k written
 
 
 def stats(v):
@@ -618,7 +629,7 @@ def main():
     extra = {"attention_only_tokens_per_s": round(t.T / (attn_ms / 1e3), 1) if attn_ms else None,
              "warm_ms_per_step": round(warm_ms, 5),
              "warm_tokens_per_s": round(t.T / (warm_ms / 1e3), 1),
-             "k1_bytes_per_step": k1_bytes(t)}
+             "prep_bytes_per_step": prep_bytes(t)}
 
     legs = {}
     if not args.no_legs:
