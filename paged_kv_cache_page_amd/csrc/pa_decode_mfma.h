@@ -379,12 +379,16 @@ __device__ __forceinline__ DecSrc dec_src(const AttnArgs& a, const DecSeg& d, in
 // reads wait for it: the walk waits for these loads itself (dec_wait). The
 // "memory" clobber keeps other memory accesses on their side of it; M0 is
 // set right before each compiler use of it and holds nothing across code.
+// The loads are marked non-temporal (nt): a decode row's K/V rows are read
+// once per tick, so the caches need not keep them, and the prefill tiles that
+// the fused tick re-reads stay cached instead (measured: decode rows alone
+// 88.6 -> 78.6 us, the packed tick's step 132.5 -> 124.3 us, same GPU).
 __device__ __forceinline__ void dec_dma16(const char* base, uint32_t voff, uint32_t lds) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(bs),
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(bs),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
