@@ -304,7 +304,7 @@ pa_status_t pa_profile_reset(void);
  * Measurement helpers (not part of a tick).
  *
  * pa_probe_stream_read -- read `bytes` of device memory at `buf` once, as a
- * plain stream of 16-byte loads over the whole GPU, and write one 32-bit word
+ * plain stream of non-temporal 16-byte loads over the whole GPU, and write one 32-bit word
  * per thread to `sink` (pa_probe_sink_words() words of device memory): the
  * practical read bandwidth of this GPU, against which the HBM-bound kernels'
  * achieved bandwidth is read. bytes > 0 and a multiple of 16, buf 16-byte
