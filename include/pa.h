@@ -197,8 +197,8 @@ size_t pa_paged_attention_workspace_size(int32_t S, int32_t T, int32_t Hq, int32
  * to nearest-even into the storage dtype.
  *
  * Host scalars: max_query_len >= every L and max_seq_len >= every n (they
- * size the grids; rows beyond them are not computed). Sequences with L = 0
- * produce nothing. kv_split_tokens: keys per split-KV partition of a decode
+ * size the grids; rows beyond them are not computed). S < 2^30 (else
+ * PA_ERR_INVALID_ARG). Sequences with L = 0 produce nothing. kv_split_tokens: keys per split-KV partition of a decode
  * row (0 = library default; otherwise a multiple of 16 in [16, 65536]).
  * workspace: device scratch of at least
  * pa_paged_attention_workspace_size(...) bytes (NULL allowed when that is 0);
@@ -206,6 +206,11 @@ size_t pa_paged_attention_workspace_size(int32_t S, int32_t T, int32_t Hq, int32
  * Preconditions (not checked): L <= n; the first ceil(n / P) entries of each
  * block-table row are valid page ids; pages shared by several sequences are
  * read-only during the call.
+ * Caching: decode rows stream their K/V past the caches (each row's keys are
+ * read once), except rows whose first page is also another decode row's
+ * first page (a prefix shared through the page tables: Helios blog, "Prefix
+ * caching"), whose keys are loaded into the caches for the other sharers.
+ * This changes no result.
  */
 pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const void* v_pool,
                                       const int32_t* block_tables, const int32_t* seq_lens,

@@ -530,9 +530,9 @@ pa_status_t attention_setup(const void* q, const void* k_pool, const void* v_poo
                             size_t workspace_bytes, AttnCall& c) {
   c.empty = false;
   c.dtype = dtype;
-  if (!dtype_ok(dtype) || S < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || head_dim < 1 ||
-      page_size < 1 || num_pages < 1 || max_blocks_per_seq < 1 || max_query_len < 0 ||
-      max_seq_len < 0 || !isfinite(scale))
+  if (!dtype_ok(dtype) || S < 0 || S >= kRowShared || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
+      head_dim < 1 || page_size < 1 || num_pages < 1 || max_blocks_per_seq < 1 ||
+      max_query_len < 0 || max_seq_len < 0 || !isfinite(scale))
     return PA_ERR_INVALID_ARG;
   if (kv_split_tokens != 0 && (kv_split_tokens < 16 || kv_split_tokens > 65536 ||
                                kv_split_tokens % 16))

@@ -157,6 +157,7 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
 // partials at slot pslot + part of the split-KV workspace), KV head kvh.
 struct DecSeg {
   int seq, token, pslot, kbeg, kend, part, nparts, kvh;
+  int cached = 0;  // the row's keys go through the caches (a shared prefix)
 };
 
 // Walk of decode wave gw = 4 wg + wave over the chunks of the decode key axis
@@ -236,7 +237,8 @@ struct DecodeCursor {
       const int off = r.y, n = r.z;
       const int pad = (n + A - 1) / A * A;
       const int c0 = chunk * C, c1 = c0 + C;
-      d.seq = r.x;
+      d.seq = r.x & (kRowShared - 1);
+      d.cached = (r.x & kRowShared) != 0;
       d.token = r.w;
       d.pslot = pb;
       d.kbeg = max(c0, off) - off;
@@ -321,6 +323,7 @@ struct DecSrc {
   int pg0;            // the range's first page
   int kbeg;           // first key (a multiple of 16)
   int nbuf;           // 16-key buffers (>= 1)
+  int cached;         // ordinary loads (a shared prefix) instead of streaming ones
 };
 
 // Per-lane source offsets of the K and V loads within a 16-key buffer (one
@@ -367,6 +370,7 @@ __device__ __forceinline__ DecSrc dec_src(const AttnArgs& a, const DecSeg& d, in
   s.pg0 = d.kbeg >> a.p_shift;
   s.kbeg = d.kbeg;
   s.nbuf = (d.kend - d.kbeg + 15) / 16;
+  s.cached = __builtin_amdgcn_readfirstlane(d.cached);
   return s;
 }
 
@@ -379,18 +383,26 @@ __device__ __forceinline__ DecSrc dec_src(const AttnArgs& a, const DecSeg& d, in
 // reads wait for it: the walk waits for these loads itself (dec_wait). The
 // "memory" clobber keeps other memory accesses on their side of it; M0 is
 // set right before each compiler use of it and holds nothing across code.
-// The loads are marked non-temporal (nt): a decode row's K/V rows are read
+// STREAM marks the load non-temporal (nt): a decode row's K/V rows are read
 // once per tick, so the caches need not keep them, and the prefill tiles that
 // the fused tick re-reads stay cached instead (measured: decode rows alone
-// 88.6 -> 78.6 us, the packed tick's step 132.5 -> 124.3 us, same GPU).
+// 88.6 -> 78.6 us, the packed tick's step 132.5 -> 124.3 us, same GPU). Rows
+// that share their first pages with other rows (a cached prefix) load them
+// without the hint, so that the sharers read them from the caches.
+template <bool STREAM>
 __device__ __forceinline__ void dec_dma16(const char* base, uint32_t voff, uint32_t lds) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(bs),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(bs),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(bs),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -419,10 +431,18 @@ __device__ __forceinline__ void dec_issue(const AttnArgs& a, const DecSrc& s, in
   const int row0 = kb & ((1 << a.p_shift) - 1);
   const size_t step_off = (((size_t)page << a.p_shift) + row0) * ln.slot_stride;
   const uint32_t lk = ln.lds + (uint32_t)(2 * SH::BUF * buf), lv = lk + SH::BUF;
+  if (s.cached) {
 #pragma unroll
-  for (int q = 0; q < SH::NQ; ++q) {
-    dec_dma16(s.kbase + step_off, ln.k_off[q], lk + 1024 * q);
-    dec_dma16(s.vbase + step_off, ln.v_off[q], lv + 1024 * q);
+    for (int q = 0; q < SH::NQ; ++q) {
+      dec_dma16<false>(s.kbase + step_off, ln.k_off[q], lk + 1024 * q);
+      dec_dma16<false>(s.vbase + step_off, ln.v_off[q], lv + 1024 * q);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < SH::NQ; ++q) {
+      dec_dma16<true>(s.kbase + step_off, ln.k_off[q], lk + 1024 * q);
+      dec_dma16<true>(s.vbase + step_off, ln.v_off[q], lv + 1024 * q);
+    }
   }
 }
 

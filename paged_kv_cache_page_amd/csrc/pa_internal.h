@@ -71,6 +71,12 @@ struct AttnArgs {
 //     so that a prefill item does not wait for a second load to learn them
 //   cut prefill items: cap_pf x (sequence, row tile, J, slot), merged by the
 //     prefill merge kernel after the tick
+// Bit of a decode row's sequence index in the plan's row list: set when the
+// row's first page is also the first page of another decode row of the tick
+// (a prefix shared through the page tables), so that its keys are loaded
+// into the caches, where the sharers find them; the other rows' keys are read
+// once and are loaded as a stream. The host bounds S below this bit.
+constexpr int kRowShared = 1 << 30;
 constexpr int kPlanLine = 32;  // ints per 128-byte cache line
 struct PlanOffsets {
   size_t rows, nparts, pbase, first_row, pf, pf_shape, merge, total;

@@ -17,7 +17,10 @@
 //                 partition size A = C = that size, so a chunk never spans
 //                 two rows and a row's partitions depend on the row alone.
 //                 A row of several partitions owns that many consecutive
-//                 split-KV partial slots;
+//                 split-KV partial slots. A row whose first page is also
+//                 another decode row's first page (a shared prefix, found
+//                 with a hash of the rows' first page ids) is marked so that
+//                 the decode kernels load its keys through the caches;
 //   prefill entries (sequence, row tile, piece) for every sequence with query
 //                 length > 1, ordered by decreasing number of key tiles, so that
 //                 the longest start first (longest-processing-time-first
@@ -46,6 +49,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 constexpr int kCostBins = 2048;     // key tiles of a prefill item, capped
+
+// Bin of a page id in the hash of the decode rows' first pages (multiplicative
+// hashing, top bits). Two rows in one bin count as sharing: a collision only
+// makes a row's loads cached instead of streamed.
+__device__ __forceinline__ int page_hash(int pg) {
+  static_assert(kCostBins == 2048, "11-bit hash");
+  return (int)(((uint32_t)pg * 2654435761u) >> 21);
+}
 
 // Inclusive prefix sum over the wave with DPP lane moves (no LDS round
 // trips): shifts by 1, 2, 4, 8 within each 16-lane row, then lane 15 of a row
@@ -184,34 +195,25 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   }
 
   // ---- pass 1: shapes, padded decode keys (the key axis fits an int: the
-  // caller's bounds are checked on the host) ----
+  // caller's bounds are checked on the host), and the decode rows' first
+  // pages counted in a hash of page ids (the bins array, not yet in use) ----
   int my_keys = 0;
   for (int s = lane; s < a.S; s += 64) {
+    // (the first block-table entry is read for every row, so that its load
+    // goes out with the shape's instead of after them)
+    const int fp = a.block_tables[(size_t)s * a.max_blocks];
     const SeqShape sh = seq_shape(a, s);
     if (s < kCachedSeqs) {
       s_L[s] = sh.L;
       s_n[s] = sh.n;
       s_q0[s] = sh.q0;
     }
-    if (sh.L == 1 && sh.n >= 1) my_keys += (sh.n + A - 1) / A * A;
+    if (sh.L == 1 && sh.n >= 1) {
+      my_keys += (sh.n + A - 1) / A * A;
+      atomicAdd(&s_hist[page_hash(fp)], 1);
+    }
   }
   const int total_keys = wave_sum32(my_keys);  // length of the decode key axis
-  wave_lds_sync();
-
-  // ---- prefill items: key tiles (histogram, sum, max) ----
-  long long my_tiles = 0;
-  int my_maxt = 0;
-  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
-    const int ntiles = (sh.L + TM - 1) / TM;
-    for (int mt = lane; mt < ntiles; mt += 64) {
-      const int t = item_tiles(sh, mt, TM);
-      atomicAdd(&s_hist[t], 1);
-      my_tiles += t;
-      my_maxt = max(my_maxt, t);
-    }
-  });
-  const long long item_tiles_all = wave_sum(my_tiles);  // per KV head
-  const int maxt = wave_max(my_maxt);
   wave_lds_sync();
 
   // ---- chunk size of the decode key axis: one chunk per decode wave of the
@@ -230,6 +232,71 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   int chunks = (int)((tk + (unsigned)C - 1u) / (unsigned)C);
   if (chunks > cap_dec) chunks = cap_dec;  // (never: the workspace query bounds the chunks)
   const int n_static = chunks < (int)waves ? chunks : (int)waves;
+
+  // ---- pass 2: decode rows, their offsets on the key axis, chunk starts,
+  // partial slots (rows of more than one partition) ----
+  int row_base = 0, off_base = 0, slot_base = 0;
+  for (int c0 = 0; c0 < a.S; c0 += 64) {
+    const int s = c0 + lane;
+    SeqShape sh{0, 0, 0};
+    int is_dec = 0, pad = 0, fp = 0;
+    if (s < a.S) {
+      fp = a.block_tables[(size_t)s * a.max_blocks];
+      sh = shape(s);
+      if (sh.L == 1 && sh.n >= 1) {
+        is_dec = 1;
+        pad = (sh.n + A - 1) / A * A;
+      }
+    }
+    int nrows, npad;
+    const int ri = row_base + wave_excl_scan(is_dec, &nrows);
+    const int off = off_base + wave_excl_scan(pad, &npad);
+    int np = 0, j0 = 0, j1 = -1;
+    if (is_dec) {
+      j0 = off / C;
+      j1 = (off + pad - 1) / C;
+      np = j1 - j0 + 1;
+    }
+    int nslots;
+    const int pb = slot_base + wave_excl_scan(np > 1 ? np : 0, &nslots);
+    if (is_dec) {
+      // the row's first page is read by another decode row too (bit 30 of
+      // the sequence index, which the host bounds below 2^30): its keys are
+      // loaded into the caches as usual, the others' as a stream
+      const int shared = s_hist[page_hash(fp)] > 1 ? kRowShared : 0;
+      dec_rows[ri] = make_int4(s | shared, off, sh.n, sh.q0);
+      nparts_of[ri] = np;
+      pbase_of[ri] = pb;
+      // chunks whose first key falls in this row start here
+      for (int j = (off + C - 1) / C; j <= j1; ++j)
+        if (j < cap_dec) first_row[j] = ri;
+    }
+    row_base += nrows;
+    off_base += npad;
+    slot_base += nslots;
+  }
+
+  // the bins are free again: zero them for the prefill items' tile counts
+  wave_lds_sync();
+  for (int i = lane; i < kCostBins / 4; i += 64)
+    reinterpret_cast<int4*>(s_hist)[i] = make_int4(0, 0, 0, 0);
+  wave_lds_sync();
+
+  // ---- prefill items: key tiles (histogram, sum, max) ----
+  long long my_tiles = 0;
+  int my_maxt = 0;
+  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
+    const int ntiles = (sh.L + TM - 1) / TM;
+    for (int mt = lane; mt < ntiles; mt += 64) {
+      const int t = item_tiles(sh, mt, TM);
+      atomicAdd(&s_hist[t], 1);
+      my_tiles += t;
+      my_maxt = max(my_maxt, t);
+    }
+  });
+  const long long item_tiles_all = wave_sum(my_tiles);  // per KV head
+  const int maxt = wave_max(my_maxt);
+  wave_lds_sync();
 
   // ---- piece length Tp: the mean tile count per prefill workgroup, but no
   // less than the time a decode wave spends on its chunk (items shorter than
@@ -256,44 +323,6 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
       }
       Tp *= 2;
     }
-  }
-
-  // ---- pass 2: decode rows, their offsets on the key axis, chunk starts,
-  // partial slots (rows of more than one partition) ----
-  int row_base = 0, off_base = 0, slot_base = 0;
-  for (int c0 = 0; c0 < a.S; c0 += 64) {
-    const int s = c0 + lane;
-    SeqShape sh{0, 0, 0};
-    int is_dec = 0, pad = 0;
-    if (s < a.S) {
-      sh = shape(s);
-      if (sh.L == 1 && sh.n >= 1) {
-        is_dec = 1;
-        pad = (sh.n + A - 1) / A * A;
-      }
-    }
-    int nrows, npad;
-    const int ri = row_base + wave_excl_scan(is_dec, &nrows);
-    const int off = off_base + wave_excl_scan(pad, &npad);
-    int np = 0, j0 = 0, j1 = -1;
-    if (is_dec) {
-      j0 = off / C;
-      j1 = (off + pad - 1) / C;
-      np = j1 - j0 + 1;
-    }
-    int nslots;
-    const int pb = slot_base + wave_excl_scan(np > 1 ? np : 0, &nslots);
-    if (is_dec) {
-      dec_rows[ri] = make_int4(s, off, sh.n, sh.q0);
-      nparts_of[ri] = np;
-      pbase_of[ri] = pb;
-      // chunks whose first key falls in this row start here
-      for (int j = (off + C - 1) / C; j <= j1; ++j)
-        if (j < cap_dec) first_row[j] = ri;
-    }
-    row_base += nrows;
-    off_base += npad;
-    slot_base += nslots;
   }
 
   // ---- entries per cost bin: piece j of an item of t tiles cut into J has

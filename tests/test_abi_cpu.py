@@ -72,6 +72,7 @@ def attn(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(Hq=6, Hkv=4), INVALID),
     (dict(S=-1), INVALID),
+    (dict(S=2 ** 30), INVALID),                    # the plan marks rows with bit 30
     (dict(T=-1), INVALID),
     (dict(Hkv=0), INVALID),
     (dict(num_pages=0), INVALID),
