@@ -129,23 +129,33 @@ __device__ __forceinline__ int item_tiles(const SeqShape& sh, int mt, int TM) {
 // Pieces of an item of t tiles for piece length Tp (1 = not cut).
 __device__ __forceinline__ int item_pieces(int t, int Tp) { return t > Tp ? (t + Tp - 1) / Tp : 1; }
 
-// Calls f(s, shape) for every prefill sequence, the whole wave together (its
-// lanes then go over the sequence's row tiles); sequences are found 64 at a
-// time with a ballot, so decode-only stretches cost one test per lane.
+// Calls f(s, shape, mt) for every prefill item (sequence s, row tile mt of TM
+// tokens), one item per lane: the sequences are taken 64 at a time, their
+// tile counts scanned over the wave, and then each lane of an item finds its
+// sequence by a binary search over the lanes' first item indices (shuffles,
+// no LDS), so a wave pass covers up to 64 items of any sequences. Lanes past
+// the last item of a pass get no call.
 template <typename Shape, typename F>
-__device__ __forceinline__ void for_prefill_seqs(int S, Shape&& shape, F&& f) {
+__device__ __forceinline__ void for_prefill_items(int S, int TM, Shape&& shape, F&& f) {
   const int lane = threadIdx.x & 63;
   for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
     SeqShape sh{0, 0, 0};
     if (s < S) sh = shape(s);
-    unsigned long long m = __ballot(s < S && is_prefill(sh));
-    while (m) {
-      const int i = __builtin_ctzll(m);
-      m &= m - 1;
-      const SeqShape u{__builtin_amdgcn_readlane(sh.L, i), __builtin_amdgcn_readlane(sh.n, i),
-                       __builtin_amdgcn_readlane(sh.q0, i)};
-      f(c0 + i, u);
+    const int nt = (s < S && is_prefill(sh)) ? (sh.L + TM - 1) / TM : 0;
+    int total;
+    const int first = wave_excl_scan(nt, &total);  // first item of the lane's sequence
+    for (int b0 = 0; b0 < total; b0 += 64) {
+      const int item = b0 + lane;
+      // the last lane whose sequence starts at or before this item (it holds
+      // tiles: a lane without tiles shares its first index with the next lane)
+      int k = 0;
+#pragma unroll
+      for (int step = 32; step >= 1; step >>= 1)
+        if (k + step < 64 && __shfl(first, k + step) <= item) k += step;
+      const SeqShape u{__shfl(sh.L, k), __shfl(sh.n, k), __shfl(sh.q0, k)};
+      const int mt = item - __shfl(first, k);
+      if (item < total) f(c0 + k, u, mt);
     }
   }
 }
@@ -285,14 +295,11 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   // ---- prefill items: key tiles (histogram, sum, max) ----
   long long my_tiles = 0;
   int my_maxt = 0;
-  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
-    const int ntiles = (sh.L + TM - 1) / TM;
-    for (int mt = lane; mt < ntiles; mt += 64) {
-      const int t = item_tiles(sh, mt, TM);
-      atomicAdd(&s_hist[t], 1);
-      my_tiles += t;
-      my_maxt = max(my_maxt, t);
-    }
+  for_prefill_items(a.S, TM, shape, [&](int, const SeqShape& sh, int mt) {
+    const int t = item_tiles(sh, mt, TM);
+    atomicAdd(&s_hist[t], 1);
+    my_tiles += t;
+    my_maxt = max(my_maxt, t);
   });
   const long long item_tiles_all = wave_sum(my_tiles);  // per KV head
   const int maxt = wave_max(my_maxt);
@@ -331,12 +338,9 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   if (Tp < maxt) {
     for (int b = lane; b <= maxt; b += 64) s_hist[b] = 0;
     wave_lds_sync();
-    for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
-      const int ntiles = (sh.L + TM - 1) / TM;
-      for (int mt = lane; mt < ntiles; mt += 64) {
-        const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
-        for (int j = 0; j < J; ++j) atomicAdd(&s_hist[(j + 1) * t / J - j * t / J], 1);
-      }
+    for_prefill_items(a.S, TM, shape, [&](int, const SeqShape& sh, int mt) {
+      const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
+      for (int j = 0; j < J; ++j) atomicAdd(&s_hist[(j + 1) * t / J - j * t / J], 1);
     });
     wave_lds_sync();
   }
@@ -356,22 +360,19 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
 
   // ---- scatter the prefill entries into their bins; a cut item takes
   // J * Hkv partial slots ----
-  for_prefill_seqs(a.S, shape, [&](int s, const SeqShape& sh) {
-    const int ntiles = (sh.L + TM - 1) / TM;
-    for (int mt = lane; mt < ntiles; mt += 64) {
-      const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
-      int slot = 0;
-      if (J > 1) {
-        slot = atomicAdd(&s_slot_next, J * a.Hkv);
-        const int m = atomicAdd(&s_merge_next, 1);
-        if (m < cap_pf) merge_items[m] = make_int4(s, mt, J, slot);
-      }
-      for (int j = 0; j < J; ++j) {
-        const int idx = atomicAdd(&s_cur[(j + 1) * t / J - j * t / J], 1);
-        if (idx < cap_pf) {
-          pf_items[idx] = make_int4(s, mt, j | (J << 16), slot);
-          pf_shapes[idx] = make_int4(sh.q0, sh.L, sh.n, 0);
-        }
+  for_prefill_items(a.S, TM, shape, [&](int s, const SeqShape& sh, int mt) {
+    const int t = item_tiles(sh, mt, TM), J = item_pieces(t, Tp);
+    int slot = 0;
+    if (J > 1) {
+      slot = atomicAdd(&s_slot_next, J * a.Hkv);
+      const int m = atomicAdd(&s_merge_next, 1);
+      if (m < cap_pf) merge_items[m] = make_int4(s, mt, J, slot);
+    }
+    for (int j = 0; j < J; ++j) {
+      const int idx = atomicAdd(&s_cur[(j + 1) * t / J - j * t / J], 1);
+      if (idx < cap_pf) {
+        pf_items[idx] = make_int4(s, mt, j | (J << 16), slot);
+        pf_shapes[idx] = make_int4(sh.q0, sh.L, sh.n, 0);
       }
     }
   });
