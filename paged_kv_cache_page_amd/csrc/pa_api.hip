@@ -608,9 +608,6 @@ pa_status_t attention_setup(const void* q, const void* k_pool, const void* v_poo
   a.pf_workers = (!wl.token_mode && wl.cap_pf > 0) ? tick_grid(dtype, head_dim, G) : 1;
   // not a fused tick unless pa_tick_forward says so
   a.fused = 0;
-  a.k_new = nullptr;
-  a.v_new = nullptr;
-  a.positions = nullptr;
   a.cos_sin = nullptr;
   a.max_pos = 0;
 
@@ -724,17 +721,14 @@ pa_status_t tick_forward_impl(void* q, void* k, const void* v, const int32_t* po
 
   // One launch for the slot mapping, the page write and (seq mode) the plan,
   // which reads only query_start_loc and seq_lens; then the attention kernels.
-  // bf16 ticks are fused: the first launch writes only the prefill chunks'
-  // pages (and the slots and the plan), the attention kernels rotate the query
-  // rows they read and write the decode rows' pages themselves, and q and k
-  // are left as given.
+  // bf16 ticks are fused: the first launch writes every token's rotated K and
+  // its V into their slots and each decode row's rotated query into its output
+  // row (where the decode kernel reads it), the prefill items rotate their
+  // query rows where they read them, and q and k are left as given.
   const bool plan = !c.empty && !c.wl.token_mode;
   const bool fused = plan && dtype == PA_BF16;
   if (fused) {
     c.a.fused = 1;
-    c.a.k_new = k;
-    c.a.v_new = v;
-    c.a.positions = positions;
     c.a.cos_sin = cos_sin;
     c.a.max_pos = max_pos;
   }

@@ -35,14 +35,12 @@ struct AttnArgs {
   float* pf_ws;         // partials: o [pf_slots][kPrefillRows][D], then (m, l) [pf_slots][kPrefillRows]
   int32_t pf_slots;     // partial slots (0 = never split)
   int32_t pf_workers;   // workgroups of the kernel that runs the prefill items
-  // The fused tick (bf16): the attention kernels rotate every query row they
-  // read (q is the unrotated input), and the wave that holds a decode row's
-  // last keys rotates that row's new key, writes its K/V page slot and uses
-  // the new rows from registers. Null / 0 otherwise.
+  // The fused tick (bf16): q is the unrotated input. The prefill items rotate
+  // each query row where they read it (row i of a chunk of L rows over n keys
+  // at position n - L + i); the decode kernel reads a decode row's query,
+  // rotated by the page-write launch, from the row's output row. 0 / null
+  // otherwise.
   int32_t fused;
-  const void* k_new;          // [T, Hkv, D] this tick's K rows, unrotated
-  const void* v_new;          // [T, Hkv, D] this tick's V rows
-  const int32_t* positions;   // [T]
   const float* cos_sin;       // [max_pos, D] or null (no RoPE)
   int32_t max_pos;
 };
