@@ -434,10 +434,22 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
   const int tb = pj * ntiles / pJ, te = (pj + 1) * ntiles / pJ;  // this piece's tiles
   const int last_key = n - L;           // row i sees keys <= last_key + i
 
-  // The wave's two 16-row blocks: rows 32 wave + 16 b + col.
+  // The wave's two 16-row blocks: rows 32 wave + 16 b + col. Every global
+  // load of the item's set-up goes out before any of them is used: the query
+  // rows, their cos/sin rows and the first page ids, so that the set-up waits
+  // for one round trip to memory rather than one per step (behind a decode
+  // stream sharing the GPU, a round trip takes microseconds).
   uint4 qop[2][DSTEPS];
   int tok[2], head[2], limit[2], min_limit[2];
   bool row_ok[2];
+  // the fused tick's q is the unrotated input: the lane's dims grp * 8 + 32 ds
+  // (pairs ds, ds + DSTEPS / 2) are rotated at the row's position, exactly as
+  // the page writer rotates a stored key. Row i of a chunk of L rows over n
+  // keys is the token at position n - L + i (the tick's rows are the
+  // sequence's last keys), so the cos/sin loads need no load of the position.
+  const bool rope = a.fused && a.cos_sin && a.max_pos > 0;
+  float rc[2][DSTEPS / 2][8], rs[2][DSTEPS / 2][8];
+  bool rope_ok[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int r0 = wave * kRowsPerWave + 16 * b;
@@ -453,22 +465,24 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
 #pragma unroll
     for (int ds = 0; ds < DSTEPS; ++ds)
       qop[b][ds] = *reinterpret_cast<const uint4*>(qrow + (ds * 32 + grp * 8) * 2);
-    if (a.fused && a.cos_sin) {
-      // the fused tick's q is the unrotated input: rotate the lane's dims
-      // grp * 8 + 32 ds (pairs ds, ds + DSTEPS / 2) at the row's position,
-      // exactly as the page writer rotates a stored key. Row i of a chunk of
-      // L rows over n keys is the token at position n - L + i (the tick's
-      // rows are the sequence's last keys), so the cos/sin loads go out with
-      // the query loads instead of after a load of the position.
-      const int pos = last_key + tq;
-      if (pos >= 0 && pos < a.max_pos) {
+    const int pos = last_key + tq;
+    rope_ok[b] = pos >= 0 && pos < a.max_pos;  // (other rows stay as given)
+    if (rope) {
+      const int pc = clampi(pos, 0, a.max_pos - 1);
 #pragma unroll
-        for (int ds = 0; ds < DSTEPS / 2; ++ds) {
-          float c[8], sn[8];
-          rope_load8(a.cos_sin, D, pos, grp * 8 + 32 * ds, c, sn);
-          rope_bf16x8(qop[b][ds], qop[b][ds + DSTEPS / 2], c, sn);
-        }
-      }
+      for (int ds = 0; ds < DSTEPS / 2; ++ds)
+        rope_load8(a.cos_sin, D, pc, grp * 8 + 32 * ds, rc[b][ds], rs[b][ds]);
+    }
+  }
+  const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
+  const int npg = min((kmax + (1 << p_shift) - 1) >> p_shift, kItemPages);
+  const int pg_first = tid < npg ? clampi(bt_row[tid], 0, a.num_pages - 1) : 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (rope && rope_ok[b]) {
+#pragma unroll
+      for (int ds = 0; ds < DSTEPS / 2; ++ds)
+        rope_bf16x8(qop[b][ds], qop[b][ds + DSTEPS / 2], rc[b][ds], rs[b][ds]);
     }
 #pragma unroll
     for (int ds = 0; ds < DSTEPS; ++ds) qop[b][ds] = keep_if(qop[b][ds], row_ok[b]);
@@ -484,12 +498,13 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, PfSmem<D>& sm, i
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) acc_o[b][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
   const char* kpool = (const char*)a.k_pool + (size_t)kvh * row_bytes;
   const char* vpool = (const char*)a.v_pool + (size_t)kvh * row_bytes;
 
-  const int npg = min((kmax + (1 << p_shift) - 1) >> p_shift, kItemPages);
-  for (int i = tid; i < npg; i += kPfThreads) sm.pt[i] = clampi(bt_row[i], 0, a.num_pages - 1);
+  // the sequence's page ids into LDS (the first kPfThreads loaded above)
+  if (tid < npg) sm.pt[tid] = pg_first;
+  for (int i = tid + kPfThreads; i < npg; i += kPfThreads)
+    sm.pt[i] = clampi(bt_row[i], 0, a.num_pages - 1);
   __syncthreads();
 
   // A ring of kPfStages LDS stages: the loads of the next kPfStages - 1 tiles
