@@ -197,7 +197,7 @@ size_t pa_paged_attention_workspace_size(int32_t S, int32_t T, int32_t Hq, int32
  * to nearest-even into the storage dtype.
  *
  * Host scalars: max_query_len >= every L and max_seq_len >= every n (they
- * size the grids; rows beyond them are not computed). S < 2^30 (else
+ * size the grids; rows beyond them are not computed). S < 2^29 (else
  * PA_ERR_INVALID_ARG). Sequences with L = 0 produce nothing. kv_split_tokens: keys per split-KV partition of a decode
  * row (0 = library default; otherwise a multiple of 16 in [16, 65536]).
  * workspace: device scratch of at least
@@ -211,6 +211,17 @@ size_t pa_paged_attention_workspace_size(int32_t S, int32_t T, int32_t Hq, int32
  * first page (a prefix shared through the page tables: Helios blog, "Prefix
  * caching"), whose keys are loaded into the caches for the other sharers.
  * This changes no result.
+ * Shared prefixes read once (bf16, kv_split_tokens = 0, S <= 64): decode
+ * rows whose page tables start with the same pages as the lowest-indexed
+ * decode row holding that first page (their common leading pages, short of
+ * the page with a row's last key) are gathered, up to 16 / (Hq / Hkv) rows
+ * at a time, and each such group reads those pages once for all its rows;
+ * each row's remaining keys are its own split-KV partitions, and the merge
+ * sums both (same section: a cached prefix is not recomputed, and here not
+ * re-read either). Results are those of the split-KV merge over a different
+ * cut of the key axis: equal within rounding, not bit for bit, to the
+ * ungrouped call. When the partial results of the groups would not fit the
+ * workspace the call does not group.
  */
 pa_status_t pa_paged_attention_varlen(const void* q, const void* k_pool, const void* v_pool,
                                       const int32_t* block_tables, const int32_t* seq_lens,

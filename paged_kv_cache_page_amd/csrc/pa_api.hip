@@ -193,7 +193,12 @@ WsLayout workspace_layout(int S, int T, int Hq, int D, int max_query_len, int ma
       const long by_cap = (keys + split_max(P) - 1) / split_max(P);
       const long chunks = waves > by_cap ? waves : by_cap;
       if (chunks < w.cap_dec) w.cap_dec = chunks;
-      if ((long)S + chunks < w.part_slots) w.part_slots = (long)S + chunks;
+      // (bf16: room for grouped rows of a shared prefix, whose members also
+      // hold partials of their group row's partitions; the plan groups rows
+      // only while their partials fit)
+      const long group_room = dt == PA_BF16 ? kGroupSlotsPerRow * (long)S : 0;
+      if ((long)S + chunks + group_room < w.part_slots)
+        w.part_slots = (long)S + chunks + group_room;
     }
     if (max_query_len > 1) {
       // a tile holds at least kPrefillRows / 8 tokens (the largest supported group is 8)
@@ -389,7 +394,7 @@ using namespace pa;
 #pragma GCC visibility push(default)
 extern "C" {
 
-int32_t pa_abi_version(void) { return 6; }
+int32_t pa_abi_version(void) { return 7; }
 
 void pa_set_validation(int32_t on) { g_validate.store(on ? 1 : 0, std::memory_order_relaxed); }
 
@@ -530,7 +535,7 @@ pa_status_t attention_setup(const void* q, const void* k_pool, const void* v_poo
                             size_t workspace_bytes, AttnCall& c) {
   c.empty = false;
   c.dtype = dtype;
-  if (!dtype_ok(dtype) || S < 0 || S >= kRowShared || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
+  if (!dtype_ok(dtype) || S < 0 || S >= kRowGroup || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
       head_dim < 1 || page_size < 1 || num_pages < 1 || max_blocks_per_seq < 1 ||
       max_query_len < 0 || max_seq_len < 0 || !isfinite(scale))
     return PA_ERR_INVALID_ARG;
@@ -606,6 +611,13 @@ pa_status_t attention_setup(const void* q, const void* k_pool, const void* v_poo
   a.pf_slots = wl.pf_slots;
   a.pf_ws = (float*)((char*)workspace + wl.plan_bytes + wl.partial_bytes);
   a.pf_workers = (!wl.token_mode && wl.cap_pf > 0) ? tick_grid(dtype, head_dim, G) : 1;
+  // rows sharing a prefix are grouped on the bf16 matrix-core decode path,
+  // with automatic partitions (a fixed partition size keeps a row's
+  // partitions a function of the row alone) and a merge launch
+  a.group_rows = (dtype == PA_BF16 && !wl.token_mode && a.part_tokens == 0 && a.max_parts > 1 &&
+                  decode_supported(dtype, head_dim, G))
+                     ? 1
+                     : 0;
   // not a fused tick unless pa_tick_forward says so
   a.fused = 0;
   a.cos_sin = nullptr;

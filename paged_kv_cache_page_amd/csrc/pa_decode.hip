@@ -509,7 +509,7 @@ hipError_t launch_decode(pa_dtype_t dt, const AttnArgs& a, bool token_mode, hipS
 
 hipError_t launch_split_reduce(pa_dtype_t dt, const AttnArgs& a, bool token_mode,
                                hipStream_t s) {
-  const long rows = token_mode ? a.T : a.S;
+  const long rows = token_mode ? a.T : plan_rows(a.S);
   const long threads = rows * a.Hq * (a.D / 4) * kMergeLanes;
   if (threads == 0 || a.max_parts <= 1) return hipSuccess;
   const unsigned blocks = (unsigned)((threads + 255) / 256);

@@ -77,7 +77,7 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
   const long rh = idx / quads;
   const int h = (int)(rh % a.Hq);
   const long row = rh / a.Hq;
-  if (row >= (TOKEN_MODE ? a.T : a.S)) return;
+  if (row >= (TOKEN_MODE ? (long)a.T : plan_rows(a.S))) return;
   int nparts, token;
   size_t slot0;  // partial slot of part 0
   if constexpr (TOKEN_MODE) {
@@ -158,6 +158,8 @@ __device__ __forceinline__ void split_reduce_task(const AttnArgs& a, long idx) {
 struct DecSeg {
   int seq, token, pslot, kbeg, kend, part, nparts, kvh;
   int cached = 0;  // the row's keys go through the caches (a shared prefix)
+  int group = 0;   // a group row: its members (rows grow + 1 .. grow + group)
+  int grow = 0;
 };
 
 // Walk of decode wave gw = 4 wg + wave over the chunks of the decode key axis
@@ -173,6 +175,8 @@ struct DecodeCursor {
   const int* first_row;   // first row of each chunk
   const int* nparts_of;   // partitions per row
   const int* pbase_of;    // first partial slot per row
+  const int* kstart_of;   // first key per row
+  const int* part0_of;    // first partition index per row
   int* counter;           // claimed items
   int n_rows, C, n_chunks, n_static, n_items, A, Hkv, kvh, chunk, i;
   int claim;   // item claimed ahead (lane 0)
@@ -203,6 +207,8 @@ struct DecodeCursor {
     first_row = a.plan + po.first_row;
     nparts_of = a.plan + po.nparts;
     pbase_of = a.plan + po.pbase;
+    kstart_of = a.plan + po.kstart;
+    part0_of = a.plan + po.part0;
     counter = a.plan + plan_dec_cursor(a.Hq);
     n_rows = a.plan[0];
     C = a.plan[2];
@@ -233,17 +239,19 @@ struct DecodeCursor {
       }
       if (chunk >= n_chunks) return false;
       const int4 r = rows[i];
-      const int np = nparts_of[i], pb = pbase_of[i];
-      const int off = r.y, n = r.z;
+      const int np = nparts_of[i], pb = pbase_of[i], k0 = kstart_of[i], p0 = part0_of[i];
+      const int off = r.y, n = r.z;  // the row's keys: [k0, k0 + n) of the sequence
       const int pad = (n + A - 1) / A * A;
       const int c0 = chunk * C, c1 = c0 + C;
-      d.seq = r.x & (kRowShared - 1);
+      d.seq = r.x & (kRowGroup - 1);
       d.cached = (r.x & kRowShared) != 0;
+      d.group = (r.x & kRowGroup) ? r.w : 0;
+      d.grow = i;
       d.token = r.w;
       d.pslot = pb;
-      d.kbeg = max(c0, off) - off;
-      d.kend = min(min(c1, off + pad) - off, n);
-      d.part = chunk - off / C;
+      d.kbeg = max(c0, off) - off + k0;
+      d.kend = min(min(c1, off + pad) - off, n) + k0;
+      d.part = chunk - off / C + p0;
       d.nparts = np;
       d.kvh = kvh;
       if (off + pad >= c1 || i + 1 >= n_rows)  // the chunk ends in this row
@@ -548,6 +556,7 @@ __device__ __forceinline__ float lane_sum_xor(float x) {
 template <int D, int G>
 struct DecPre {
   int page_raw;
+  int mslot;  // a group row: the first partial slot of this lane's member
   uint4 qb[MfmaDecodeShape<D, G>::KSTEPS];
 };
 
@@ -560,14 +569,25 @@ __device__ __forceinline__ DecPre<D, G> decode_prefetch(const AttnArgs& a, const
   const int pg0 = d.kbeg >> a.p_shift;
   const int npg = ((d.kend - 1) >> a.p_shift) - pg0 + 1;
   const int* bt_row = a.block_tables + (size_t)d.seq * a.max_blocks;
-  p.page_raw = bt_row[pg0 + (lane < npg ? lane : 0)];
+  p.page_raw = bt_row[min(pg0 + (lane < npg ? lane : 0), a.max_blocks - 1)];
   const size_t row_bytes = (size_t)SH::ROWB;
   // the fused tick's page-write launch left the row's rotated query in its
   // output row (q itself is the unrotated input); that row's result is written
   // only once every range of the row has read it
   const char* qbase = a.fused ? (const char*)a.out : (const char*)a.q;
-  const char* qrow = qbase + ((size_t)d.token * a.Hq + (size_t)d.kvh * G) * row_bytes;
-  const int hq = col < G ? col : 0;
+  // column col of the score product: head col of the row; in a group row,
+  // head col % G of member col / G (its own query row)
+  int token = d.token, hq = col < G ? col : 0;
+  p.mslot = 0;
+  if (d.group > 0) {
+    const PlanOffsets po = plan_offsets(a.S, a.Hq, a.cap_dec, a.cap_pf);
+    const int m = min(d.grow + 1 + min(col / G, d.group - 1), (int)plan_rows(a.S) - 1);
+    token = reinterpret_cast<const int4*>(a.plan + po.rows)[m].w;
+    p.mslot = a.plan[po.pbase + m];
+    hq = col % G;
+  }
+  token = min(max(token, 0), a.T - 1);
+  const char* qrow = qbase + ((size_t)token * a.Hq + (size_t)d.kvh * G) * row_bytes;
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)
     p.qb[ks] = *reinterpret_cast<const uint4*>(qrow + hq * row_bytes + 16 * rrow + 64 * ks);
@@ -591,11 +611,13 @@ __device__ __forceinline__ int decode_range(const AttnArgs& a, int buf0, const D
   // Q^T operand, zero in the lanes of heads >= G. Its loads (and the page ids)
   // were issued with the previous range: they are waited for here, before the
   // next buffer's loads are issued, so that wait does not include those.
+  // (a group row's columns: G per member)
+  const int ncol = d.group > 0 ? d.group * G : G;
   uint4 qb[SH::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < SH::KSTEPS; ++ks)
-    qb[ks] = col < G ? pre.qb[ks] : make_uint4(0u, 0u, 0u, 0u);
-  const float bias = col < G ? 0.f : -INFINITY;
+    qb[ks] = col < ncol ? pre.qb[ks] : make_uint4(0u, 0u, 0u, 0u);
+  const float bias = col < ncol ? 0.f : -INFINITY;
   __builtin_amdgcn_sched_barrier(0);
 
   float m_run = kNegBig, l_part = 0.f;
@@ -623,10 +645,24 @@ __device__ __forceinline__ int decode_range(const AttnArgs& a, int buf0, const D
   // of head col.
   float l = lane_sum_xor<16>(l_part);
   l = lane_sum_xor<32>(l);
-  if (col < G) {
+  if (col < ncol) {
     const size_t row_bytes = (size_t)SH::ROWB;
-    const int hq = d.kvh * G + col;
-    if (d.nparts == 1) {
+    const int hq = d.kvh * G + (d.group > 0 ? col % G : col);
+    if (d.group > 0) {
+      // partition part of the group row: a partial of this lane's member
+      // (the plan keeps every member's slots inside the workspace)
+      if (pre.mslot + d.part >= a.part_slots) return buf;
+      const size_t pi = ((size_t)pre.mslot + d.part) * a.Hq + hq;
+      float* po = a.ws + pi * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<float4*>(po + 16 * db + 4 * rrow) =
+            make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+      if (rrow == 0) {
+        float* ml = a.ws + (size_t)a.part_slots * a.Hq * D;
+        *reinterpret_cast<float2*>(ml + 2 * pi) = make_float2(m_run, l);
+      }
+    } else if (d.nparts == 1) {
       const float inv = 1.f / l;
       char* orow = (char*)a.out + ((size_t)d.token * a.Hq + hq) * row_bytes;
 #pragma unroll

@@ -43,6 +43,9 @@ struct AttnArgs {
   int32_t fused;
   const float* cos_sin;       // [max_pos, D] or null (no RoPE)
   int32_t max_pos;
+  // Decode rows sharing a prefix may be grouped (the bf16 matrix-core decode
+  // walks group rows; the other decode paths do not): 1 / 0.
+  int32_t group_rows;
 };
 
 // Plan layout, in ints from the start of the workspace:
@@ -55,10 +58,20 @@ struct AttnArgs {
 //     queue of KV head h at kPlanLine * (1 + h); then the counter of the
 //     claimed decode chunks on line 1 + Hq. All zeroed by the plan kernel,
 //     advanced with device-scope atomics
-//   decode rows: S x (sequence, key offset, keys, token); row i's keys occupy
-//     [offset, offset + round_up(keys, A)) of the concatenated key axis
-//   partitions per decode row: S ints
-//   first partial slot per decode row: S ints (rows of one partition own none)
+//   decode rows: plan_rows(S) x (sequence, key offset, keys, token); row i's
+//     keys occupy [offset, offset + round_up(keys, A)) of the concatenated key
+//     axis and are the sequence's keys [kstart, kstart + keys). A group row
+//     (kRowGroup) is the shared prefix of m sharing rows, which follow it in
+//     the list: its sequence is one whose page table holds the prefix, its
+//     token field is m, and each of its partitions writes one partial per
+//     member (partition p of the group row at the member's slot base + p)
+//   partitions per decode row: plan_rows(S) ints (0 for a group row, which
+//     the merge skips; a member counts the group row's partitions too)
+//   first partial slot per decode row: plan_rows(S) ints (rows of one
+//     partition own none)
+//   first key per decode row (kstart): plan_rows(S) ints
+//   first partition index per decode row: plan_rows(S) ints (a member's own
+//     partitions follow its group row's)
 //   first decode row of each chunk: cap_dec ints
 //   prefill entries (16-byte aligned): cap_pf x (sequence, row tile,
 //     piece j | pieces J << 16, first partial slot), in decreasing cost order;
@@ -69,22 +82,32 @@ struct AttnArgs {
 //     so that a prefill item does not wait for a second load to learn them
 //   cut prefill items: cap_pf x (sequence, row tile, J, slot), merged by the
 //     prefill merge kernel after the tick
-// Bit of a decode row's sequence index in the plan's row list: set when the
-// row's first page is also the first page of another decode row of the tick
-// (a prefix shared through the page tables), so that its keys are loaded
-// into the caches, where the sharers find them; the other rows' keys are read
-// once and are loaded as a stream. The host bounds S below this bit.
+// Bits of a decode row's sequence index in the plan's row list. kRowShared:
+// the row's keys are read by other rows too (a prefix shared through the
+// page tables), so they are loaded into the caches, where the sharers find
+// them; the other rows' keys are read once and are loaded as a stream.
+// kRowGroup: a group row (above). The host bounds S below both bits.
 constexpr int kRowShared = 1 << 30;
+constexpr int kRowGroup = 1 << 29;
 constexpr int kPlanLine = 32;  // ints per 128-byte cache line
+// Rows of the decode row list: the decode rows, and at most one group row
+// per two of them.
+__host__ __device__ inline long plan_rows(long S) { return S + S / 2 + 1; }
+// Partial slots per decode row reserved for group members (bf16, automatic
+// partitions).
+constexpr long kGroupSlotsPerRow = 4;
 struct PlanOffsets {
-  size_t rows, nparts, pbase, first_row, pf, pf_shape, merge, total;
+  size_t rows, nparts, pbase, kstart, part0, first_row, pf, pf_shape, merge, total;
 };
 __host__ __device__ inline PlanOffsets plan_offsets(long S, long Hq, long cap_dec, long cap_pf) {
   PlanOffsets o;
+  const size_t R = (size_t)plan_rows(S);
   o.rows = (size_t)kPlanLine * (2 + (size_t)Hq);
-  o.nparts = o.rows + 4 * (size_t)S;
-  o.pbase = o.nparts + (size_t)S;
-  o.first_row = o.pbase + (size_t)S;
+  o.nparts = o.rows + 4 * R;
+  o.pbase = o.nparts + R;
+  o.kstart = o.pbase + R;
+  o.part0 = o.kstart + R;
+  o.first_row = o.part0 + R;
   o.pf = (o.first_row + (size_t)cap_dec + 3) / 4 * 4;
   o.pf_shape = o.pf + 4 * (size_t)cap_pf;
   o.merge = o.pf_shape + 4 * (size_t)cap_pf;

@@ -49,6 +49,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 constexpr int kCostBins = 2048;     // key tiles of a prefill item, capped
+// Leading pages compared when grouping rows by a shared prefix.
+constexpr int kGroupMaxPages = 1024;
+constexpr int kGroupFirstPages = 16;  // of them, read with the rows' shapes
 
 // Bin of a page id in the hash of the decode rows' first pages (multiplicative
 // hashing, top bits). Two rows in one bin count as sharing: a collision only
@@ -97,6 +100,20 @@ __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
   return v;
+}
+
+// For each lane with `on`, the mask of the lanes with `on` holding the same
+// value v (0 for the others): one round per distinct value, each taking the
+// value of the lowest lane still unmatched.
+__device__ __forceinline__ unsigned long long wave_match(int v, bool on) {
+  unsigned long long todo = __ballot(on), mine = 0;
+  while (todo != 0) {
+    const int u = __builtin_amdgcn_readlane(v, __ffsll((long long)todo) - 1);
+    const unsigned long long m = __ballot(on && v == u);
+    if (on && v == u) mine = m;
+    todo &= ~m;
+  }
+  return mine;
 }
 
 struct SeqShape {
@@ -166,6 +183,7 @@ template <int NC>
 struct alignas(16) PlanLds {
   int hist[kCostBins];
   int L[NC], n[NC], q0[NC];
+  int grp[4][64];  // per-lane values of the decode row groups (one wave pass)
   int slot_next, merge_next;
 };
 
@@ -208,22 +226,41 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   // caller's bounds are checked on the host), and the decode rows' first
   // pages counted in a hash of page ids (the bins array, not yet in use) ----
   int my_keys = 0;
+  int fp0 = 0;  // (at most 64 sequences) the lane's sequence: first page and shape
+  SeqShape sh0{0, 0, 0};
+  // Rows may be grouped by a shared prefix (below): then the lane's first
+  // kGroupFirstPages page ids are read here too, beside the shape's loads
+  const int Gq = a.Hq / a.Hkv;
+  const int Rmax = Gq > 0 ? 16 / Gq : 0;  // a power of two: G divides 16
+  const bool may_group = a.group_rows && a.part_tokens == 0 && a.S <= 64 && Rmax >= 2;
+  int bt0[kGroupFirstPages];
+#pragma unroll
+  for (int j = 0; j < kGroupFirstPages; ++j) bt0[j] = -1;
   for (int s = lane; s < a.S; s += 64) {
     // (the first block-table entry is read for every row, so that its load
     // goes out with the shape's instead of after them)
-    const int fp = a.block_tables[(size_t)s * a.max_blocks];
+    const int* bt = a.block_tables + (size_t)s * a.max_blocks;
+    const int fp = bt[0];
+    if (may_group) {
+#pragma unroll
+      for (int j = 0; j < kGroupFirstPages; ++j) bt0[j] = j < a.max_blocks ? bt[j] : -1;
+    }
     const SeqShape sh = seq_shape(a, s);
     if (s < kCachedSeqs) {
       s_L[s] = sh.L;
       s_n[s] = sh.n;
       s_q0[s] = sh.q0;
     }
+    if (s == lane) {
+      fp0 = fp;
+      sh0 = sh;
+    }
     if (sh.L == 1 && sh.n >= 1) {
       my_keys += (sh.n + A - 1) / A * A;
       atomicAdd(&s_hist[page_hash(fp)], 1);
     }
   }
-  const int total_keys = wave_sum32(my_keys);  // length of the decode key axis
+  int total_keys = wave_sum32(my_keys);  // length of the decode key axis
   wave_lds_sync();
 
   // ---- chunk size of the decode key axis: one chunk per decode wave of the
@@ -231,21 +268,184 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
   // or chunks capped at the largest partition) are claimed from a counter ----
   // (32-bit unsigned divisions: the 64-bit ones are long software routines)
   const unsigned waves = (unsigned)max(1, a.dec_grid * 4 / a.Hkv);
-  const unsigned tk = (unsigned)total_keys;
-  const unsigned dec_share = (tk + waves - 1u) / waves;  // keys per decode wave (no overflow)
-  int C = a.part_tokens;
-  if (C <= 0) {
-    const unsigned c = (dec_share + 15u) / 16u * 16u;
-    C = (int)(c < (unsigned)a.part_min ? (unsigned)a.part_min
-                                       : (c > (unsigned)a.part_max ? (unsigned)a.part_max : c));
+  int C = 0, chunks = 0;
+  unsigned dec_share = 0;  // keys per decode wave
+  auto chunking = [&](int tkeys) {
+    const unsigned tk = (unsigned)tkeys;
+    dec_share = (tk + waves - 1u) / waves;  // (no overflow)
+    C = a.part_tokens;
+    if (C <= 0) {
+      const unsigned c = (dec_share + 15u) / 16u * 16u;
+      C = (int)(c < (unsigned)a.part_min ? (unsigned)a.part_min
+                                         : (c > (unsigned)a.part_max ? (unsigned)a.part_max : c));
+    }
+    chunks = (int)((tk + (unsigned)C - 1u) / (unsigned)C);
+    if (chunks > cap_dec) chunks = cap_dec;  // (never: the workspace query bounds the chunks)
+  };
+  // partitions of the axis range [o, o + len)
+  auto parts = [&](int o, int len) { return (o + len - 1) / C - o / C + 1; };
+  int* kstart_of = plan + po.kstart;
+  int* part0_of = plan + po.part0;
+  // chunks whose first key falls in axis range [o, o + len) start in row ri
+  auto chunk_starts = [&](int o, int len, int ri) {
+    for (int j = (o + C - 1) / C; j <= (o + len - 1) / C; ++j)
+      if (j < cap_dec) first_row[j] = ri;
+  };
+
+  // ---- decode rows grouped by a shared prefix (bf16 matrix-core decode,
+  // automatic partitions, at most 64 sequences: one lane per sequence) ----
+  // A decode row whose first page id is another decode row's (the hash bins
+  // above, confirmed on the ids) shares a prefix with the one of smallest
+  // index among them, its leader: the leading pages on which their page
+  // tables agree, but no page holding the row's last key. The rows of one
+  // leader and one prefix length are cut, in lane order, into groups of at
+  // most 16 / G rows (the columns of one score product). A group of two or
+  // more rows reads the prefix once: a group row, laid before its members'
+  // rows, whose every partition gives one partial per member; each member's
+  // own row then covers its keys after the prefix, and the merge sums both.
+  // The leader itself keeps its whole row (loaded through the caches).
+  // Layout on the key axis, in lane order of the units: an ungrouped row is
+  // one unit; a group (at its first member's lane) is the group row's prefix
+  // keys, then each member's keys after the prefix, in lane order. Each lane
+  // computes its own row; groups are found with ballots (one round per
+  // distinct first page, then per distinct prefix) and their sums pass
+  // through LDS (a group's last member holds them).
+  bool grouped = false;
+  int row_base_g = 0;  // decode rows of the grouped list
+  const bool dec0 = lane < a.S && sh0.L == 1 && sh0.n >= 1;
+  const bool shared0 = dec0 && s_hist[page_hash(fp0)] > 1;
+  if (may_group && __ballot(shared0) != 0) {
+    const int s = lane;
+    const unsigned long long below = (1ull << s) - 1ull;
+    const unsigned long long same_fp = wave_match(fp0, shared0);  // (in every lane: ballots)
+    const int lead = shared0 ? __ffsll((long long)same_fp) - 1 : s;
+    // leading page ids equal to the leader's: the first kGroupFirstPages
+    // from the leader's lane, then eight per round from memory
+    const bool follower = shared0 && lead != s;
+    const int cap_pages = follower ? min((sh0.n - 1) >> a.p_shift, kGroupMaxPages) : 0;
+    int lp_pages = 0;
+    bool run = true;
+#pragma unroll
+    for (int j = 0; j < kGroupFirstPages; ++j) {
+      const int vl = __shfl(bt0[j], lead);  // (every lane takes part in the shuffle)
+      if (run && j < cap_pages && bt0[j] == vl) ++lp_pages;
+      else run = false;
+    }
+    if (run && cap_pages > kGroupFirstPages) {
+      const int* bs = a.block_tables + (size_t)s * a.max_blocks;
+      const int* bl = a.block_tables + (size_t)lead * a.max_blocks;
+      for (int p0 = kGroupFirstPages; p0 < cap_pages; p0 += 8) {
+        int vs[8], vl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          vs[j] = p0 + j < cap_pages ? bs[p0 + j] : 0;
+          vl[j] = p0 + j < cap_pages ? bl[p0 + j] : 1;
+        }
+        int eq = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (eq == j && vs[j] == vl[j]) ++eq;
+        lp_pages += eq;
+        if (eq < 8) break;
+      }
+    }
+    // rows of one leader and one prefix length: their rank decides the group
+    // (bits: group index 0..4, prefix pages 5..15, leader 16..21)
+    const bool cand = lp_pages >= 1;
+    const int key = (lead << 16) | (lp_pages << 5);
+    const unsigned long long same = wave_match(key, cand);
+    const int lg = 31 - __builtin_clz(Rmax);
+    const int rank = __popcll(same & below), size = __popcll(same);
+    const int sg = rank >> lg;
+    const bool member = cand && min(Rmax, size - (sg << lg)) >= 2;
+    const unsigned long long gm = wave_match(key | sg, member);  // the group's lanes
+    grouped = __ballot(member) != 0;
+    if (grouped) {
+      int* s_pm = sm.grp[0];    // a member's keys after the prefix (padded)
+      int* s_np = sm.grp[1];    // a member's own partitions
+      int* s_gk = sm.grp[2];    // (first member) the group's keys after the prefix
+      int* s_gs = sm.grp[3];    // (first member) the group's partial slots
+      const int first = member ? __ffsll((long long)gm) - 1 : s;
+      const bool last = member && (gm >> s) == 1ull;
+      const int idx = __popcll(gm & below), gsize = __popcll(gm);
+      const int g_lp = lp_pages << a.p_shift;
+      const int pm = member ? (sh0.n - g_lp + A - 1) / A * A : 0;
+      if (member) s_pm[s] = pm;
+      wave_lds_sync();
+      int kpre = 0;  // keys of the group's members before this one
+      for (unsigned long long m = gm & below; m != 0; m &= m - 1ull)
+        kpre += s_pm[__ffsll((long long)m) - 1];
+      if (last) s_gk[first] = kpre + pm;
+      wave_lds_sync();
+      const bool own = dec0 && !member;
+      const bool head = member && first == s;
+      const int len = own ? (sh0.n + A - 1) / A * A : (head ? g_lp + s_gk[s] : 0);
+      const int nemit = own ? 1 : (head ? 1 + gsize : 0);
+      int nkeys, nrows;
+      const int off = wave_excl_scan(len, &nkeys);
+      const int ri = wave_excl_scan(nemit, &nrows);
+      chunking(nkeys);
+      // (every lane takes part in the shuffles)
+      const int off_g = __shfl(off, first), ri_g = __shfl(ri, first);
+      const int o_m = off_g + g_lp + kpre;  // a member's own keys on the axis
+      const int kg = member ? parts(off_g, g_lp) : 0;  // the group row's partitions
+      const int npm = member ? parts(o_m, pm) : 0;
+      if (member) s_np[s] = npm;
+      wave_lds_sync();
+      int npre = 0;  // own partitions of the group's members before this one
+      for (unsigned long long m = gm & below; m != 0; m &= m - 1ull)
+        npre += s_np[__ffsll((long long)m) - 1];
+      if (last) s_gs[first] = (idx + 1) * kg + npre + npm;
+      wave_lds_sync();
+      const int np_own = own ? parts(off, len) : 0;
+      const int slots = own ? (np_own > 1 ? np_own : 0) : (head ? s_gs[s] : 0);
+      int nslots;
+      const int pb = wave_excl_scan(slots, &nslots);
+      const int pb_g = __shfl(pb, first);
+      // group only while the partial slots fit the workspace (a member holds
+      // its group row's partials and its own)
+      if (nslots > a.part_slots) {
+        grouped = false;
+      } else {
+        if (own) {
+          dec_rows[ri] = make_int4(s | (shared0 ? kRowShared : 0), off, sh0.n, sh0.q0);
+          nparts_of[ri] = np_own;
+          pbase_of[ri] = pb;
+          kstart_of[ri] = 0;
+          part0_of[ri] = 0;
+          chunk_starts(off, len, ri);
+        }
+        if (head) {
+          // the group row: the leader's page table holds the prefix
+          dec_rows[ri] = make_int4(lead | kRowShared | kRowGroup, off, g_lp, gsize);
+          nparts_of[ri] = 0;
+          pbase_of[ri] = 0;
+          kstart_of[ri] = 0;
+          part0_of[ri] = 0;
+          chunk_starts(off, g_lp, ri);
+        }
+        if (member) {
+          const int rm = ri_g + 1 + idx;
+          dec_rows[rm] = make_int4(s, o_m, sh0.n - g_lp, sh0.q0);
+          nparts_of[rm] = kg + npm;
+          pbase_of[rm] = pb_g + idx * kg + npre;
+          kstart_of[rm] = g_lp;
+          part0_of[rm] = kg;
+          chunk_starts(o_m, pm, rm);
+        }
+        row_base_g = nrows;
+      }
+    }
   }
-  int chunks = (int)((tk + (unsigned)C - 1u) / (unsigned)C);
-  if (chunks > cap_dec) chunks = cap_dec;  // (never: the workspace query bounds the chunks)
+  if (!grouped) chunking(total_keys);
   const int n_static = chunks < (int)waves ? chunks : (int)waves;
 
   // ---- pass 2: decode rows, their offsets on the key axis, chunk starts,
   // partial slots (rows of more than one partition) ----
   int row_base = 0, off_base = 0, slot_base = 0;
+  if (grouped) {
+    row_base = row_base_g;
+  } else {
   for (int c0 = 0; c0 < a.S; c0 += 64) {
     const int s = c0 + lane;
     SeqShape sh{0, 0, 0};
@@ -271,12 +471,14 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
     const int pb = slot_base + wave_excl_scan(np > 1 ? np : 0, &nslots);
     if (is_dec) {
       // the row's first page is read by another decode row too (bit 30 of
-      // the sequence index, which the host bounds below 2^30): its keys are
+      // the sequence index, which the host bounds below 2^29): its keys are
       // loaded into the caches as usual, the others' as a stream
       const int shared = s_hist[page_hash(fp)] > 1 ? kRowShared : 0;
       dec_rows[ri] = make_int4(s | shared, off, sh.n, sh.q0);
       nparts_of[ri] = np;
       pbase_of[ri] = pb;
+      kstart_of[ri] = 0;
+      part0_of[ri] = 0;
       // chunks whose first key falls in this row start here
       for (int j = (off + C - 1) / C; j <= j1; ++j)
         if (j < cap_dec) first_row[j] = ri;
@@ -284,6 +486,7 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
     row_base += nrows;
     off_base += npad;
     slot_base += nslots;
+  }
   }
 
   // the bins are free again: zero them for the prefill items' tile counts

@@ -186,7 +186,8 @@ int tick_grid(pa_dtype_t dt, int D, int G) {
 }
 
 hipError_t launch_tick_reduce(const AttnArgs& a, hipStream_t s) {
-  const long dec_threads = a.max_parts > 1 ? (long)a.S * a.Hq * (a.D / 4) * kMergeLanes : 0;
+  const long dec_threads =
+      a.max_parts > 1 ? plan_rows(a.S) * a.Hq * (a.D / 4) * kMergeLanes : 0;
   const int dec_blocks = (int)((dec_threads + kReduceThreads - 1) / kReduceThreads);
   // cut items use at least 2 Hkv partial slots each: at most pf_slots / 2
   // (item, KV head) pairs, kPrefillRows * (D / 4) threads per pair

@@ -46,7 +46,7 @@ def test_library_exports_nothing_else():
 
 
 def test_status_strings_and_version():
-    assert pa.pa_abi_version() == 6
+    assert pa.pa_abi_version() == 7
     for code in range(5):
         assert pa.pa_status_string(code).startswith("PA_")
     assert "UNKNOWN" in pa.pa_status_string(99)
@@ -107,24 +107,28 @@ def test_attention_empty_tick_is_ok_without_touching_memory():
 
 def _plan_bytes(S, cap_dec, cap_pf, Hq):
     # header 32, one 32-int line per prefill queue cursor (Hq) and one for the counter
-    # of claimed decode chunks, decode rows 4 * S, partitions and first partial slot per row 2 * S,
-    # chunk starts cap_dec, then (16-byte aligned) prefill entries 4 * cap_pf, their
-    # sequence shapes 4 * cap_pf and cut items 4 * cap_pf (ints), padded to 256 bytes
-    pf = -(-(32 * (2 + Hq) + 6 * S + cap_dec) // 4) * 4
+    # of claimed decode chunks; R = S + S // 2 + 1 rows of the decode row list (the
+    # decode rows and at most one group row per two of them): the rows 4 * R, and
+    # partitions, first partial slot, first key and first partition index per row
+    # 4 * R; chunk starts cap_dec, then (16-byte aligned) prefill entries 4 * cap_pf,
+    # their sequence shapes 4 * cap_pf and cut items 4 * cap_pf (ints), padded to 256 bytes
+    R = S + S // 2 + 1
+    pf = -(-(32 * (2 + Hq) + 8 * R + cap_dec) // 4) * 4
     return -(-(pf + 12 * cap_pf) * 4 // 256) * 256
 
 
 def _auto_slots(S, Hq, max_seq_len, P, max_parts, dec_grid=256):
-    """Partial slots with automatic partitions: at most max_parts per row, and
-    at most rows + chunks, the chunks of the decode key axis numbering at most
-    the decode waves per KV head (dec_grid * 4 waves over at least Hq / 8 KV
-    heads; without a GPU the library assumes 256 compute units) or the axis
-    over the largest partition (63 pages, at most 65536 keys)."""
+    """Partial slots with automatic partitions (bf16): at most max_parts per
+    row, and at most rows + chunks plus 4 per row for the members of grouped
+    rows (a shared prefix read once), the chunks of the decode key axis
+    numbering at most the decode waves per KV head (dec_grid * 4 waves over at
+    least Hq / 8 KV heads; without a GPU the library assumes 256 compute units)
+    or the axis over the largest partition (63 pages, at most 65536 keys)."""
     waves = -(-(dec_grid * 4 * 8) // Hq)
     split_max = min(63 * P, 65536) // 16 * 16
     by_cap = -(-(S * (-(-max_seq_len // 16) * 16)) // split_max)
     chunks = max(waves, by_cap)
-    return min(S * max_parts, chunks), min(S * max_parts, S + chunks)
+    return min(S * max_parts, chunks), min(S * max_parts, S + chunks + 4 * S)
 
 
 def test_workspace_size_query():
@@ -136,12 +140,12 @@ def test_workspace_size_query():
     assert ws(64, 64, 32, 128, 1, 256, 256, 0, BF16) == (
         _plan_bytes(64, cap, 0, 32) + slots * 32 * 130 * 4)
     cap, slots = _auto_slots(64, 32, 4096, 256, 17)
-    assert (cap, slots) == (256, 320)
+    assert (cap, slots) == (256, 576)
     n = ws(64, 64, 32, 128, 1, 4096, 256, 0, BF16)
     assert n == _plan_bytes(64, cap, 0, 32) + slots * 32 * 130 * 4
     # long rows: 36 rows of up to 32768 keys with Hq = 32 (at most 256 waves per KV head)
     cap, slots = _auto_slots(36, 32, 32768, 256, 129)
-    assert (cap, slots) == (256, 292)
+    assert (cap, slots) == (256, 436)
     assert ws(36, 36, 32, 128, 1, 32768, 256, 0, BF16) == (
         _plan_bytes(36, cap, 0, 32) + slots * 32 * 130 * 4)
     # an explicit split of 1024 keys: partitions aligned to the row start, 4 partials

@@ -10,8 +10,8 @@ import torch
 import oracle
 import paged_kv_cache_page_amd as pa
 from paged_kv_cache_page_amd import workloads as W
-from _gpu import (BF16_MAX_ABS, DEV, DevTick, check_attention, host_f32, host_storage, i32,
-                  run_gpu_tick, say, storage_tensor)
+from _gpu import (BF16_MAX_ABS, BF16_MEAN_ABS, DEV, DevTick, check_attention, host_f32,
+                  host_storage, i32, run_gpu_tick, say, storage_tensor)
 import _pins
 
 pytestmark = pytest.mark.gpu
@@ -139,11 +139,36 @@ def test_page_permutation_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_shared_prefix_equals_private_copies_bitwise():
+def _attend_with_plan(d, kv_split_tokens=0):
+    """Attention with a workspace of our own; returns (out, decode rows in the
+    plan's row list), the count the plan writes first (group rows included)."""
+    t = d.t
+    dt = pa.PA_BF16 if t.dtype == W.BF16 else pa.PA_F32
+    need = pa.pa_paged_attention_workspace_size(t.S, t.T, t.Hq, t.D, t.max_query_len,
+                                                t.max_seq_len, t.P, kv_split_tokens, dt)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
+    out = pa.pa_paged_attention_varlen(d.q, d.k_pool, d.v_pool, d.block_tables, d.seq_lens,
+                                       d.qsl, t.max_query_len, t.max_seq_len, scale=t.scale,
+                                       kv_split_tokens=kv_split_tokens, workspace=ws)
+    torch.cuda.synchronize()
+    return out, int(ws[:4].view(torch.int32).item())
+
+
+def test_shared_prefix_read_once_matches_private_copies():
+    """Prefix caching (Helios blog, "Prefix caching"): sequences that share
+    prefix pages attend to them as if each had its own copy. The shared
+    prefix is read once per group of sharing rows (group rows in the plan),
+    so the shared tick and the private-copy tick sum the prefix in different
+    partitions: both are checked against the oracle, and against each other
+    at the same tolerance."""
     t = W.make_config(5, poison=True)
     d = DevTick(t).write()
-    a = d.attend()
-    torch.cuda.synchronize()
+    say("shared prefix: grouped rows")
+    a, rows = _attend_with_plan(d)
+    n_dec = int((t.query_lens == 1).sum())
+    assert rows > n_dec, (rows, n_dec)  # the 32 sharers were grouped
+    ref = oracle_tick(t)
+    check_attention(a, ref, t.dtype, "shared prefix, grouped")
     # give every sharing sequence its own copy of the prefix pages
     bt = t.block_tables.copy()
     kp, vp = d.k_pool, d.v_pool
@@ -161,7 +186,77 @@ def test_shared_prefix_equals_private_copies_bitwise():
     b_out = pa.pa_paged_attention_varlen(d.q, kp2, vp2, i32(bt), d.seq_lens, d.qsl,
                                          t.max_query_len, t.max_seq_len, scale=t.scale)
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b_out.view(torch.int16))
+    check_attention(b_out, ref, t.dtype, "private copies")
+    diff = (host_f32(a).astype(np.float64) - host_f32(b_out).astype(np.float64))
+    assert np.abs(diff).max() <= BF16_MAX_ABS and np.abs(diff).mean() <= BF16_MEAN_ABS
+
+
+# (Hq, Hkv, D, P, sharers, prefix pages, own keys after the prefix: low, high)
+GROUP_CASES = [
+    (32, 8, 128, 256, 10, 2, 1, 300),    # G = 4: groups of 4, 4 and a lone sharer
+    (16, 16, 128, 16, 20, 5, 1, 40),     # G = 1: groups of 16 and 3 (one-key suffixes)
+    (32, 4, 64, 16, 7, 3, 16, 64),       # G = 8: groups of 2 (and a lone sharer), D = 64
+    (16, 8, 64, 256, 6, 1, 1, 256),      # G = 2: one group of 5 (up to 8 per group)
+    (32, 8, 128, 16, 40, 64, 1, 2000),   # a 1024-key prefix over several chunks, 40 sharers
+    (16, 8, 128, 16, 6, 16, 1, 40),      # a prefix of exactly 16 pages
+    (32, 8, 128, 16, 9, 17, 1, 300),     # 17 prefix pages (the last one compared in memory)
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROUP_CASES)))
+def test_grouped_prefix_rows(case):
+    """Decode rows sharing prefix pages, grouped (group rows read the prefix
+    once for up to 16 / G sharers, whose own rows start after it; the merge
+    sums both) against the oracle, beside rows that share nothing; and the
+    same tick with a fixed split, which never groups."""
+    Hq, Hkv, D, P, m, pp, lo, hi = GROUP_CASES[case]
+    rng = np.random.default_rng(700 + case)
+    own = [int(x) for x in rng.integers(lo, hi + 1, size=m)]
+    sl = [pp * P + x for x in own] + [int(x) for x in rng.integers(20, 3000, size=5)]
+    t = W.build_tick(rng, name="grouped", dtype=W.BF16, Hq=Hq, Hkv=Hkv, D=D, P=P,
+                     seq_lens=sl, query_lens=[1] * len(sl), theta=1e4, poison=True,
+                     shared_prefix_pages=pp, shared_prefix_seqs=range(m))
+    say("grouped prefix rows", GROUP_CASES[case])
+    d = DevTick(t).write()
+    out, rows = _attend_with_plan(d)
+    assert rows > len(sl), (rows, len(sl))
+    ref = oracle_tick(t)
+    check_attention(out, ref, t.dtype, "grouped")
+    fixed, rows_fixed = _attend_with_plan(d, 512)
+    assert rows_fixed == len(sl)
+    check_attention(fixed, ref, t.dtype, "fixed split")
+
+
+def test_grouped_prefix_tree():
+    """Sharers whose page tables leave the leader's at different pages (a
+    prefix tree; the pages after the split hold copies of the leader's, under
+    other page ids): rows of one common-prefix length form their own groups,
+    and every row still matches the oracle."""
+    rng = np.random.default_rng(731)
+    P, pp = 16, 6
+    own = [int(x) for x in rng.integers(1, 200, size=12)]
+    sl = [pp * P + x for x in own] + [int(x) for x in rng.integers(20, 900, size=3)]
+    t = W.build_tick(rng, name="tree", dtype=W.BF16, Hq=32, Hkv=8, D=128, P=P,
+                     seq_lens=sl, query_lens=[1] * len(sl), theta=1e4, poison=True,
+                     pool_factor=2.0, shared_prefix_pages=pp, shared_prefix_seqs=range(12))
+    spare = sorted(set(range(t.num_pages)) - set(t.block_tables[t.block_tables >= 0].tolist()))
+    bt = t.block_tables.copy()
+    kp, vp = t.k_pool.copy(), t.v_pool.copy()
+    # sequences 3..6 leave at page 4, 7..9 at page 2; 1, 2, 10, 11 keep all 6
+    for seqs, cut in ((range(3, 7), 4), (range(7, 10), 2)):
+        for s in seqs:
+            for j in range(cut, pp):
+                new = spare.pop()
+                kp[new] = kp[bt[s, j]]
+                vp[new] = vp[bt[s, j]]
+                bt[s, j] = new
+    t = W.Tick(**{**t.__dict__, "block_tables": bt, "k_pool": kp, "v_pool": vp})
+    say("grouped prefix tree")
+    d = DevTick(t).write()
+    out, rows = _attend_with_plan(d)
+    # G = 4: groups of at most 4 rows: {1, 2, 10, 11}, {3..6}, {7, 8, 9}
+    assert rows == len(sl) + 3, (rows, len(sl))
+    check_attention(out, oracle_tick(t), t.dtype, "prefix tree")
 
 
 def _subset_tick(t, seqs):
