@@ -52,7 +52,8 @@ struct AttnArgs {
 //   header [32]: [0] decode rows R, [1] prefill entries (per KV head), [2]
 //     chunk keys C, [3] chunks, [4] row alignment A, [5] cut prefill items,
 //     [6] chunks taken one per decode wave n_s, [7] claimed items (chunks
-//     past n_s x Hkv), [8..31] unused
+//     past n_s x Hkv), [8] prefill queues found empty (counted by the
+//     tick kernel's claims), [9..31] unused
 //   prefill queue cursors: Hq counters, one per 128-byte line (Hq >= Hkv
 //     bounds the KV heads, which the workspace query does not see): the
 //     queue of KV head h at kPlanLine * (1 + h); then the counter of the
@@ -115,6 +116,7 @@ __host__ __device__ inline PlanOffsets plan_offsets(long S, long Hq, long cap_de
   return o;
 }
 __host__ __device__ inline int plan_pf_cursor(int h) { return kPlanLine * (1 + h); }
+__host__ __device__ inline int plan_pf_dry() { return 8; }
 __host__ __device__ inline int plan_dec_cursor(int Hq) { return kPlanLine * (1 + Hq); }
 
 // Query rows per prefill workgroup; a tile holds kPrefillRows / G tokens.

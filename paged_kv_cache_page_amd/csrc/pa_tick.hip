@@ -25,22 +25,28 @@ namespace pa {
 
 namespace {
 
-// Next prefill item of KV head kvh's queue for the whole workgroup: thread 0
-// claims it, the others read it from LDS.
-__device__ __forceinline__ int pf_take(int* cursor, int* s_slot) {
-  if (threadIdx.x == 0)
-    *s_slot = __hip_atomic_fetch_add(cursor, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Next prefill item of a queue for the whole workgroup: thread 0 claims it
+// and, in the same round trip, reads how many queues are known to be empty;
+// the others read both from LDS. The one claim that returns n_items exactly
+// (the first past the queue's end) adds its queue to that count.
+__device__ __forceinline__ int2 pf_take(int* cursor, int* dry, int n_items, int2* s_slot) {
+  if (threadIdx.x == 0) {
+    const int it = __hip_atomic_fetch_add(cursor, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int d = __hip_atomic_load(dry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (it == n_items) __hip_atomic_fetch_add(dry, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_slot = make_int2(it, d + (it == n_items ? 1 : 0));
+  }
   __syncthreads();
-  const int it = *s_slot;
+  const int2 r = *s_slot;
   __syncthreads();  // everyone has read the slot before it is written again
-  return it;
+  return r;
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void tick_kernel(
     AttnArgs a) {
   __shared__ PfSmem<D> sm;
-  __shared__ int s_next;
+  __shared__ int2 s_next;
   static_assert(kPfThreads == 64 * 4, "decode workers are workgroups of four waves");
   // decode workers keep their K/V buffers in the (not yet used) prefill tile
   // buffers: sm.k and sm.v, which follow each other
@@ -54,6 +60,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int4* items = reinterpret_cast<const int4*>(a.plan + po.pf);
   const int4* shapes = reinterpret_cast<const int4*>(a.plan + po.pf_shape);
   const int n_items = a.plan[1];
+  int* dry = a.plan + plan_pf_dry();
   const int home = blockIdx.x % a.Hkv;
   for (int hh = 0; hh < a.Hkv; ++hh) {
     const int kvh = home + hh < a.Hkv ? home + hh : home + hh - a.Hkv;
@@ -61,7 +68,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     // the entry index (read from LDS) is the same in every lane: reading it
     // from the first lane tells the compiler, so the entry and everything
     // derived from it stay in scalar registers with scalar branches
-    int it = __builtin_amdgcn_readfirstlane(pf_take(cursor, &s_next));
+    int2 c = pf_take(cursor, dry, n_items, &s_next);
+    int it = __builtin_amdgcn_readfirstlane(c.x);
     while (it < n_items) {
       // (the next entry is claimed only once this one is done: claimed ahead,
       // the last entries sat with busy workgroups while the decode workers,
@@ -73,8 +81,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       __builtin_amdgcn_s_setprio(2);
       prefill_item<D, G>(a, sm, items[it], shapes[it], kvh);
       __builtin_amdgcn_s_setprio(0);
-      it = __builtin_amdgcn_readfirstlane(pf_take(cursor, &s_next));
+      c = pf_take(cursor, dry, n_items, &s_next);
+      it = __builtin_amdgcn_readfirstlane(c.x);
     }
+    // every queue is known to be empty: the rest of the walk would only claim
+    // past their ends, one round trip each
+    if (__builtin_amdgcn_readfirstlane(c.y) >= a.Hkv) break;
   }
 }
 
