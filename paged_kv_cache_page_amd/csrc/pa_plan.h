@@ -41,11 +41,15 @@
 namespace pa {
 
 // The plan is one wave: its lanes' LDS traffic is ordered by waiting for the
-// wave's own LDS operations (no workgroup barrier, which would also wait for
-// the workgroup's other waves).
+// wave's own LDS operations (lgkmcnt 0; the vmcnt and expcnt fields at their
+// maxima, so the plan's global stores stay in flight: a workgroup-scope fence
+// would wait for them at every step), with compiler barriers on both sides
+// and no workgroup barrier (which would also wait for the other waves).
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 constexpr int kCostBins = 2048;     // key tiles of a prefill item, capped
@@ -86,20 +90,27 @@ __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
   return incl - v;
 }
 
-__device__ __forceinline__ long long wave_sum(long long v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 __device__ __forceinline__ int wave_sum32(int v) {
   return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
 
+// Sum over the wave of non-negative per-lane values below 2^48 (uniform):
+// the low 24 and the high bits summed apart in 32 bits, each sum below 2^30.
+__device__ __forceinline__ long long wave_sum(long long v) {
+  const int lo = wave_sum32((int)(v & 0xFFFFFF)), hi = wave_sum32((int)(v >> 24));
+  return ((long long)hi << 24) + lo;
+}
+
+// Maximum over the wave of non-negative values (uniform): the moves of the
+// prefix sum, with max in place of +; lanes a move does not reach read 0.
 __device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+  v = max(v, dpp0<0x111, 0xF>(v));
+  v = max(v, dpp0<0x112, 0xF>(v));
+  v = max(v, dpp0<0x114, 0xF>(v));
+  v = max(v, dpp0<0x118, 0xF>(v));
+  v = max(v, dpp0<0x142, 0xA>(v));
+  v = max(v, dpp0<0x143, 0xC>(v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // For each lane with `on`, the mask of the lanes with `on` holding the same
@@ -451,8 +462,9 @@ __device__ void plan_wave(const AttnArgs& a, int* plan, int cap_dec, int cap_pf,
     SeqShape sh{0, 0, 0};
     int is_dec = 0, pad = 0, fp = 0;
     if (s < a.S) {
-      fp = a.block_tables[(size_t)s * a.max_blocks];
-      sh = shape(s);
+      // (at most 64 sequences: pass 1's loads, still in registers)
+      fp = a.S <= 64 ? fp0 : a.block_tables[(size_t)s * a.max_blocks];
+      sh = a.S <= 64 ? sh0 : shape(s);
       if (sh.L == 1 && sh.n >= 1) {
         is_dec = 1;
         pad = (sh.n + A - 1) / A * A;
