@@ -71,3 +71,65 @@ def test_random_small_ticks_match_the_oracle(case):
     bits = (lambda a: a.view(np.uint32)) if dtype == W.F32 else (lambda a: a)
     assert np.array_equal(bits(host_storage(d.k_pool, dtype)), bits(res["k_pool"]))
     assert np.array_equal(bits(host_storage(d.v_pool, dtype)), bits(res["v_pool"]))
+
+
+@st.composite
+def shared_prefix_ticks(draw):
+    D = draw(st.sampled_from([64, 128]))
+    G = draw(st.sampled_from([1, 2, 4, 8]))
+    Hkv = draw(st.sampled_from([1, 2]))
+    P = draw(st.sampled_from([16, 32, 256]))
+    pp = draw(st.integers(1, 6))        # pages of the shared prefix
+    m = draw(st.integers(2, 12))        # sequences that share it (decode rows)
+    seq_lens = [pp * P + draw(st.integers(1, 200)) for _ in range(m)]
+    query_lens = [1] * m
+    for _ in range(draw(st.integers(0, 3))):  # other rows: decode or a chunk
+        n = draw(st.integers(2, 300))
+        seq_lens.append(n)
+        query_lens.append(draw(st.sampled_from([1, 1, draw(st.integers(2, n))])))
+    # page from which each sharer holds copies of the prefix under other ids
+    # (pp: it keeps them all), so that sharers agree with the lowest-indexed
+    # one on different numbers of leading pages
+    leave = [draw(st.integers(0, pp)) for _ in range(m)]
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    return D, G, Hkv, P, pp, seq_lens, query_lens, leave, seed
+
+
+@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(shared_prefix_ticks())
+def test_random_shared_prefix_ticks_match_the_oracle(case):
+    """Decode rows sharing leading pages (bf16, automatic split: the plan
+    groups them so that each group reads the shared pages once) against the
+    oracle, the pools bit for bit (Helios blog, "Prefix caching": the sharers
+    read the same physical pages)."""
+    D, G, Hkv, P, pp, sl, ql, leave, seed = case
+    rng = np.random.default_rng(seed)
+    m = len(leave)
+    # the pages the tick needs, and room for every copy
+    blocks = [(n + P - 1) // P for n in sl]
+    needed = pp + sum(b - (pp if s < m else 0) for s, b in enumerate(blocks))
+    t = W.build_tick(rng, name="prop-shared", dtype=W.BF16, Hq=G * Hkv, Hkv=Hkv, D=D, P=P,
+                     seq_lens=sl, query_lens=ql, theta=1e4, poison=True,
+                     pool_pages=needed + m * pp, shared_prefix_pages=pp,
+                     shared_prefix_seqs=range(m))
+    spare = sorted(set(range(t.num_pages)) - set(t.block_tables[t.block_tables >= 0].tolist()))
+    bt, kp, vp = t.block_tables.copy(), t.k_pool.copy(), t.v_pool.copy()
+    for s in range(m):
+        for j in range(leave[s], pp):
+            new = spare.pop()
+            kp[new], vp[new] = kp[bt[s, j]], vp[bt[s, j]]
+            bt[s, j] = new
+    t = W.Tick(**{**t.__dict__, "block_tables": bt, "k_pool": kp, "v_pool": vp})
+    say("prop shared", D, G, Hkv, P, pp, sl, ql, leave)
+    d = DevTick(t)
+    out = pa.pa_tick_forward(d.q, d.k, d.v, d.positions, d.block_tables, d.seq_lens, d.qsl,
+                             d.oracle_table(), d.k_pool, d.v_pool, t.max_query_len,
+                             t.max_seq_len, scale=t.scale, kv_split_tokens=0)
+    torch.cuda.synchronize()
+    res = oracle.run_tick(t.dtype, t.q, t.k, t.v, t.positions, t.block_tables, t.qsl,
+                          t.seq_lens, t.k_pool, t.v_pool,
+                          oracle.rope_table(t.max_pos, t.D, t.theta), t.scale)
+    check_attention(out, res["out"], t.dtype, "prop shared")
+    assert np.array_equal(host_storage(d.k_pool, t.dtype), res["k_pool"])
+    assert np.array_equal(host_storage(d.v_pool, t.dtype), res["v_pool"])
