@@ -280,10 +280,14 @@ def prewarm(torch, step, ms):
     return n
 
 
-def timed(torch, step, steps, warmup, stream, wall=None):
-    """Warm-up, then `steps` steps between two events (synchronised on both
-    sides): ms per step. `wall`, a list, receives the host seconds of the
-    timed region."""
+PREWARM_MS = 0.0  # --prewarm-ms, for every timed pass
+
+
+def timed(torch, step, steps, warmup, stream, wall=None, prewarm_ms=None):
+    """Pre-warm (PREWARM_MS unless given), warm-up, then `steps` steps between
+    two events (synchronised on both sides): ms per step. `wall`, a list,
+    receives the host seconds of the timed region."""
+    prewarm(torch, step, PREWARM_MS if prewarm_ms is None else prewarm_ms)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -554,6 +558,8 @@ def main():
     ap.add_argument("--sample", action="store_true",
                     help="only time pa_sample_tokens over one tick's logits rows")
     args = ap.parse_args()
+    global PREWARM_MS
+    PREWARM_MS = args.prewarm_ms
     if args.sample:
         bench_sample(args.steps, args.warmup, not args.no_cpu)
         return
@@ -593,7 +599,6 @@ def main():
     if args.only in ("decode-rows", "prefill-chunks"):
         mask = t.query_lens == 1 if args.only == "decode-rows" else t.query_lens > 1
         sub = tick.sub(mask)
-        prewarm(torch, sub, args.prewarm_ms)
         ms = timed(torch, sub, args.steps, args.warmup, tick.stream)
         print(json.dumps({"only": args.only, "workload": t.name, "ms_per_call": round(ms, 5),
                           "steps": args.steps}), flush=True)
@@ -602,7 +607,8 @@ def main():
     log("warmup", args.warmup, "+ timed", args.steps, "steps (cold: 3 rotated copies)")
     prewarm_steps = prewarm(torch, tick.step, args.prewarm_ms)
     walls = []
-    ms_per_step = timed(torch, tick.step, args.steps, args.warmup, tick.stream, walls)
+    ms_per_step = timed(torch, tick.step, args.steps, args.warmup, tick.stream, walls,
+                        prewarm_ms=0.0)
     wall = walls[0]
     if args.only == "step":
         print(json.dumps({"only": "step", "workload": t.name, "ms_per_step": round(ms_per_step, 5),
@@ -701,8 +707,9 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "prewarm": {"ms": args.prewarm_ms, "steps": prewarm_steps,
-                    "note": "untimed steps before the warm-up steps, so that the timed steps run "
-                            "at the clocks of a GPU in steady use"},
+                    "note": "untimed steps before the warm-up steps (of this pass and of every "
+                            "other timed pass), so that the timed steps run at the clocks of a "
+                            "GPU in steady use"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": t.dtype,
         "data": "synthetic",
