@@ -434,6 +434,7 @@ def bench_sample(steps, warmup, with_cpu):
     p = torch.full((R,), 0.95, dtype=torch.float32, device=dev)
     u = torch.from_numpy(rng.random(R, dtype=np.float32)).to(dev)
     out = torch.empty(R, dtype=torch.int32, device=dev)
+    prewarm(torch, lambda i: pa.pa_sample_tokens(logits, T, k, p, u, out=out), PREWARM_MS)
     for _ in range(warmup):
         pa.pa_sample_tokens(logits, T, k, p, u, out=out)
     torch.cuda.synchronize()
