@@ -20,7 +20,10 @@
 // float32 screen for a positive weight against it; the row's workgroup then
 // keeps those that pass against the row's maximum, in LDS, in index order. That list is a leading part of the ranking and holds every
 // token of positive weight, so top-k, top-p and the draw run on it alone; a
-// row whose list would not fit runs them over the row instead.
+// row whose list would not fit runs them over the row instead. A list of at
+// most 512 tokens (the usual case at low temperatures) is ranked by the row's
+// first wave alone, with 8-bit digits, no workgroup barrier and one exp per
+// token.
 //
 // Weights are floor(exp((x - max) / T) * 2^32) in float64: the subtraction and
 // the division are IEEE operations (this file is built without contraction),
@@ -297,6 +300,168 @@ __device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, fl
   return (pick >= 0 && pick < V) ? pick : top;
 }
 
+// ---- short lists: one wave, no workgroup barriers ----
+// A list of at most kWaveList tokens is ranked by the row's first wave alone
+// (the others have left): lane l holds tokens kWavePer l .. kWavePer l + 7 of
+// the list with their sort keys and weights in registers (one exp per token),
+// and each radix pass needs only the wave's own LDS ordering. The cutoffs and
+// the draw are the same functions of the list as above (a shortest leading
+// part, then the first token in index order whose running weight passes
+// floor(u * S)), so the token is the same; only the digit width differs.
+constexpr int kWavePer = 8;
+constexpr int kWaveList = 64 * kWavePer;
+constexpr int kWaveDigit = 8;
+constexpr int kWaveBins = 1 << kWaveDigit;
+constexpr int kWaveBinsPerLane = kWaveBins / 64;
+static_assert(kWaveBins <= kBins, "the wave's bins are the first of the workgroup's");
+
+// The wave's LDS operations complete in order: wait for them, with compiler
+// barriers on both sides so that none moves across.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// select_cutoff for one wave over the lanes' registers (n = tokens this lane
+// holds).
+template <bool BY_WEIGHT>
+__device__ u64 wave_select_cutoff(const u64 (&key)[kWavePer], const u64 (&wt)[kWavePer], int n,
+                                  int ibits, u64 floor_key, float p, u64 target, SampleLds& L) {
+  const int lane = threadIdx.x;
+  const int nbits = 32 + ibits;
+  u64 prefix = 0, rem = target;
+  int done = 0;
+  for (;;) {
+    const int width = min(kWaveDigit, nbits - done);
+    const int shift = nbits - done - width;
+    wave_lds_sync();  // the previous pass's reads of the bins are done
+#pragma unroll
+    for (int i = 0; i < kWaveBinsPerLane; ++i) {
+      L.cnt[lane + 64 * i] = 0u;
+      L.mass[lane + 64 * i] = 0ull;
+      L.maxkey[lane + 64 * i] = 0ull;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < kWavePer; ++j) {
+      if (j >= n) continue;
+      const u64 k = key[j];
+      if (k < floor_key) continue;
+      if (done > 0 && (k >> (shift + width)) != prefix) continue;
+      const int d = (int)((k >> shift) & (u64)((1u << width) - 1u));
+      if (BY_WEIGHT) {
+        if (wt[j] == 0ull) continue;
+        atomicAdd(&L.mass[d], wt[j]);
+      }
+      atomicAdd(&L.cnt[d], 1u);
+      atomicMax(&L.maxkey[d], k);
+    }
+    wave_lds_sync();
+    // lane l scans buckets kWaveBins - 1 - (4 l + i): larger buckets first
+    u64 v[kWaveBinsPerLane];
+    u64 s = 0;
+#pragma unroll
+    for (int i = 0; i < kWaveBinsPerLane; ++i) {
+      const int b = kWaveBins - 1 - (kWaveBinsPerLane * lane + i);
+      v[i] = BY_WEIGHT ? L.mass[b] : (u64)L.cnt[b];
+      s += v[i];
+    }
+    const u64 incl = wave_incl_scan(s, lane);
+    if (BY_WEIGHT && done == 0) {
+      const u64 total = __shfl(incl, 63, 64);
+      const double need = ceil((double)p * (double)total);
+      rem = need >= 1.0 ? (u64)need : 1ull;
+    }
+    const u64 before = incl - s;
+    const u64 owners = __ballot(incl >= rem && before < rem);
+    if (owners == 0ull) return ~0ull;  // no bucket chosen (input outside the contract): keep nothing
+    const int owner = __ffsll((long long)owners) - 1;
+    // in the owner: its first bucket where the running count or weight reaches
+    // rem, and what is left of rem inside it
+    u64 cum = before;
+    int pick = kWaveBinsPerLane - 1;
+    bool got = false;
+#pragma unroll
+    for (int i = 0; i < kWaveBinsPerLane; ++i) {
+      if (!got && cum + v[i] >= rem) {
+        pick = i;
+        got = true;
+      }
+      if (!got) cum += v[i];
+    }
+    const int d = __shfl(kWaveBins - 1 - (kWaveBinsPerLane * lane + pick), owner, 64);
+    rem = __shfl(rem - cum, owner, 64);
+    const u64 count = (u64)L.cnt[d];
+    const u64 top_key = L.maxkey[d];
+    prefix = (prefix << width) | (u64)d;
+    done += width;
+    if (count == 1ull) return top_key;
+    if (done >= nbits) return prefix;
+  }
+}
+
+// draw() for a list of at most kWaveList tokens, by the workgroup's first wave.
+__device__ int32_t draw_wave(const SampleLds& Lc, int n, int ibits, int V, int32_t k, float p,
+                             float u, const Scale& c, int32_t top, SampleLds& L) {
+  const int lane = threadIdx.x;
+  const int j0 = lane * kWavePer;
+  const int mine = max(0, min(kWavePer, n - j0));
+  u64 key[kWavePer], wt[kWavePer];
+  int32_t idx[kWavePer];
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j) {
+    key[j] = 0ull;
+    wt[j] = 0ull;
+    idx[j] = top;
+    if (j < mine) {
+      const float x = Lc.cx[j0 + j];
+      idx[j] = Lc.ci[j0 + j];
+      key[j] = sort_key(x, idx[j], ibits);
+      wt[j] = weight(x, c);
+    }
+  }
+  u64 cut = 0;
+  if (k > 1 && k < n) cut = wave_select_cutoff<false>(key, wt, mine, ibits, 0ull, p, (u64)k, L);
+  if (p < 1.f) {
+    const u64 c2 = wave_select_cutoff<true>(key, wt, mine, ibits, cut, p, 0ull, L);
+    cut = c2 > cut ? c2 : cut;
+  }
+  // from here on wt holds the kept weights (0 for the tokens cut)
+  u64 s = 0;
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j) {
+    wt[j] = (j < mine && key[j] >= cut) ? wt[j] : 0ull;
+    s += wt[j];
+  }
+  const u64 incl = wave_incl_scan(s, lane);
+  const u64 S = __shfl(incl, 63, 64);
+  double tr = floor((double)u * (double)S);
+  if (!(tr >= 0.0)) tr = 0.0;
+  if (S > 0 && tr > (double)(S - 1)) tr = (double)(S - 1);
+  const u64 target = (u64)tr;
+  // the lane whose tokens the running weight passes target in, then the token
+  const u64 before = incl - s;
+  const u64 owners = __ballot(incl > target && before <= target);
+  int32_t pick = top;
+  if (owners != 0ull) {
+    int32_t hit = top;
+    u64 acc = before;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < kWavePer; ++j) {
+      acc += wt[j];
+      if (!found && acc > target) {
+        hit = idx[j];
+        found = true;
+      }
+    }
+    pick = __shfl(hit, __ffsll((long long)owners) - 1, 64);
+  }
+  return (pick >= 0 && pick < V) ? pick : top;
+}
+
 // Slices of a row: ceil(V / kSliceLen) workgroups of kScreenThreads threads per
 // row, each thread holding kRegs logits in registers (one read of the row),
 // find their slice's largest key and list, in index order, the
@@ -399,7 +564,8 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
 // the row's maximum -- exactly the tokens of the row that pass it, in index
 // order -- go to the LDS list, and top-k, top-p and the draw run on it. A
 // slice that overflowed its capacity, or a list longer than kList, sends the
-// row down the path that reads the row itself.
+// row down the path that reads the row itself. A list of at most kWaveList
+// tokens is ranked by the first wave alone (draw_wave).
 __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, SampleWs w) {
   __shared__ SampleLds L;
   const int r = blockIdx.x;
@@ -460,6 +626,12 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, Sam
       listed += tot;
     }
     __syncthreads();
+    if (listed <= (u64)kWaveList) {
+      if (t >= 64) return;  // no workgroup barrier follows
+      const int32_t pick = draw_wave(L, (int)listed, a.ibits, V, k, p, u, c, top, L);
+      if (t == 0) a.out[r] = pick;
+      return;
+    }
     if (listed <= (u64)kList) {
       ListSrc src{L.cx, L.ci, (int)listed};
       const int32_t pick = draw(src, a.ibits, V, k, p, u, c, top, L);

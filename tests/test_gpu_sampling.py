@@ -63,7 +63,7 @@ def test_small_and_ragged_vocab(V):
     check(logits, T, k, p, u, f"V={V}")
 
 
-@pytest.mark.parametrize("V", [3000, 5000])   # all tokens fit the kernel's LDS list, or not
+@pytest.mark.parametrize("V", [300, 3000, 5000])   # a one-wave list, a workgroup list, or none
 def test_ties_signed_zeros_and_minus_inf(V):
     rng = np.random.default_rng(7)
     R = 40
@@ -149,3 +149,32 @@ def test_long_merged_list_without_slice_overflow():
     p = rng.choice([1.0, 0.99, 0.9, 0.5], R).astype(np.float32)
     u = rng.random(R, dtype=np.float32)
     check(logits, T, k, p, u, "long merged list")
+
+
+def test_list_lengths_around_the_one_wave_limit():
+    # 8 slices of 3072 tokens; row r lists exactly n[r] tokens (values N(0, 1),
+    # spread over every slice so that no slice overflows), the rest sit 200
+    # below and weigh 0. Lists of up to 512 tokens are ranked by one wave,
+    # longer ones by the whole workgroup: both sides of that limit, and the
+    # ends of a wave's lanes (63, 64, 65 tokens)
+    rng = np.random.default_rng(17)
+    n = np.array([8, 9, 63, 64, 65, 200, 511, 512, 513, 777, 1024, 1025, 2000] * 2)
+    R, V = n.size, 24576
+    logits = np.full((R, V), -200.0, np.float32) + rng.standard_normal((R, V)).astype(np.float32)
+    for r in range(R):
+        per = np.full(8, n[r] // 8) + (np.arange(8) < n[r] % 8)
+        idx = np.concatenate([sl * 3072 + rng.choice(3072, c, replace=False)
+                              for sl, c in enumerate(per)])
+        logits[r, idx] = rng.standard_normal(idx.size).astype(np.float32)
+        if r >= R // 2:
+            logits[r, idx[::3]] = logits[r, idx[0]]   # ties across the listed tokens
+    T = np.full(R, 1.0, np.float32)
+    T[1::4] = 0.5
+    k = rng.choice([0, 0, 5, 50, 500], R).astype(np.int32)
+    k[2] = n[2] - 1
+    k[3] = n[3]
+    p = rng.choice([1.0, 0.95, 0.5, 0.01], R).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    u[0] = 0.0
+    u[1] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    check(logits, T, k, p, u, "list lengths")
