@@ -67,6 +67,9 @@ struct SampleLds {
   u64 mass[kBins];
   u64 maxkey[kBins];
   u64 wave[kWaves];
+  u64 wcount[kWaves];      // per wave, read once: its slices' listed tokens,
+  u64 wmax[kWaves];        // their largest key
+  uint32_t wflag[kWaves];  // and whether one of them overflowed
   u64 sel[4];  // chosen bucket, the target left inside it, its count, its largest key
   uint32_t off[kThreads];  // where each slice's list starts when laid end to end
 };
@@ -141,8 +144,6 @@ __device__ inline u64 group_max(u64 v, u64* wave) {
 __device__ inline u64 block_incl_scan(u64 v, SampleLds& L, u64* total) {
   return group_incl_scan<kWaves>(v, L.wave, total);
 }
-
-__device__ inline u64 block_max(u64 v, SampleLds& L) { return group_max<kWaves>(v, L.wave); }
 
 // Index of the token a sort key belongs to, clamped into [lo, hi).
 __device__ inline int32_t key_index(u64 key, int ibits, int32_t lo, int32_t hi) {
@@ -517,7 +518,10 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
     if (t == 0) w.count[slot] = 0;
     return;
   }
-  const float mf = row[key_index(best, a.ibits, lo, hi)];
+  // the slice's largest logit from its key's float bits (-0.0 comes back as
+  // +0.0, which screens the same)
+  const uint32_t kb = (uint32_t)(best >> a.ibits);
+  const float mf = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb);
   const float zf = 22.5f * T;
 
   // index order is (register, wave, lane): per-(register, wave) counts from
@@ -534,15 +538,18 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
     if (lane == 0) s_cnt[j][wv] = (uint32_t)__popcll(bal);
   }
   __syncthreads();
-  if (t == 0) {
-    uint32_t run = 0;
-    for (int j = 0; j < kRegs; ++j)
-      for (int v = 0; v < kW; ++v) {
-        const uint32_t n = s_cnt[j][v];
-        s_cnt[j][v] = run;
-        run += n;
-      }
-    s_total = run;
+  static_assert(kRegs * kW <= 64, "one lane per (register, wave) count");
+  if (t < 64) {  // exclusive offsets in index order, by the first wave
+    uint32_t* cnt = &s_cnt[0][0];
+    const uint32_t n = lane < kRegs * kW ? cnt[lane] : 0u;
+    uint32_t incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    if (lane < kRegs * kW) cnt[lane] = incl - n;
+    if (lane == 63) s_total = incl;
   }
   __syncthreads();
   Cand* out = w.cand + slot * kSliceCap;
@@ -575,29 +582,58 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, Sam
   const int nsl = w.nsl;
   const size_t slot0 = (size_t)r * nsl;
 
-  const u64 best = block_max(t < nsl ? w.lmax[slot0 + t] : 0ull, L);
-  const int32_t top = key_index(best, a.ibits, 0, V);
+  // One read of the slices' maxima and counts (thread t: slice t) and one
+  // workgroup reduction: the row's largest key, whether a slice overflowed,
+  // and each slice's offset in the lists laid end to end (per-wave words of
+  // their own: nothing writes them again).
   const float T = a.temperature[r];
   const int32_t k = a.top_k[r];
   const float p = a.top_p[r];
+  const float u = a.uniforms[r];
+  const int lane = t & 63, wv = t >> 6;
+  u64 best = t < nsl ? w.lmax[slot0 + t] : 0ull;
+  const int32_t n_t = t < nsl ? w.count[slot0 + t] : 0;
+#pragma unroll
+  for (int o = 32; o; o >>= 1) {
+    const u64 x = __shfl_xor(best, o, 64);
+    best = x > best ? x : best;
+  }
+  const bool ovf_w = __ballot(n_t > kSliceCap) != 0ull;
+  const u64 inc_w = wave_incl_scan((u64)n_t, lane);
+  if (lane == 63) {
+    L.wcount[wv] = inc_w;
+    L.wmax[wv] = best;
+    L.wflag[wv] = ovf_w ? 1u : 0u;
+  }
+  __syncthreads();
+  u64 before = 0, n_all = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) {
+    const u64 x = L.wcount[j], m = L.wmax[j];
+    before += (j < wv) ? x : 0ull;
+    n_all += x;
+    best = m > best ? m : best;
+    overflow = overflow || L.wflag[j] != 0u;
+  }
+  const int32_t top = key_index(best, a.ibits, 0, V);
   if (!(T > 0.f) || k == 1) {
     if (t == 0) a.out[r] = top;
     return;
   }
+  // the row's largest logit from its key's float bits (-0.0 comes back as
+  // +0.0, which weighs and screens the same)
+  const uint32_t kb = (uint32_t)(best >> a.ibits);
   Scale c;
-  c.mf = row[top];
+  c.mf = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb);
   c.m = (double)c.mf;
   c.T = (double)T;
   c.zf = 22.5f * T;
-  const float u = a.uniforms[r];
 
-  const int32_t n_t = t < nsl ? w.count[slot0 + t] : 0;
-  const bool overflow = block_max(n_t > kSliceCap ? 1ull : 0ull, L) != 0ull;
   if (!overflow) {
-    // the slices' lists laid end to end: slice offsets by one scan, then each
-    // flat position finds its slice by binary search over the offsets
-    u64 n_all;
-    const u64 end_t = block_incl_scan((u64)n_t, L, &n_all);
+    // the slices' lists laid end to end: each flat position finds its slice
+    // by binary search over the offsets
+    const u64 end_t = inc_w + before;
     if (t < nsl) L.off[t] = (uint32_t)(end_t - (u64)n_t);
     __syncthreads();
     u64 listed = 0;
