@@ -10,6 +10,7 @@ ulp), which changes a token only when a uniform lands within a few parts in
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, given, settings as hsettings, strategies as st
 
 from oracle import sampling as osm
 import paged_kv_cache_page_amd as pa
@@ -178,3 +179,30 @@ def test_list_lengths_around_the_one_wave_limit():
     u[0] = 0.0
     u[1] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
     check(logits, T, k, p, u, "list lengths")
+
+
+@st.composite
+def random_rows(draw):
+    # up to 6 rows of up to 7000 tokens: every draw path (one-wave and
+    # workgroup lists, overflowing slices), spreads from flat to peaked, ties
+    R = draw(st.integers(1, 6))
+    V = draw(st.integers(1, 7000))
+    spread = draw(st.sampled_from([0.25, 1.0, 4.0, 16.0]))
+    ties = draw(st.booleans())
+    rng = np.random.default_rng(draw(st.integers(0, 2**31 - 1)))
+    logits = (rng.standard_normal((R, V)) * spread).astype(np.float32)
+    if ties:
+        logits = np.round(logits).astype(np.float32)
+    T = rng.choice([0.0, 0.1, 0.2, 0.7, 1.0, 2.0], R).astype(np.float32)
+    k = np.where(rng.random(R) < 0.5, 0, rng.integers(1, V + 3, R)).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.5, 0.1, 1e-6], R).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    return logits, T, k, p, u
+
+
+@hsettings(max_examples=30, deadline=None, derandomize=True, database=None,
+           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(random_rows())
+def test_random_rows_match_the_oracle(case):
+    logits, T, k, p, u = case
+    check(logits, T, k, p, u, f"random rows {logits.shape}")
