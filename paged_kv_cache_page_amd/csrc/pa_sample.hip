@@ -303,8 +303,8 @@ __device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, fl
 
 // ---- short lists: one wave, no workgroup barriers ----
 // A list of at most kWaveList tokens is ranked by the row's first wave alone
-// (the others have left): lane l holds tokens kWavePer l .. kWavePer l + 7 of
-// the list with their sort keys and weights in registers (one exp per token),
+// (the others have left): lane l holds tokens l, l + 64, ... of the list with
+// their sort keys and weights in registers (one exp per token),
 // and each radix pass needs only the wave's own LDS ordering. The cutoffs and
 // the draw are the same functions of the list as above (a shortest leading
 // part, then the first token in index order whose running weight passes
@@ -404,11 +404,13 @@ __device__ u64 wave_select_cutoff(const u64 (&key)[kWavePer], const u64 (&wt)[kW
 }
 
 // draw() for a list of at most kWaveList tokens, by the workgroup's first wave.
+// Lane l holds list positions l + 64 j (j < jn = ceil(n / 64)), so a list of
+// n tokens costs each lane jn exps; index order is (j, lane).
 __device__ int32_t draw_wave(const SampleLds& Lc, int n, int ibits, int V, int32_t k, float p,
                              float u, const Scale& c, int32_t top, SampleLds& L) {
   const int lane = threadIdx.x;
-  const int j0 = lane * kWavePer;
-  const int mine = max(0, min(kWavePer, n - j0));
+  const int jn = (n + 63) >> 6;                  // uniform
+  const int mine = max(0, (n - lane + 63) >> 6);  // positions l + 64 j < n: j < mine
   u64 key[kWavePer], wt[kWavePer];
   int32_t idx[kWavePer];
 #pragma unroll
@@ -416,9 +418,10 @@ __device__ int32_t draw_wave(const SampleLds& Lc, int n, int ibits, int V, int32
     key[j] = 0ull;
     wt[j] = 0ull;
     idx[j] = top;
-    if (j < mine) {
-      const float x = Lc.cx[j0 + j];
-      idx[j] = Lc.ci[j0 + j];
+    if (j < jn) {  // uniform; the last j's positions past n are read clamped and left out by mine
+      const int q = min(lane + 64 * j, n - 1);
+      const float x = Lc.cx[q];
+      idx[j] = Lc.ci[q];
       key[j] = sort_key(x, idx[j], ibits);
       wt[j] = weight(x, c);
     }
@@ -436,29 +439,28 @@ __device__ int32_t draw_wave(const SampleLds& Lc, int n, int ibits, int V, int32
     wt[j] = (j < mine && key[j] >= cut) ? wt[j] : 0ull;
     s += wt[j];
   }
-  const u64 incl = wave_incl_scan(s, lane);
-  const u64 S = __shfl(incl, 63, 64);
+  const u64 S = __shfl(wave_incl_scan(s, lane), 63, 64);
   double tr = floor((double)u * (double)S);
   if (!(tr >= 0.0)) tr = 0.0;
   if (S > 0 && tr > (double)(S - 1)) tr = (double)(S - 1);
   const u64 target = (u64)tr;
-  // the lane whose tokens the running weight passes target in, then the token
-  const u64 before = incl - s;
-  const u64 owners = __ballot(incl > target && before <= target);
+  // in index order, one wave scan per j: the first position where the
+  // running weight passes target
   int32_t pick = top;
-  if (owners != 0ull) {
-    int32_t hit = top;
-    u64 acc = before;
-    bool found = false;
+  u64 run = 0;
+  bool done = false;
 #pragma unroll
-    for (int j = 0; j < kWavePer; ++j) {
-      acc += wt[j];
-      if (!found && acc > target) {
-        hit = idx[j];
-        found = true;
-      }
+  for (int j = 0; j < kWavePer; ++j) {
+    if (done || j >= jn) continue;  // uniform
+    const u64 incl = wave_incl_scan(wt[j], lane);
+    const u64 tot = __shfl(incl, 63, 64);
+    if (run + tot > target) {
+      const u64 owners = __ballot(run + incl > target && run + incl - wt[j] <= target);
+      pick = __shfl(idx[j], __ffsll((long long)owners) - 1, 64);
+      done = true;
+    } else {
+      run += tot;
     }
-    pick = __shfl(hit, __ffsll((long long)owners) - 1, 64);
   }
   return (pick >= 0 && pick < V) ? pick : top;
 }
