@@ -332,8 +332,27 @@ __device__ u64 wave_select_cutoff(const u64 (&key)[kWavePer], const u64 (&wt)[kW
                                   int ibits, u64 floor_key, float p, u64 target, SampleLds& L) {
   const int lane = threadIdx.x;
   const int nbits = 32 + ibits;
-  u64 prefix = 0, rem = target;
-  int done = 0;
+  // The leading key bits that every candidate shares need no pass (each such
+  // pass would choose the one bucket that holds them all, leaving rem as it
+  // is): start the descent below them.
+  u64 kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j) {
+    if (j >= n || key[j] < floor_key || (BY_WEIGHT && wt[j] == 0ull)) continue;
+    kmin = key[j] < kmin ? key[j] : kmin;
+    kmax = key[j] > kmax ? key[j] : kmax;
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) {
+    const u64 a = __shfl_xor(kmin, o, 64), b = __shfl_xor(kmax, o, 64);
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  if (kmin > kmax) return ~0ull;    // no candidate: keep nothing (as when no bucket is chosen)
+  if (kmin == kmax) return kmin;    // one candidate: its own key
+  int done = __clzll((long long)(kmin ^ kmax)) - (64 - nbits);
+  u64 prefix = done > 0 ? kmin >> (nbits - done) : 0ull, rem = target;
+  bool first = true;
   for (;;) {
     const int width = min(kWaveDigit, nbits - done);
     const int shift = nbits - done - width;
@@ -370,7 +389,7 @@ __device__ u64 wave_select_cutoff(const u64 (&key)[kWavePer], const u64 (&wt)[kW
       s += v[i];
     }
     const u64 incl = wave_incl_scan(s, lane);
-    if (BY_WEIGHT && done == 0) {
+    if (BY_WEIGHT && first) {
       const u64 total = __shfl(incl, 63, 64);
       const double need = ceil((double)p * (double)total);
       rem = need >= 1.0 ? (u64)need : 1ull;
@@ -398,6 +417,7 @@ __device__ u64 wave_select_cutoff(const u64 (&key)[kWavePer], const u64 (&wt)[kW
     const u64 top_key = L.maxkey[d];
     prefix = (prefix << width) | (u64)d;
     done += width;
+    first = false;
     if (count == 1ull) return top_key;
     if (done >= nbits) return prefix;
   }
