@@ -59,6 +59,7 @@ struct SampleArgs {
 
 constexpr int kPer = 8;      // consecutive tokens per thread in the index-order passes
 constexpr int kList = 4096;  // tokens the LDS list holds; a longer list reads the row again
+constexpr int kListPer = 4;  // candidates per thread and pass when the draw lays out the list
 
 struct SampleLds {
   float cx[kList];    // listed tokens: logit
@@ -658,27 +659,45 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a, Sam
     const u64 end_t = inc_w + before;
     if (t < nsl) L.off[t] = (uint32_t)(end_t - (u64)n_t);
     __syncthreads();
+    // (kListPer consecutive positions per thread: their loads go out together)
     u64 listed = 0;
-    for (int base = 0; base < (int)n_all; base += kThreads) {
-      const int q = base + t;
-      Cand e{0.f, 0};
-      bool keep = false;
-      if (q < (int)n_all) {
-        int lo_s = 0, hi_s = nsl - 1;  // the last slice whose offset is <= q
-        while (lo_s < hi_s) {
-          const int mid = (lo_s + hi_s + 1) >> 1;
-          if ((int)L.off[mid] <= q) lo_s = mid; else hi_s = mid - 1;
+    for (int base = 0; base < (int)n_all; base += kThreads * kListPer) {
+      const int q0 = base + t * kListPer;
+      int sl = 0;  // the last slice whose offset is <= q0
+      if (q0 < (int)n_all) {
+        int hi_s = nsl - 1;
+        while (sl < hi_s) {
+          const int mid = (sl + hi_s + 1) >> 1;
+          if ((int)L.off[mid] <= q0) sl = mid; else hi_s = mid - 1;
         }
-        e = w.cand[(slot0 + lo_s) * kSliceCap + (size_t)(q - (int)L.off[lo_s])];
-        keep = !(c.mf - e.x > c.zf);
+      }
+      Cand e[kListPer];
+#pragma unroll
+      for (int i = 0; i < kListPer; ++i) {
+        const int q = q0 + i;
+        e[i] = Cand{0.f, 0};
+        if (q < (int)n_all) {
+          while (sl + 1 < nsl && (int)L.off[sl + 1] <= q) ++sl;  // past the slice's end
+          e[i] = w.cand[(slot0 + sl) * kSliceCap + (size_t)(q - (int)L.off[sl])];
+        }
+      }
+      bool keep[kListPer];
+      uint32_t kc = 0;
+#pragma unroll
+      for (int i = 0; i < kListPer; ++i) {
+        keep[i] = q0 + i < (int)n_all && !(c.mf - e[i].x > c.zf);
+        kc += keep[i] ? 1u : 0u;
       }
       u64 tot;
-      const u64 inc = block_incl_scan(keep ? 1ull : 0ull, L, &tot);
-      if (keep) {
-        const u64 pos = listed + inc - 1ull;
-        if (pos < (u64)kList) {
-          L.cx[pos] = e.x;
-          L.ci[pos] = e.i;
+      u64 pos = listed + block_incl_scan((u64)kc, L, &tot) - kc;
+#pragma unroll
+      for (int i = 0; i < kListPer; ++i) {
+        if (keep[i]) {
+          if (pos < (u64)kList) {
+            L.cx[pos] = e[i].x;
+            L.ci[pos] = e[i].i;
+          }
+          ++pos;
         }
       }
       listed += tot;
