@@ -75,12 +75,15 @@ struct SampleLds {
   uint32_t off[kThreads];  // where each slice's list starts when laid end to end
 };
 
-__device__ inline u64 sort_key(float x, int32_t i, int ibits) {
+__device__ inline uint32_t order_bits(float x) {
   uint32_t b = __float_as_uint(x);
   if (b == 0x80000000u) b = 0u;                     // -0.0 ranks with +0.0
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);    // unsigned order = float order
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // unsigned order = float order
+}
+
+__device__ inline u64 sort_key(float x, int32_t i, int ibits) {
   const uint32_t inv = ((1u << ibits) - 1u) - (uint32_t)i;
-  return ((u64)b << ibits) | (u64)inv;
+  return ((u64)order_bits(x) << ibits) | (u64)inv;
 }
 
 // The row's largest logit and temperature, in the two precisions the weights use.
@@ -525,15 +528,21 @@ __global__ __launch_bounds__(kScreenThreads) void sample_screen_kernel(SampleArg
     const int i = lo + kScreenThreads * j + t;
     xs[j] = (i < hi) ? row[i] : 0.f;
   }
-  u64 best = 0;
+  // The thread's largest key. Its tokens come in increasing index order, so
+  // of equal float bits the first one seen has the larger key: compare the
+  // 32-bit order-preserving bits alone and form the 64-bit key once.
+  uint32_t bb = 0u;
+  int bi = -1;
 #pragma unroll
   for (int j = 0; j < kRegs; ++j) {
     const int i = lo + kScreenThreads * j + t;
-    if (i < hi) {
-      const u64 k = sort_key(xs[j], i, a.ibits);
-      best = k > best ? k : best;
+    const uint32_t b = order_bits(xs[j]);
+    if (i < hi && (bi < 0 || b > bb)) {
+      bb = b;
+      bi = i;
     }
   }
+  u64 best = bi >= 0 ? ((u64)bb << a.ibits) | (u64)(((1u << a.ibits) - 1u) - (uint32_t)bi) : 0ull;
   best = group_max<kScreenThreads / 64>(best, s_wave);
   if (t == 0) w.lmax[slot] = best;
   const float T = a.temperature[r];
