@@ -308,11 +308,12 @@ __device__ int32_t draw(const Src& src, int ibits, int V, int32_t k, float p, fl
 // ---- short lists: one wave, no workgroup barriers ----
 // A list of at most kWaveList tokens is ranked by the row's first wave alone
 // (the others have left): lane l holds tokens l, l + 64, ... of the list with
-// their sort keys and weights in registers (one exp per token),
-// and each radix pass needs only the wave's own LDS ordering. The cutoffs and
-// the draw are the same functions of the list as above (a shortest leading
-// part, then the first token in index order whose running weight passes
-// floor(u * S)), so the token is the same; only the digit width differs.
+// their sort keys and weights in registers (one exp per token), and each
+// radix pass needs only the wave's own LDS ordering. The cutoffs and the draw
+// are the same functions of the list as above (a shortest leading part, then
+// the first token in index order whose running weight passes floor(u * S)),
+// so the token is the same; only the digit width and the first pass differ
+// (the descent starts below the key bits all candidates share).
 constexpr int kWavePer = 8;
 constexpr int kWaveList = 64 * kWavePer;
 constexpr int kWaveDigit = 8;
